@@ -1,0 +1,394 @@
+/*
+ * CPU oracle for the block-scaled low-precision linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg do. It shares no code, header, table or constant with
+ * the HIP library; every number format is decoded here from its bit layout
+ * and every sum is taken in fp64, in the order the definitions state.
+ *
+ * What it computes (sources are the five web pages bundled as the
+ * reference; each function names the page and section it follows):
+ *
+ *   - per-token activation quantization to e4m3fn with one fp32 scale per
+ *     row (the "(q_fp8, scale)" pairs of the sly-radiance README, fused
+ *     norm/quant section; constants amax/448, round-to-nearest-even and
+ *     saturation are the workload's own definition);
+ *   - Y = dequant(A) . dequant(W)^T (+ bias) with e4m3 weights carrying one
+ *     E8M0 scale per 32x32 block, row-major [N/32, K/32]
+ *     (vLLM DeepSeek-V4 AMD mono runner page, AttnWeights: "wqkv_scale
+ *     [64, 224] uint8 E8M0 (32 x 32 blocks)");
+ *   - the same with fp4 e2m1 weights packed two per byte and one E8M0 scale
+ *     per row per 32 along K, [N, K/32] (same page, MonoLayerWeights.check,
+ *     "AITER's A8W4 layout");
+ *   - the optional bias / tanh-GELU epilogue (flash-rt groot_n17 frontend,
+ *     module docstring: bias and bias+GELU fused into the FP8 GEMM epilogue;
+ *     the tanh GELU is the cortiq vit.rs ACT_SRC shader, act == 2 branch).
+ *
+ * Parallelism: OpenMP over output elements; each output is computed by one
+ * thread in one fixed order, so results are bit-identical for any thread
+ * count (the cortiq dit.rs page makes the same argument for its row split).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#define OR_EPI_NONE 0
+#define OR_EPI_BIAS 1
+#define OR_EPI_BIAS_GELU_TANH 2
+
+/* ---------------------------------------------------------------- codecs */
+
+/* e4m3fn (OCP 8-bit float, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, NaN only at S.1111.111). The pages name the dtype
+ * torch.float8_e4m3fn (vLLM DeepSeek-V4 mono runner, AttnWeights). */
+double or_e4m3_value(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m, -9);            /* subnormal: m/8 * 2^(1-7) */
+    else
+        mag = ldexp((double)(8 + m), e - 10);  /* (1 + m/8) * 2^(e-7) */
+    return s ? -mag : mag;
+}
+
+/* e2m1 (OCP 4-bit float: 2 exponent bits with bias 1, 1 mantissa bit, no
+ * NaN or infinity). The dtype is torch.float4_e2m1fn_x2 on the mono runner
+ * page (MonoLayerWeights.check). `c` is one nibble. */
+double or_e2m1_value(uint8_t c)
+{
+    int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double mag = (e == 0) ? 0.5 * m                        /* m/2 * 2^(1-1) */
+                          : ldexp((double)(2 + m), e - 2); /* (1 + m/2) * 2^(e-1) */
+    return s ? -mag : mag;
+}
+
+/* E8M0: an unsigned biased exponent, value 2^(s-127); 255 encodes NaN. */
+double or_e8m0_value(uint8_t s)
+{
+    if (s == 255)
+        return NAN;
+    return ldexp(1.0, (int)s - 127);
+}
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
+double or_bf16_value(uint16_t b)
+{
+    union { uint32_t u; float f; } v;
+    v.u = (uint32_t)b << 16;
+    return (double)v.f;
+}
+
+/* Round a real number held exactly in a double to the nearest binary32
+ * (the C cast rounds to nearest-even). */
+static float to_f32(double x) { return (float)x; }
+
+/* Nearest e4m3fn code to `v`, ties to the code with the even mantissa bit,
+ * magnitudes above the largest finite value (448) saturate to it, and the
+ * sign of v (also of -0 and of negatives that round to zero) goes to bit 7.
+ * The search walks the 127 non-negative finite codes, which are increasing
+ * in value, and decides between the two neighbours of |v| by comparing |v|
+ * with their midpoint, which is exact in fp64 (both neighbours have 4-bit
+ * significands). `v` must be finite. */
+uint8_t or_e4m3_encode(double v)
+{
+    double a = fabs(v);
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    uint8_t lo, code;
+    double mid;
+    if (a >= 448.0)
+        return sign | 0x7E;
+    lo = 0;
+    while (lo < 0x7E && or_e4m3_value((uint8_t)(lo + 1)) <= a)
+        ++lo;
+    /* now value(lo) <= a < value(lo + 1) and lo < 0x7E */
+    mid = 0.5 * (or_e4m3_value(lo) + or_e4m3_value((uint8_t)(lo + 1)));
+    if (a < mid)
+        code = lo;
+    else if (a > mid)
+        code = (uint8_t)(lo + 1);
+    else
+        code = (lo & 1) ? (uint8_t)(lo + 1) : lo;
+    return sign | code;
+}
+
+/* Nearest e2m1 code (nibble) with the same rules; saturates at 6. */
+uint8_t or_e2m1_encode(double v)
+{
+    double a = fabs(v);
+    uint8_t sign = signbit(v) ? 0x8 : 0x0;
+    uint8_t lo, code;
+    double mid;
+    if (a >= 6.0)
+        return sign | 0x7;
+    lo = 0;
+    while (lo < 0x7 && or_e2m1_value((uint8_t)(lo + 1)) <= a)
+        ++lo;
+    mid = 0.5 * (or_e2m1_value(lo) + or_e2m1_value((uint8_t)(lo + 1)));
+    if (a < mid)
+        code = lo;
+    else if (a > mid)
+        code = (uint8_t)(lo + 1);
+    else
+        code = (lo & 1) ? (uint8_t)(lo + 1) : lo;
+    return sign | code;
+}
+
+/* ------------------------------------------------------------ quantizer */
+
+/* Per-token quantization of bf16 activations [M, K] (row stride ldx
+ * elements) to e4m3fn codes [M, K] (row stride ldq bytes) and one fp32
+ * scale per row, the "(q_fp8, scale)" pair the sly-radiance README's fused
+ * producers hand to its W4A8 GEMM (fused norm/quant rows of its table):
+ *     amax  = max_k |x[m,k]|
+ *     s[m]  = fl32(amax / 448)
+ *     q     = enc(fl32(x / s[m]))           (enc: nearest, ties even, saturate)
+ * A row of zeros gets s = 0 and signed-zero codes. Dividing two binary32
+ * values in fp64 and rounding the quotient to binary32 gives the correctly
+ * rounded binary32 quotient (53 >= 2*24 + 2). */
+void or_quant_rows(const uint16_t *x, int64_t ldx, int64_t M, int64_t K,
+                   uint8_t *q, int64_t ldq, float *s)
+{
+    int64_t m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        const uint16_t *xr = x + m * ldx;
+        uint8_t *qr = q + m * ldq;
+        double amax = 0.0;
+        float sc;
+        int64_t k;
+        for (k = 0; k < K; ++k) {
+            double a = fabs(or_bf16_value(xr[k]));
+            if (a > amax)
+                amax = a;
+        }
+        sc = to_f32(amax / 448.0);
+        s[m] = sc;
+        for (k = 0; k < K; ++k) {
+            double xv = or_bf16_value(xr[k]);
+            if (sc == 0.0f)
+                qr[k] = signbit(xv) ? 0x80 : 0x00;
+            else
+                qr[k] = or_e4m3_encode((double)to_f32(xv / (double)sc));
+        }
+    }
+}
+
+/* ------------------------------------------------------------- epilogue */
+
+/* tanh-approximated GELU: 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))),
+ * the act == 2 branch of the cortiq vit.rs bias/activation shader, taken
+ * here in fp64 with sqrt(2/pi) at full precision and without the shader's
+ * +-15 clamp on the tanh argument (tanh is +-1 to fp64 precision there). */
+double or_gelu_tanh(double v)
+{
+    const double pi = acos(-1.0);
+    const double c = sqrt(2.0 / pi);
+    return 0.5 * v * (1.0 + tanh(c * (v + 0.044715 * v * v * v)));
+}
+
+static double epilogue(double pre, int epi)
+{
+    return epi == OR_EPI_BIAS_GELU_TANH ? or_gelu_tanh(pre) : pre;
+}
+
+/* ---------------------------------------------------------------- GEMMs */
+
+/* One output of the block-scaled e4m3 GEMM Y = dequant(A) dequant(W)^T
+ * (+ bias), the y = x . W^T linear layer (cortiq dit.rs, Proj::matmat doc
+ * comment). `a` is one row of e4m3 codes [K], `w` one row of W [K], `ws`
+ * that row's block-row of E8M0 scales [K/32] (the grid is [N/32, K/32]
+ * with one scale per 32x32 block). In fp64:
+ *   acc   = sum_kb 2^(ws[kb]-127) * sum_{k in block kb} a[k] w[k]
+ *   pre   = a_scale * acc (+ bias)
+ *   out   = pre, or GELU_tanh(pre)
+ *   absum = a_scale * sum_kb 2^(ws[kb]-127) * sum_k |a[k] w[k]|           */
+static void one_bs_fp8(const uint8_t *a, float a_scale, const uint8_t *w,
+                       const uint8_t *ws, const uint16_t *bias_n, int epi,
+                       int64_t K, double *out, double *absum)
+{
+    double acc = 0.0, abs_acc = 0.0, pre;
+    int64_t kb, k;
+    for (kb = 0; kb < K / 32; ++kb) {
+        double blk = 0.0, blk_abs = 0.0, sc = or_e8m0_value(ws[kb]);
+        for (k = kb * 32; k < kb * 32 + 32; ++k) {
+            double p = or_e4m3_value(a[k]) * or_e4m3_value(w[k]);
+            blk += p;
+            blk_abs += fabs(p);
+        }
+        acc += sc * blk;
+        abs_acc += sc * blk_abs;
+    }
+    pre = (double)a_scale * acc;
+    if (epi >= OR_EPI_BIAS)
+        pre += or_bf16_value(*bias_n);
+    *out = epilogue(pre, epi);
+    *absum = fabs((double)a_scale) * abs_acc;
+}
+
+/* One output of the MXFP4-weight GEMM ("A8W4", mono runner page,
+ * MonoLayerWeights.check): `w` is one row of fp4 e2m1 codes packed two per
+ * byte [K/2], element k in byte k/2, low nibble for even k; `ws` is that
+ * row's E8M0 scales [K/32], one per 32 consecutive k.
+ *   w[k] = e2m1(nibble_k) * 2^(ws[k/32]-127); the rest as one_bs_fp8.     */
+static void one_mxfp4(const uint8_t *a, float a_scale, const uint8_t *w,
+                      const uint8_t *ws, const uint16_t *bias_n, int epi,
+                      int64_t K, double *out, double *absum)
+{
+    double acc = 0.0, abs_acc = 0.0, pre;
+    int64_t kb, k;
+    for (kb = 0; kb < K / 32; ++kb) {
+        double blk = 0.0, blk_abs = 0.0, sc = or_e8m0_value(ws[kb]);
+        for (k = kb * 32; k < kb * 32 + 32; ++k) {
+            uint8_t byte = w[k / 2];
+            uint8_t nib = (k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+            double p = or_e4m3_value(a[k]) * or_e2m1_value(nib);
+            blk += p;
+            blk_abs += fabs(p);
+        }
+        acc += sc * blk;
+        abs_acc += sc * blk_abs;
+    }
+    pre = (double)a_scale * acc;
+    if (epi >= OR_EPI_BIAS)
+        pre += or_bf16_value(*bias_n);
+    *out = epilogue(pre, epi);
+    *absum = fabs((double)a_scale) * abs_acc;
+}
+
+/* Whole GEMMs. A e4m3 [M, K] (row stride lda), a_scale fp32 [M],
+ * W [N, K] e4m3 (row stride ldw) with WS [N/32, K/32], or W [N, K/2] fp4x2
+ * (row stride ldw bytes) with WS [N, K/32]; bias bf16 [N] for epi >= 1.
+ * out and absum are [M, N] row-major. K and N are multiples of 32. */
+void or_gemm_bs_fp8(const uint8_t *a, int64_t lda, const float *a_scale,
+                    const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                    const uint16_t *bias, int epi,
+                    int64_t M, int64_t N, int64_t K,
+                    double *out, double *absum)
+{
+    int64_t idx;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (idx = 0; idx < M * N; ++idx) {
+        int64_t m = idx / N, n = idx % N;
+        one_bs_fp8(a + m * lda, a_scale[m], w + n * ldw, ws + (n / 32) * (K / 32),
+                   bias ? bias + n : NULL, epi, K, out + idx, absum + idx);
+    }
+}
+
+void or_gemm_mxfp4_w4a8(const uint8_t *a, int64_t lda, const float *a_scale,
+                        const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                        const uint16_t *bias, int epi,
+                        int64_t M, int64_t N, int64_t K,
+                        double *out, double *absum)
+{
+    int64_t idx;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (idx = 0; idx < M * N; ++idx) {
+        int64_t m = idx / N, n = idx % N;
+        one_mxfp4(a + m * lda, a_scale[m], w + n * ldw, ws + n * (K / 32),
+                  bias ? bias + n : NULL, epi, K, out + idx, absum + idx);
+    }
+}
+
+/* The same for a list of sampled outputs (ms[i], ns[i]), for problems too
+ * large to evaluate whole; out and absum are [count]. */
+void or_gemm_bs_fp8_sampled(const uint8_t *a, int64_t lda, const float *a_scale,
+                            const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                            const uint16_t *bias, int epi, int64_t K,
+                            int64_t count, const int64_t *ms, const int64_t *ns,
+                            double *out, double *absum)
+{
+    int64_t i;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (i = 0; i < count; ++i) {
+        int64_t m = ms[i], n = ns[i];
+        one_bs_fp8(a + m * lda, a_scale[m], w + n * ldw, ws + (n / 32) * (K / 32),
+                   bias ? bias + n : NULL, epi, K, out + i, absum + i);
+    }
+}
+
+void or_gemm_mxfp4_w4a8_sampled(const uint8_t *a, int64_t lda, const float *a_scale,
+                                const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                                const uint16_t *bias, int epi, int64_t K,
+                                int64_t count, const int64_t *ms, const int64_t *ns,
+                                double *out, double *absum)
+{
+    int64_t i;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (i = 0; i < count; ++i) {
+        int64_t m = ms[i], n = ns[i];
+        one_mxfp4(a + m * lda, a_scale[m], w + n * ldw, ws + n * (K / 32),
+                  bias ? bias + n : NULL, epi, K, out + i, absum + i);
+    }
+}
+
+/* --------------------------------------------------- weight preparation */
+
+/* e4m3 weight codes from real values: one enc() per element (offline weight
+ * preparation; the workloads draw weight values and encode them). */
+void or_encode_e4m3(const float *v, int64_t count, uint8_t *q)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < count; ++i)
+        q[i] = or_e4m3_encode((double)v[i]);
+}
+
+/* MXFP4 weight quantization of real values [N, K] (row-major, K % 32 == 0)
+ * by the OCP Microscaling v1.0 conversion, per group of 32 consecutive k:
+ *   shared exponent X = floor(log2(amax)) - 2   (2 = e2m1's largest exponent)
+ *   scale byte       = X + 127, clamped to [0, 254]
+ *   element          = enc_e2m1(v / 2^(byte-127))   (nearest, ties even,
+ *                                                    saturating at 6)
+ * A group of zeros gets scale byte 0 and zero codes. Output: packed
+ * [N, K/2] (low nibble = even k) and scales [N, K/32]. The sly-radiance
+ * README's checkpoints are MXFP4 produced this way offline; the conversion
+ * rule itself is the OCP specification's. */
+void or_quant_mxfp4_weights(const float *v, int64_t N, int64_t K,
+                            uint8_t *packed, uint8_t *scales)
+{
+    int64_t n, KB = K / 32;
+#pragma omp parallel for schedule(static)
+    for (n = 0; n < N; ++n) {
+        int64_t kb, k;
+        for (kb = 0; kb < KB; ++kb) {
+            const float *g = v + n * K + kb * 32;
+            double amax = 0.0, unit;
+            int X, byte;
+            for (k = 0; k < 32; ++k)
+                if (fabs((double)g[k]) > amax)
+                    amax = fabs((double)g[k]);
+            if (amax == 0.0) {
+                byte = 0;
+            } else {
+                int e2;
+                frexp(amax, &e2);          /* amax = f * 2^e2, f in [0.5, 1) */
+                X = (e2 - 1) - 2;          /* floor(log2 amax) - emax(e2m1) */
+                byte = X + 127;
+                if (byte < 0) byte = 0;
+                if (byte > 254) byte = 254;
+            }
+            scales[n * KB + kb] = (uint8_t)byte;
+            unit = ldexp(1.0, byte - 127);
+            for (k = 0; k < 32; k += 2) {
+                uint8_t lo = or_e2m1_encode((double)g[k] / unit);
+                uint8_t hi = or_e2m1_encode((double)g[k + 1] / unit);
+                packed[n * (K / 2) + kb * 16 + k / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
+}
+
+/* Threads the OpenMP runtime will use (for reporting). */
+int or_num_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

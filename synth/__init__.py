@@ -1,0 +1,166 @@
+"""Seeded synthetic workloads for the block-scaled linear layer.
+
+Both the CPU oracle's tests and the GPU library's tests and benchmark draw
+their inputs here; this module holds random draws and the offline weight
+preparation that turns drawn weight values into stored codes, nothing of the
+layer's own arithmetic (activation quantization, decoding, the GEMM or its
+epilogue).
+
+Every tensor has its own PCG64 stream, keyed by (seed, tensor id), so a
+tensor does not change when another one's shape does: W is the same across
+an M sweep, and A for M rows is the first M rows of A for more rows.
+
+Workloads (shapes from the vLLM DeepSeek-V4 AMD mono runner page's weight
+tables, the flash-rt groot_n17 ViT fc1 site and the sly-radiance README's
+fused gate_up):
+
+  tiny     M=16,  N=256,   K=256,  e4m3 W, 32x32 E8M0, bias epilogue
+  decode   M in {1,4,8,16,64}, N=2048, K=7168, e4m3 W (wqkv's [2048, 7168]
+           with its [64, 224] scale grid), no bias
+  prefill  M=4096, N=7168, K=8192, e4m3 W, 1% of A's columns scaled x20
+  ffn_up   M=2048, N=4096, K=1024, e4m3 W, bias + tanh-GELU (second variant
+           bias only)
+  gate_up  M in {1,16,512,4096}, N=34816, K=5120, MXFP4 W (e2m1 + 1x32 E8M0)
+
+Value laws: A ~ N(0,1) rounded to bf16; e4m3 W = nearest e4m3 code of an
+N(0, 0.05) sample; 32x32 scale bytes uniform on [120, 130]; bias ~ N(0, 0.1)
+rounded to bf16; MXFP4 W from N(0, 0.02) samples by the OCP MX conversion.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+EPI_NONE, EPI_BIAS, EPI_BIAS_GELU_TANH = 0, 1, 2
+
+# tensor ids of the per-tensor streams
+_T_A, _T_OUTLIER, _T_W, _T_WS, _T_BIAS = 0, 1, 2, 3, 4
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    fmt: str               # "fp8" (e4m3 W, 32x32 scales) or "mxfp4"
+    epilogue: int
+    outlier_frac: float = 0.0
+    m_sweep: tuple = ()
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 16, 256, 256, "fp8", EPI_BIAS),
+    "decode": Workload("decode", 8, 2048, 7168, "fp8", EPI_NONE, m_sweep=(1, 4, 8, 16, 64)),
+    "prefill": Workload("prefill", 4096, 7168, 8192, "fp8", EPI_NONE, outlier_frac=0.01),
+    "ffn_up": Workload("ffn_up", 2048, 4096, 1024, "fp8", EPI_BIAS_GELU_TANH),
+    "ffn_up_bias": Workload("ffn_up_bias", 2048, 4096, 1024, "fp8", EPI_BIAS),
+    "gate_up": Workload("gate_up", 16, 34816, 5120, "mxfp4", EPI_NONE, m_sweep=(1, 16, 512, 4096)),
+}
+
+
+def _rng(seed: int, tensor: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(tensor,))))
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), torch's round-to-nearest-even cast."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def activations(wl: Workload, M: int | None = None, seed: int = 0) -> np.ndarray:
+    """bf16 bits [M, K]: N(0,1) samples; for the prefill workload
+    round(frac*K) distinct columns are multiplied by 20 before rounding."""
+    M = wl.M if M is None else M
+    a = _rng(seed, _T_A).standard_normal((M, wl.K), dtype=np.float32)
+    if wl.outlier_frac > 0:
+        cols = _rng(seed, _T_OUTLIER).choice(wl.K, size=int(round(wl.outlier_frac * wl.K)),
+                                             replace=False)
+        a[:, cols] *= np.float32(20.0)
+    return to_bf16_bits(a)
+
+
+def weight_values(wl: Workload, seed: int = 0, rows: slice | None = None) -> np.ndarray:
+    """float32 weight samples [N, K] (or a slice of rows) before encoding."""
+    std = 0.05 if wl.fmt == "fp8" else 0.02
+    rng = _rng(seed, _T_W)
+    if rows is None or rows == slice(None):
+        return rng.standard_normal((wl.N, wl.K), dtype=np.float32) * np.float32(std)
+    start, stop = rows.start or 0, rows.stop
+    rng.standard_normal((start, wl.K), dtype=np.float32)  # advance the stream
+    return rng.standard_normal((stop - start, wl.K), dtype=np.float32) * np.float32(std)
+
+
+def _encode_e4m3_weights(v: np.ndarray) -> np.ndarray:
+    # Offline weight preparation with torch's float8_e4m3fn cast (nearest,
+    # ties to even). The samples are far below the format's range, where the
+    # cast and a saturating encoder agree; a CPU test compares the result
+    # with the oracle's encoder on every generated value of the tiny
+    # workload and on samples of the others.
+    assert np.abs(v).max() < 448.0
+    return torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _mx_quantize_rows(v: np.ndarray):
+    # Offline OCP MX conversion of weight rows: per 32 consecutive k, the
+    # shared exponent floor(log2 amax) - 2, its E8M0 byte (clamped to
+    # [0, 254]), and each element's nearest e2m1 code (ties to the even
+    # code, saturating at 6) of v / 2^exponent. A CPU test checks the
+    # result bit for bit against the oracle's own conversion.
+    n, K = v.shape
+    g = v.reshape(n, K // 32, 32).astype(np.float64)
+    amax = np.abs(g).max(axis=2)
+    _, ex = np.frexp(amax)
+    byte = np.where(amax > 0, np.clip(ex - 1 - 2 + 127, 0, 254), 0).astype(np.int64)
+    x = g / np.ldexp(1.0, byte - 127)[..., None]
+    a = np.minimum(np.abs(x), 6.0)
+    lo = np.searchsorted(_E2M1_GRID, a, side="right") - 1          # grid[lo] <= a
+    hi = np.minimum(lo + 1, 7)
+    mid = 0.5 * (_E2M1_GRID[lo] + _E2M1_GRID[hi])
+    code = np.where(a < mid, lo, np.where(a > mid, hi, np.where(lo & 1, hi, lo)))
+    code = np.where(a >= 6.0, 7, code)
+    code = code | np.where(np.signbit(x), 8, 0)
+    code = code.reshape(n, K).astype(np.uint8)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, byte.astype(np.uint8)
+
+
+def weights(wl: Workload, seed: int = 0):
+    """(W, W scales): e4m3 codes [N, K] with E8M0 [N/32, K/32] uniform on
+    [120, 130], or MXFP4 packed [N, K/2] with E8M0 [N, K/32]."""
+    if wl.fmt == "fp8":
+        w = _encode_e4m3_weights(weight_values(wl, seed))
+        ws = _rng(seed, _T_WS).integers(120, 131, size=(wl.N // 32, wl.K // 32),
+                                        dtype=np.uint8)
+        return w, ws
+    packed = np.empty((wl.N, wl.K // 2), dtype=np.uint8)
+    scales = np.empty((wl.N, wl.K // 32), dtype=np.uint8)
+    rng = _rng(seed, _T_W)
+    chunk = 2048
+    for r0 in range(0, wl.N, chunk):
+        r1 = min(wl.N, r0 + chunk)
+        v = rng.standard_normal((r1 - r0, wl.K), dtype=np.float32) * np.float32(0.02)
+        packed[r0:r1], scales[r0:r1] = _mx_quantize_rows(v)
+    return packed, scales
+
+
+def bias(wl: Workload, seed: int = 0):
+    """bf16 bits [N] ~ N(0, 0.1), or None for workloads without a bias."""
+    if wl.epilogue == EPI_NONE:
+        return None
+    b = _rng(seed, _T_BIAS).standard_normal((wl.N,), dtype=np.float32) * np.float32(0.1)
+    return to_bf16_bits(b)
+
+
+def make(name: str, M: int | None = None, seed: int = 0) -> dict:
+    """All inputs of a workload: A bf16 bits, W, W scales, bias, epilogue."""
+    wl = WORKLOADS[name]
+    w, ws = weights(wl, seed)
+    return {"wl": wl, "M": wl.M if M is None else M, "a_bf16": activations(wl, M, seed),
+            "w": w, "w_scale": ws, "bias": bias(wl, seed), "epilogue": wl.epilogue}
