@@ -1,0 +1,130 @@
+/*
+ * bsgemm: the block-scaled low-precision linear layer of transformer
+ * inference on AMD Instinct MI355X (gfx950), as a C ABI.
+ *
+ *   1. fp8_quant_rows   bf16 activations -> per-token e4m3fn codes + fp32 scale
+ *   2. gemm_bs_fp8      Y = dequant(A) dequant(W)^T (+ bias, + tanh-GELU), W in
+ *                       e4m3fn with one E8M0 scale per 32x32 block
+ *   3. gemm_mxfp4_w4a8  the same with MXFP4 weights (fp4 e2m1, one E8M0 scale
+ *                       per row per 32 along K)
+ *
+ * Sources (web pages bundled as the reference):
+ *   - formats and scale grids: vLLM DeepSeek-V4 AMD mono runner page,
+ *     AttnWeights ("wqkv [2048, 7168] e4m3", "wqkv_scale [64, 224] uint8
+ *     E8M0 (32 x 32 blocks)") and MonoLayerWeights.check (fp4x2 weights
+ *     [.., N, K/2] with uint8 scales [N, K/32], "AITER's A8W4 layout");
+ *   - per-token (q_fp8, scale) pairs feeding the W4A8 GEMM: sly-radiance
+ *     README, fused norm/quant rows of its file table;
+ *   - bias / bias+GELU fused into the FP8 GEMM epilogue: flash-rt
+ *     groot_n17 frontend, module docstring and _fused_epilogue_enabled;
+ *   - the tanh GELU: cortiq vit.rs, ACT_SRC shader, act == 2 branch;
+ *   - raw device pointers + sizes + a stream, caller-owned outputs, shape
+ *     checks because loads are unbounded: flash-rt groot_n17 (bf16_nn_bias
+ *     call sites) and the mono runner page (_check_tensors, forward).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller. Nothing
+ *     is allocated, freed or synchronized; work is enqueued on `stream`
+ *     (a hipStream_t passed as void*, NULL = the null stream) and the call
+ *     returns before it runs. Calls may be captured into a HIP graph.
+ *   - Matrices are row-major with a leading dimension (row stride) given in
+ *     elements (bytes for 8-bit and packed data). Base pointers and leading
+ *     dimensions in bytes must be multiples of 16.
+ *   - Arguments are checked on the host before anything is launched; on
+ *     error nothing is launched and outputs are untouched. The first call
+ *     on a device also checks that it is a gfx950 (BS_EARCH otherwise).
+ *   - Inputs must not overlap outputs.
+ *   - Returns BS_OK (0) or a negative bs_status.
+ */
+#ifndef BSGEMM_H
+#define BSGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum bs_status {
+    BS_OK = 0,
+    BS_EINVAL = -1,      /* a size, leading dimension, epilogue or null pointer is invalid */
+    BS_EALIGN = -2,      /* a pointer or leading dimension is not 16-byte aligned */
+    BS_EARCH = -3,       /* no HIP device, or the current device is not gfx950 */
+    BS_EWORKSPACE = -4,  /* workspace smaller than bs_workspace_bytes() */
+    BS_ELAUNCH = -5      /* the kernel launch failed (hipGetLastError) */
+};
+
+enum bs_epilogue {
+    BS_EPI_NONE = 0,            /* y = s[m] * acc                               */
+    BS_EPI_BIAS = 1,            /* y = s[m] * acc + bias[n]                     */
+    BS_EPI_BIAS_GELU_TANH = 2   /* y = gelu_tanh(s[m] * acc + bias[n])          */
+};
+
+/*
+ * Per-token quantization to e4m3fn (the "(q_fp8, scale)" pair of the
+ * sly-radiance README's fused producers). For each row m of x:
+ *     amax    = max_k |x[m,k]|
+ *     scale[m]= amax / 448                     (fp32, correctly rounded)
+ *     q[m,k]  = e4m3fn(x[m,k] / scale[m])      (fp32 division correctly
+ *               rounded, then nearest e4m3 value with ties to the even
+ *               mantissa, saturating at +-448, sign kept also for zeros)
+ * A row of zeros gets scale 0 and codes 0x00 / 0x80 (for -0).
+ *   x_bf16  [M, K] bf16, row stride ld_x elements (ld_x >= K, 2*ld_x % 16 == 0)
+ *   q_e4m3  [M, K] uint8 out, row stride ld_q bytes (ld_q >= K, ld_q % 16 == 0)
+ *   scale   [M] fp32 out
+ *   M >= 1, K >= 32, K % 32 == 0. NaN/Inf inputs are not supported.
+ */
+int fp8_quant_rows(const void *x_bf16, int64_t ld_x, void *q_e4m3, int64_t ld_q,
+                   float *scale, int64_t M, int64_t K, void *stream);
+
+/*
+ * Block-scaled e4m3 GEMM (y = x W^T form):
+ *     acc[m,n] = sum_kb 2^(w_scale[n/32][kb]-127) * sum_{k in block kb}
+ *                e4m3(a[m,k]) * e4m3(w[n,k])               (fp32 accumulation)
+ *     y[m,n]   = epilogue(a_scale[m] * acc[m,n] (+ bias[n]))   -> bf16, nearest-even
+ *   a_e4m3   [M, K] uint8 e4m3fn, row stride ld_a bytes; a_scale [M] fp32
+ *            (as produced by fp8_quant_rows)
+ *   w_e4m3   [N, K] uint8 e4m3fn, row stride ld_w bytes
+ *   w_scale  [N/32, K/32] uint8 E8M0, row-major, dense (row stride K/32)
+ *   bias     [N] bf16, required iff epilogue != BS_EPI_NONE, else ignored
+ *   y_bf16   [M, N] bf16 out, row stride ld_y elements
+ *   M >= 1; N, K >= 32 and multiples of 32.
+ *   workspace / workspace_bytes: scratch the call may use, at least
+ *   bs_workspace_bytes(0, M, N, K) bytes (may be NULL when that is 0).
+ */
+int gemm_bs_fp8(const void *a_e4m3, int64_t ld_a, const float *a_scale,
+                const void *w_e4m3, int64_t ld_w, const uint8_t *w_scale,
+                const void *bias_bf16, int epilogue,
+                void *y_bf16, int64_t ld_y,
+                int64_t M, int64_t N, int64_t K,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * MXFP4-weight GEMM with e4m3 activations ("A8W4"):
+ *     w[n,k]   = e2m1(nibble k of row n) * 2^(w_scale[n][k/32]-127)
+ *     y[m,n]   = epilogue(a_scale[m] * sum_k e4m3(a[m,k]) w[n,k] (+ bias[n]))
+ *   w_fp4x2  [N, K/2] bytes, row stride ld_w bytes; element k of a row is in
+ *            byte k/2, low nibble for even k, high nibble for odd k
+ *   w_scale  [N, K/32] uint8 E8M0, row-major, dense (row stride K/32)
+ *   Everything else as gemm_bs_fp8; workspace: bs_workspace_bytes(1, M, N, K).
+ */
+int gemm_mxfp4_w4a8(const void *a_e4m3, int64_t ld_a, const float *a_scale,
+                    const void *w_fp4x2, int64_t ld_w, const uint8_t *w_scale,
+                    const void *bias_bf16, int epilogue,
+                    void *y_bf16, int64_t ld_y,
+                    int64_t M, int64_t N, int64_t K,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Scratch bytes gemm_bs_fp8 (op 0) or gemm_mxfp4_w4a8 (op 1) needs for this
+ * shape; 0 means none. */
+size_t bs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
+
+/* A static, human-readable string for a bs_status value. */
+const char *bs_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSGEMM_H */

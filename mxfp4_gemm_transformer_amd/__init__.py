@@ -1,0 +1,177 @@
+"""Block-scaled low-precision linear layer on AMD Instinct MI355X (gfx950).
+
+A thin binding of the C ABI in ``include/bsgemm.h`` (``libbsgemm.so``, built
+in-tree by ``__graft_entry__.build()``): the functions below check tensor
+dtypes, shapes and strides, allocate outputs with torch when none are given,
+and pass raw device pointers and torch's current HIP stream to the library.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback path. Importing works without a GPU; the first call that needs the
+library raises if it was not built.
+
+    q, s = fp8_quant_rows(x)                               # bf16 [M, K]
+    y = gemm_bs_fp8(q, s, w, w_scale, bias, EPI_BIAS)      # e4m3 W, 32x32 E8M0
+    y = gemm_mxfp4_w4a8(q, s, w4, w4_scale)                # fp4x2 W, 1x32 E8M0
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["fp8_quant_rows", "gemm_bs_fp8", "gemm_mxfp4_w4a8", "bs_workspace_bytes",
+           "bs_status_string", "BsError", "EPI_NONE", "EPI_BIAS", "EPI_BIAS_GELU_TANH",
+           "library_path", "load_library", "EXPORTED_SYMBOLS"]
+
+EPI_NONE, EPI_BIAS, EPI_BIAS_GELU_TANH = 0, 1, 2
+BS_OK, BS_EINVAL, BS_EALIGN, BS_EARCH, BS_EWORKSPACE, BS_ELAUNCH = 0, -1, -2, -3, -4, -5
+
+EXPORTED_SYMBOLS = ("fp8_quant_rows", "gemm_bs_fp8", "gemm_mxfp4_w4a8", "bs_workspace_bytes",
+                    "bs_status_string")
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsgemm.so")
+_lib = None
+
+
+class BsError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s failed: %s (status %d)" % (what, bs_status_string(status), status))
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libbsgemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libbsgemm.so is not built; run __graft_entry__.build() "
+                               "(hipcc --offload-arch=gfx950) first")
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib.fp8_quant_rows.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp]
+        lib.fp8_quant_rows.restype = i32
+        gemm = [vp, i64, vp, vp, i64, vp, vp, i32, vp, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
+        lib.gemm_bs_fp8.argtypes = gemm
+        lib.gemm_bs_fp8.restype = i32
+        lib.gemm_mxfp4_w4a8.argtypes = gemm
+        lib.gemm_mxfp4_w4a8.restype = i32
+        lib.bs_workspace_bytes.argtypes = [i32, i64, i64, i64]
+        lib.bs_workspace_bytes.restype = ctypes.c_size_t
+        lib.bs_status_string.argtypes = [i32]
+        lib.bs_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def bs_status_string(status: int) -> str:
+    return load_library().bs_status_string(int(status)).decode()
+
+
+def bs_workspace_bytes(op: int, M: int, N: int, K: int) -> int:
+    return int(load_library().bs_workspace_bytes(int(op), int(M), int(N), int(K)))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _u8(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype in (torch.float8_e4m3fn, getattr(torch, "float4_e2m1fn_x2", None)):
+        t = t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError("%s must be uint8 / float8_e4m3fn bytes, got %s" % (name, t.dtype))
+    return t
+
+
+def _matrix(t: torch.Tensor, name: str, rows: int, cols: int) -> int:
+    """Check a row-major [rows, cols] view with unit column stride; return its row stride."""
+    if t.dim() != 2 or tuple(t.shape) != (rows, cols) or t.stride(1) != 1:
+        raise ValueError("%s must be a [%d, %d] row-major view, got shape %s strides %s"
+                         % (name, rows, cols, tuple(t.shape), t.stride()))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    return t.stride(0) if rows > 1 else max(t.stride(0), cols)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def fp8_quant_rows(x: torch.Tensor, q: torch.Tensor | None = None,
+                   scale: torch.Tensor | None = None, stream=None):
+    """Per-token e4m3 quantization of bf16 x [M, K]. Returns (q uint8 [M, K],
+    scale fp32 [M])."""
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    M, K = x.shape
+    ldx = _matrix(x, "x", M, K)
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    q = _u8(q, "q")
+    ldq = _matrix(q, "q", M, K)
+    if scale is None:
+        scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    if scale.dtype != torch.float32 or scale.shape != (M,) or not scale.is_contiguous():
+        raise ValueError("scale must be a contiguous fp32 [M] tensor")
+    st = load_library().fp8_quant_rows(_ptr(x), ldx, _ptr(q), ldq, _ptr(scale), M, K,
+                                       ctypes.c_void_p(_stream(stream)))
+    if st != BS_OK:
+        raise BsError(st, "fp8_quant_rows")
+    return q, scale
+
+
+def _gemm(fn_name, op, a, a_scale, w, w_scale, bias, epilogue, y, workspace, stream, w_cols,
+          ws_shape):
+    a = _u8(a, "a")
+    w = _u8(w, "w")
+    M, K = a.shape
+    N = w.shape[0]
+    lda = _matrix(a, "a", M, K)
+    ldw = _matrix(w, "w", N, w_cols(K))
+    if a_scale.dtype != torch.float32 or a_scale.shape != (M,) or not a_scale.is_contiguous():
+        raise ValueError("a_scale must be a contiguous fp32 [M] tensor")
+    if w_scale.dtype != torch.uint8 or tuple(w_scale.shape) != ws_shape(N, K) \
+            or not w_scale.is_contiguous():
+        raise ValueError("w_scale must be a contiguous uint8 %s tensor" % (ws_shape(N, K),))
+    if epilogue != EPI_NONE:
+        if bias is None or bias.dtype != torch.bfloat16 or bias.shape != (N,) \
+                or not bias.is_contiguous():
+            raise ValueError("this epilogue needs a contiguous bf16 bias [N]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    if y.dtype != torch.bfloat16:
+        raise TypeError("y must be bfloat16")
+    ldy = _matrix(y, "y", M, N)
+    need = bs_workspace_bytes(op, M, N, K)
+    if need and workspace is None:
+        workspace = torch.zeros((need,), dtype=torch.uint8, device=a.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    fn = getattr(load_library(), fn_name)
+    st = fn(_ptr(a), lda, _ptr(a_scale), _ptr(w), ldw, _ptr(w_scale),
+            _ptr(bias if epilogue != EPI_NONE else None), int(epilogue), _ptr(y), ldy, M, N, K,
+            _ptr(workspace), ws_bytes, ctypes.c_void_p(_stream(stream)))
+    if st != BS_OK:
+        raise BsError(st, fn_name)
+    return y
+
+
+def gemm_bs_fp8(a, a_scale, w, w_scale, bias=None, epilogue=EPI_NONE, y=None, workspace=None,
+                stream=None):
+    """y [M, N] bf16 = epilogue(a_scale[m] * sum_k a[m,k] w[n,k] 2^(S[n/32,k/32]-127) (+ bias)).
+    a: e4m3 [M, K]; w: e4m3 [N, K]; w_scale: uint8 E8M0 [N/32, K/32]."""
+    return _gemm("gemm_bs_fp8", 0, a, a_scale, w, w_scale, bias, epilogue, y, workspace, stream,
+                 lambda K: K, lambda N, K: (N // 32, K // 32))
+
+
+def gemm_mxfp4_w4a8(a, a_scale, w, w_scale, bias=None, epilogue=EPI_NONE, y=None,
+                    workspace=None, stream=None):
+    """As gemm_bs_fp8 with fp4 e2m1 weights packed [N, K/2] (low nibble = even
+    k) and one E8M0 scale per row per 32 k, w_scale [N, K/32]."""
+    return _gemm("gemm_mxfp4_w4a8", 1, a, a_scale, w, w_scale, bias, epilogue, y, workspace,
+                 stream, lambda K: K // 2, lambda N, K: (N, K // 32))

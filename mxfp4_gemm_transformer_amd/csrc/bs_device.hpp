@@ -1,0 +1,114 @@
+// Device-side building blocks for the gfx950 kernels: vector types, the
+// e4m3fn encoder, bf16 rounding, the tanh-GELU epilogue, and the operand
+// layout of the scaled MFMA instructions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsg {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+enum { EPI_NONE = 0, EPI_BIAS = 1, EPI_BIAS_GELU_TANH = 2 };
+
+// Operand formats of V_MFMA_SCALE_F32_*_F8F6F4 (cbsz / blgp encodings).
+enum { MFMA_FMT_FP8 = 0, MFMA_FMT_FP4 = 4 };
+
+// E8M0 byte that scales by 1.0.
+constexpr int E8M0_ONE = 127;
+
+// ---------------------------------------------------------------- e4m3fn
+// Nearest e4m3fn code to a finite fp32 value, ties to the even mantissa,
+// saturating at +-448 (0x7E / 0xFE), sign kept (also for zero results).
+// Normal range: round the binary32 pattern to 3 mantissa bits by adding
+// 0x7FFFF plus the kept LSB (carry propagates into the exponent), then
+// rebias the exponent from 127 to 7. Below 2^-6 the e4m3 grid is uniform
+// with step 2^-9, so the code is rint(|v| * 2^9) (exact scaling, the
+// hardware rint rounds to nearest even).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    const uint32_t bits = __float_as_uint(v);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const uint32_t mag = bits & 0x7FFFFFFFu;
+    uint32_t code;
+    if (mag >= 0x43E00000u) {                 // |v| >= 448
+        code = 0x7Eu;
+    } else if (mag < 0x3C800000u) {           // |v| < 2^-6
+        code = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 512.0f);
+    } else {
+        const uint32_t r = mag + 0x7FFFFu + ((mag >> 20) & 1u);
+        code = (r >> 20) - (120u << 3);       // (127 - 7) << 3
+    }
+    return sign | code;
+}
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// -------------------------------------------------------------- epilogue
+__device__ __forceinline__ float gelu_tanh(float v) {
+    // 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))
+    const float u = 0.7978845608028654f * (v + 0.044715f * v * v * v);
+    return 0.5f * v * (1.0f + tanhf(u));
+}
+
+__device__ __forceinline__ float epilogue(float acc, float a_scale, float bias, int epi) {
+    float v = a_scale * acc;
+    if (epi != EPI_NONE) v += bias;
+    if (epi == EPI_BIAS_GELU_TANH) v = gelu_tanh(v);
+    return v;
+}
+
+// ------------------------------------------------------ MFMA operand layout
+// V_MFMA_SCALE_F32_16X16X128_F8F6F4 (measured on gfx950):
+//   lane l = i + 16 g (i = row of A / column of B, g = 0..3).
+//   fp8 operand, K window [k0, k0 + 128):
+//     VGPRs 0-3 hold k0 + 16 g + [0, 16), VGPRs 4-7 hold k0 + 64 + 16 g + [0, 16)
+//   fp4 operand: VGPRs 0-3 hold the 32 elements k0 + 32 g + [0, 32), two per
+//     byte, low nibble first (the packed row-major layout, unchanged)
+//   E8M0 scale of lane l applies to the 32-element block k0 + 32 g + [0, 32)
+//     of row/column i.
+//   D: lane l, VGPR v -> row 4 g + v, column i.
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4: lane l = i + 32 g (g = 0..1), window of
+//   64: fp8 VGPRs 0-3 hold k0 + 16 g + [0,16), VGPRs 4-7 hold k0 + 32 + 16 g
+//   + [0, 16); fp4 holds k0 + 32 g + [0, 32); the scale of lane l covers
+//   block k0 + 32 g + [0, 32); D: lane l, VGPR v -> row 8 (v / 4) + 4 g +
+//   v % 4, column i.
+template <bool FP4>
+__device__ __forceinline__ v4f mfma16(const v8i &a, const v8i &b, const v4f &c, int sa, int sb) {
+    if (FP4)
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, MFMA_FMT_FP8, MFMA_FMT_FP4,
+                                                                0, sa, 0, sb);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, MFMA_FMT_FP8, MFMA_FMT_FP8, 0,
+                                                            sa, 0, sb);
+}
+
+template <bool FP4>
+__device__ __forceinline__ v16f mfma32(const v8i &a, const v8i &b, const v16f &c, int sa, int sb) {
+    if (FP4)
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, MFMA_FMT_FP8, MFMA_FMT_FP4, 0,
+                                                               sa, 0, sb);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, MFMA_FMT_FP8, MFMA_FMT_FP8, 0,
+                                                           sa, 0, sb);
+}
+
+__device__ __forceinline__ v8i pack8(const uint4 &lo, const uint4 &hi) {
+    v8i r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+}
+
+__device__ __forceinline__ uint4 ldg16(const void *p) {
+    return *reinterpret_cast<const uint4 *>(p);
+}
+
+}  // namespace bsg

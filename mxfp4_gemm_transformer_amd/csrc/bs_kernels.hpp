@@ -1,0 +1,27 @@
+// Host-side launchers of the gfx950 kernels. Arguments are validated by the
+// C-ABI layer before these are called; each returns a hipError_t from
+// hipGetLastError() after its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsg {
+
+hipError_t launch_quant_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_t ld_q,
+                             float *scale, int64_t M, int64_t K, hipStream_t stream);
+
+// M <= DECODE_MAX_M: the bandwidth-bound small-M GEMM.
+constexpr int64_t DECODE_MAX_M = 64;
+
+hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
+                              const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                              const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
+                              int64_t N, int64_t K, int num_cus, hipStream_t stream);
+
+hipError_t launch_gemm_prefill(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
+                               const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                               const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
+                               int64_t N, int64_t K, int num_cus, hipStream_t stream);
+
+}  // namespace bsg

@@ -1,0 +1,143 @@
+// The C ABI of include/bsgemm.h: host-side argument checks, a once-per-device
+// gfx950 gate, and dispatch to the kernels. Nothing here allocates or
+// synchronizes. The checks mirror the mono runner page's _check_tensors
+// (exact shapes and strides are validated because the kernels' loads are
+// unbounded) and the flash-rt groot_n17 frontend's architecture gate (a
+// mismatched device would compute garbage, so it is refused).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "bs_kernels.hpp"
+#include "bsgemm.h"
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+// per device: 0 unknown, 1 gfx950, 2 refused; plus its CU count
+std::atomic<int> g_arch_state[MAX_DEVICES];
+std::atomic<int> g_num_cus[MAX_DEVICES];
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int device_check(int *num_cus) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return BS_EARCH;
+    int st = g_arch_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BS_EARCH;
+        // gcnArchName is e.g. "gfx950:sramecc+:xnack-": compare the base target
+        const char *name = prop.gcnArchName;
+        const bool ok = std::strncmp(name, "gfx950", 6) == 0 && (name[6] == '\0' || name[6] == ':');
+        g_num_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+        st = ok ? 1 : 2;
+        g_arch_state[dev].store(st, std::memory_order_release);
+    }
+    *num_cus = g_num_cus[dev].load(std::memory_order_relaxed);
+    return st == 1 ? BS_OK : BS_EARCH;
+}
+
+// Shared checks of the two GEMM entry points. `w_row_bytes` is the minimum
+// row stride of W in bytes (K for e4m3, K/2 for fp4x2).
+int check_gemm(const void *a, int64_t ld_a, const float *a_scale, const void *w, int64_t ld_w,
+               int64_t w_row_bytes, const uint8_t *w_scale, const void *bias, int epilogue,
+               const void *y, int64_t ld_y, int64_t M, int64_t N, int64_t K, size_t ws_bytes,
+               size_t ws_need) {
+    if (!a || !a_scale || !w || !w_scale || !y) return BS_EINVAL;
+    if (M < 1 || N < 32 || K < 32 || N % 32 || K % 32) return BS_EINVAL;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return BS_EINVAL;
+    if (epilogue < BS_EPI_NONE || epilogue > BS_EPI_BIAS_GELU_TANH) return BS_EINVAL;
+    if (epilogue != BS_EPI_NONE && !bias) return BS_EINVAL;
+    if (ld_a < K || ld_w < w_row_bytes || ld_y < N) return BS_EINVAL;
+    if (!aligned16(a) || !aligned16(w) || !aligned16(y)) return BS_EALIGN;
+    if (ld_a % 16 || ld_w % 16 || (2 * ld_y) % 16) return BS_EALIGN;
+    if ((reinterpret_cast<uintptr_t>(a_scale) & 3u) != 0) return BS_EALIGN;
+    if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u) != 0) return BS_EALIGN;
+    if (ws_bytes < ws_need) return BS_EWORKSPACE;
+    return BS_OK;
+}
+
+int gemm_common(bool fp4, const void *a_e4m3, int64_t ld_a, const float *a_scale, const void *w,
+                int64_t ld_w, const uint8_t *w_scale, const void *bias_bf16, int epilogue,
+                void *y_bf16, int64_t ld_y, int64_t M, int64_t N, int64_t K, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    (void)workspace;
+    const int64_t w_row = fp4 ? K / 2 : K;
+    int st = check_gemm(a_e4m3, ld_a, a_scale, w, ld_w, w_row, w_scale, bias_bf16, epilogue,
+                        y_bf16, ld_y, M, N, K, workspace_bytes,
+                        bs_workspace_bytes(fp4 ? 1 : 0, M, N, K));
+    if (st != BS_OK) return st;
+    int num_cus = 0;
+    if ((st = device_check(&num_cus)) != BS_OK) return st;
+    const auto *a = static_cast<const uint8_t *>(a_e4m3);
+    const auto *wb = static_cast<const uint8_t *>(w);
+    const auto *bias = static_cast<const uint16_t *>(bias_bf16);
+    auto *y = static_cast<uint16_t *>(y_bf16);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (M <= bsg::DECODE_MAX_M)
+        e = bsg::launch_gemm_decode(fp4, a, ld_a, a_scale, wb, ld_w, w_scale, bias, epilogue, y,
+                                    ld_y, M, N, K, num_cus, s);
+    else
+        e = bsg::launch_gemm_prefill(fp4, a, ld_a, a_scale, wb, ld_w, w_scale, bias, epilogue, y,
+                                     ld_y, M, N, K, num_cus, s);
+    return e == hipSuccess ? BS_OK : BS_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_quant_rows(const void *x_bf16, int64_t ld_x, void *q_e4m3, int64_t ld_q, float *scale,
+                   int64_t M, int64_t K, void *stream) {
+    if (!x_bf16 || !q_e4m3 || !scale) return BS_EINVAL;
+    if (M < 1 || K < 32 || K % 32 || M > INT32_MAX || K > INT32_MAX) return BS_EINVAL;
+    if (ld_x < K || ld_q < K) return BS_EINVAL;
+    if (!aligned16(x_bf16) || !aligned16(q_e4m3) || (2 * ld_x) % 16 || ld_q % 16)
+        return BS_EALIGN;
+    if ((reinterpret_cast<uintptr_t>(scale) & 3u) != 0) return BS_EALIGN;
+    int num_cus = 0;
+    int st = device_check(&num_cus);
+    if (st != BS_OK) return st;
+    hipError_t e = bsg::launch_quant_rows(static_cast<const uint16_t *>(x_bf16), ld_x,
+                                          static_cast<uint8_t *>(q_e4m3), ld_q, scale, M, K,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BS_OK : BS_ELAUNCH;
+}
+
+int gemm_bs_fp8(const void *a_e4m3, int64_t ld_a, const float *a_scale, const void *w_e4m3,
+                int64_t ld_w, const uint8_t *w_scale, const void *bias_bf16, int epilogue,
+                void *y_bf16, int64_t ld_y, int64_t M, int64_t N, int64_t K, void *workspace,
+                size_t workspace_bytes, void *stream) {
+    return gemm_common(false, a_e4m3, ld_a, a_scale, w_e4m3, ld_w, w_scale, bias_bf16, epilogue,
+                       y_bf16, ld_y, M, N, K, workspace, workspace_bytes, stream);
+}
+
+int gemm_mxfp4_w4a8(const void *a_e4m3, int64_t ld_a, const float *a_scale, const void *w_fp4x2,
+                    int64_t ld_w, const uint8_t *w_scale, const void *bias_bf16, int epilogue,
+                    void *y_bf16, int64_t ld_y, int64_t M, int64_t N, int64_t K, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    return gemm_common(true, a_e4m3, ld_a, a_scale, w_fp4x2, ld_w, w_scale, bias_bf16, epilogue,
+                       y_bf16, ld_y, M, N, K, workspace, workspace_bytes, stream);
+}
+
+size_t bs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
+    (void)op; (void)M; (void)N; (void)K;
+    return 0;  // every kernel reduces within a workgroup
+}
+
+const char *bs_status_string(int status) {
+    switch (status) {
+    case BS_OK: return "ok";
+    case BS_EINVAL: return "invalid argument (size, leading dimension, epilogue or null pointer)";
+    case BS_EALIGN: return "pointer or leading dimension not 16-byte aligned";
+    case BS_EARCH: return "no HIP device, or the current device is not gfx950";
+    case BS_EWORKSPACE: return "workspace smaller than bs_workspace_bytes()";
+    case BS_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+// Per-token activation quantization to e4m3fn: one fp32 scale per row
+// (amax / 448) and the row's codes, in one HBM pass over the bf16 input.
+// The "(q_fp8, scale)" pair is what the sly-radiance README's fused
+// producers hand to its W4A8 GEMM (fused norm/quant rows of its file table).
+#include "bs_device.hpp"
+#include "bs_kernels.hpp"
+
+namespace bsg {
+namespace {
+
+constexpr int QBLOCK = 256;
+
+// Largest |bf16| of the 8 values in a 16-byte chunk, as a magnitude bit
+// pattern (for finite values, integer order of exp|mantissa = value order).
+__device__ __forceinline__ uint32_t absmax8(const uint4 &c) {
+    uint32_t m = 0;
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m = max(m, w[i] & 0x7FFFu);
+        m = max(m, (w[i] >> 16) & 0x7FFFu);
+    }
+    return m;
+}
+
+// Codes of the 16 bf16 values in two 16-byte chunks, packed little-endian.
+__device__ __forceinline__ uint4 encode16(const uint4 &c0, const uint4 &c1, float s) {
+    const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = w[i] & 0xFFFFu, hi = w[i] >> 16;
+        uint32_t clo, chi;
+        if (s == 0.0f) {  // an all-zero row: signed zeros
+            clo = (lo >> 8) & 0x80u;
+            chi = (hi >> 8) & 0x80u;
+        } else {
+            clo = e4m3_encode(bf16_to_f32(lo) / s);
+            chi = e4m3_encode(bf16_to_f32(hi) / s);
+        }
+        out[i >> 1] |= (clo | (chi << 8)) << (16 * (i & 1));
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+__device__ __forceinline__ uint32_t group_max(uint32_t v, int width) {
+    for (int off = width / 2; off > 0; off >>= 1)
+        v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+    return v;
+}
+
+// TPR threads per row (16, 64 or 256); each holds NCH chunks of 16 values
+// in registers between the max reduction and the encode.
+template <int TPR, int NCH>
+__global__ __launch_bounds__(QBLOCK) void quant_rows_kernel(const uint16_t *__restrict__ x,
+                                                            int64_t ldx, uint8_t *__restrict__ q,
+                                                            int64_t ldq, float *__restrict__ scale,
+                                                            int64_t M, int K) {
+    constexpr int RPB = QBLOCK / TPR;
+    const int tid = threadIdx.x;
+    const int t = tid % TPR;
+    const int64_t m = (int64_t)blockIdx.x * RPB + tid / TPR;
+    const bool active = m < M;
+    const int nch = K >> 4;
+    const uint16_t *xr = x + (active ? m : 0) * ldx;
+
+    uint4 v[NCH][2];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int c = t + i * TPR;
+        if (active && c < nch) {
+            v[i][0] = ldg16(xr + 16 * c);
+            v[i][1] = ldg16(xr + 16 * c + 8);
+            amax = max(amax, max(absmax8(v[i][0]), absmax8(v[i][1])));
+        } else {
+            v[i][0] = v[i][1] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    if (TPR <= 64) {
+        amax = group_max(amax, TPR);
+    } else {
+        __shared__ uint32_t red[QBLOCK / 64];
+        amax = group_max(amax, 64);
+        if ((tid & 63) == 0) red[tid >> 6] = amax;
+        __syncthreads();
+        amax = red[0];
+#pragma unroll
+        for (int i = 1; i < QBLOCK / 64; ++i) amax = max(amax, red[i]);
+    }
+    const float s = bf16_to_f32(amax) / 448.0f;  // correctly rounded fp32 division
+    if (!active) return;
+    if (t == 0) scale[m] = s;
+    uint8_t *qr = q + m * ldq;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int c = t + i * TPR;
+        if (c < nch) *reinterpret_cast<uint4 *>(qr + 16 * c) = encode16(v[i][0], v[i][1], s);
+    }
+}
+
+// Rows too long to hold in registers: a max pass, then a second read that
+// encodes (the row is hot in L2 by then). One block of QBLOCK per row.
+__global__ __launch_bounds__(QBLOCK) void quant_rows_long_kernel(const uint16_t *__restrict__ x,
+                                                                 int64_t ldx,
+                                                                 uint8_t *__restrict__ q,
+                                                                 int64_t ldq,
+                                                                 float *__restrict__ scale,
+                                                                 int64_t M, int K) {
+    const int64_t m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nch = K >> 4;
+    const uint16_t *xr = x + m * ldx;
+    uint32_t amax = 0;
+    for (int c = tid; c < nch; c += QBLOCK)
+        amax = max(amax, max(absmax8(ldg16(xr + 16 * c)), absmax8(ldg16(xr + 16 * c + 8))));
+    __shared__ uint32_t red[QBLOCK / 64];
+    amax = group_max(amax, 64);
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = red[0];
+    for (int i = 1; i < QBLOCK / 64; ++i) amax = max(amax, red[i]);
+    const float s = bf16_to_f32(amax) / 448.0f;
+    if (tid == 0) scale[m] = s;
+    uint8_t *qr = q + m * ldq;
+    for (int c = tid; c < nch; c += QBLOCK)
+        *reinterpret_cast<uint4 *>(qr + 16 * c) =
+            encode16(ldg16(xr + 16 * c), ldg16(xr + 16 * c + 8), s);
+}
+
+template <int TPR, int NCH>
+void launch(const uint16_t *x, int64_t ldx, uint8_t *q, int64_t ldq, float *s, int64_t M, int K,
+            hipStream_t st) {
+    constexpr int RPB = QBLOCK / TPR;
+    const dim3 grid((unsigned)((M + RPB - 1) / RPB));
+    hipLaunchKernelGGL((quant_rows_kernel<TPR, NCH>), grid, dim3(QBLOCK), 0, st, x, ldx, q, ldq, s,
+                       M, K);
+}
+
+template <int TPR>
+bool launch_tpr(int nch_per_thread, const uint16_t *x, int64_t ldx, uint8_t *q, int64_t ldq,
+                float *s, int64_t M, int K, hipStream_t st) {
+    if (nch_per_thread <= 1) launch<TPR, 1>(x, ldx, q, ldq, s, M, K, st);
+    else if (nch_per_thread <= 2) launch<TPR, 2>(x, ldx, q, ldq, s, M, K, st);
+    else if (nch_per_thread <= 4) launch<TPR, 4>(x, ldx, q, ldq, s, M, K, st);
+    else if (nch_per_thread <= 8) launch<TPR, 8>(x, ldx, q, ldq, s, M, K, st);
+    else if (nch_per_thread <= 16) launch<TPR, 16>(x, ldx, q, ldq, s, M, K, st);
+    else return false;
+    return true;
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_t ld_q,
+                             float *scale, int64_t M, int64_t K, hipStream_t stream) {
+    const int k = (int)K;
+    const int nch = k / 16;
+    // Many rows: a few threads per row is enough to fill the chip; few
+    // rows: spread each row over a whole block to cut latency.
+    int tpr = M >= 512 ? 64 : 256;
+    if (nch <= 16) tpr = 16;
+    else if (nch <= 64) tpr = 64;
+    const int per = (nch + tpr - 1) / tpr;
+    bool ok;
+    if (tpr == 16) ok = launch_tpr<16>(per, x, ld_x, q, ld_q, scale, M, k, stream);
+    else if (tpr == 64) ok = launch_tpr<64>(per, x, ld_x, q, ld_q, scale, M, k, stream);
+    else ok = launch_tpr<256>(per, x, ld_x, q, ld_q, scale, M, k, stream);
+    if (!ok)
+        hipLaunchKernelGGL(quant_rows_long_kernel, dim3((unsigned)M), dim3(QBLOCK), 0, stream, x,
+                           ld_x, q, ld_q, scale, M, k);
+    return hipGetLastError();
+}
+
+}  // namespace bsg

@@ -1,0 +1,111 @@
+"""Host-side checks of the C ABI, runnable without a GPU: the library loads,
+exports every function include/bsgemm.h declares, and rejects bad arguments
+on the host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_gemm_transformer_amd as bs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "bsgemm.h")
+
+# A 16-byte-aligned fake address: only ever passed to calls that must fail
+# validation, which happens before any device access.
+FAKE = ctypes.c_void_p(0x10000)
+
+
+def _declared():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared() == sorted(bs.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bs.load_library()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_workspace():
+    for st in (0, -1, -2, -3, -4, -5):
+        assert bs.bs_status_string(st)
+    assert bs.bs_status_string(7) == "unknown status"
+    assert bs.bs_workspace_bytes(0, 8, 2048, 7168) == 0
+    assert bs.bs_workspace_bytes(1, 4096, 34816, 5120) == 0
+
+
+def _gemm(fn, a=FAKE, lda=64, s=FAKE, w=FAKE, ldw=64, ws=FAKE, bias=None, epi=0, y=FAKE, ldy=64,
+          M=8, N=64, K=64, work=None, work_bytes=0):
+    return fn(a, lda, s, w, ldw, ws, bias, epi, y, ldy, M, N, K, work, work_bytes, None)
+
+
+@pytest.mark.parametrize("name", ["gemm_bs_fp8", "gemm_mxfp4_w4a8"])
+def test_gemm_argument_checks(name):
+    lib = bs.load_library()
+    fn = getattr(lib, name)
+    E = bs.BS_EINVAL
+    assert _gemm(fn, a=None) == E
+    assert _gemm(fn, s=None) == E
+    assert _gemm(fn, w=None) == E
+    assert _gemm(fn, ws=None) == E
+    assert _gemm(fn, y=None) == E
+    assert _gemm(fn, M=0) == E
+    assert _gemm(fn, N=48) == E                    # N % 32
+    assert _gemm(fn, K=80) == E                    # K % 32
+    assert _gemm(fn, N=0) == E
+    assert _gemm(fn, epi=3) == E
+    assert _gemm(fn, epi=-1) == E
+    assert _gemm(fn, epi=1) == E                   # bias required
+    assert _gemm(fn, epi=2) == E
+    assert _gemm(fn, lda=32) == E                  # ld_a < K
+    assert _gemm(fn, ldy=32) == E                  # ld_y < N
+    assert _gemm(fn, ldw=16) == E                  # ld_w < row bytes
+    A = bs.BS_EALIGN
+    assert _gemm(fn, a=ctypes.c_void_p(0x10008)) == A
+    assert _gemm(fn, w=ctypes.c_void_p(0x10004)) == A
+    assert _gemm(fn, y=ctypes.c_void_p(0x10002)) == A
+    assert _gemm(fn, lda=72) == A
+    assert _gemm(fn, ldw=72) == A
+    assert _gemm(fn, ldy=68) == A
+    assert _gemm(fn, s=ctypes.c_void_p(0x10002)) == A
+    assert _gemm(fn, bias=ctypes.c_void_p(0x10001), epi=1) == A
+
+
+def test_quant_argument_checks():
+    lib = bs.load_library()
+    q = lambda x=FAKE, ldx=64, qq=FAKE, ldq=64, s=FAKE, M=4, K=64: lib.fp8_quant_rows(x, ldx, qq, ldq, s, M, K, None)
+    assert q(x=None) == bs.BS_EINVAL
+    assert q(qq=None) == bs.BS_EINVAL
+    assert q(s=None) == bs.BS_EINVAL
+    assert q(M=0) == bs.BS_EINVAL
+    assert q(K=48) == bs.BS_EINVAL
+    assert q(K=0) == bs.BS_EINVAL
+    assert q(ldx=32) == bs.BS_EINVAL
+    assert q(ldq=32) == bs.BS_EINVAL
+    assert q(x=ctypes.c_void_p(0x10008)) == bs.BS_EALIGN
+    assert q(qq=ctypes.c_void_p(0x10001)) == bs.BS_EALIGN
+    assert q(ldx=68) == bs.BS_EALIGN
+    assert q(ldq=72) == bs.BS_EALIGN
+    assert q(s=ctypes.c_void_p(0x10002)) == bs.BS_EALIGN
+
+
+def test_valid_call_without_a_gpu_is_refused_by_the_arch_gate():
+    import subprocess
+    import sys
+    # Run in a child with no visible devices so a GPU machine never launches on
+    # the fake addresses: the gate must answer BS_EARCH before any launch.
+    code = ("import ctypes,sys; sys.path.insert(0, %r); import mxfp4_gemm_transformer_amd as bs;"
+            "lib=bs.load_library(); F=ctypes.c_void_p(0x10000);"
+            "print(lib.fp8_quant_rows(F,64,F,64,F,4,64,None),"
+            " lib.gemm_bs_fp8(F,64,F,F,64,F,None,0,F,64,8,64,64,None,0,None))") % ROOT
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1",
+               CUDA_VISIBLE_DEVICES="-1")
+    out = subprocess.check_output([sys.executable, "-c", code], env=env, text=True, timeout=120)
+    assert out.split() == [str(bs.BS_EARCH)] * 2
