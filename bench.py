@@ -1,0 +1,249 @@
+"""Benchmark of the block-scaled linear layer on one MI355X.
+
+A step is one pass of the whole path over one batch: per-token quantization
+of bf16 activations (fp8_quant_rows) followed by the block-scaled GEMM with
+its fused epilogue (gemm_bs_fp8 / gemm_mxfp4_w4a8). Inputs are resident in
+HBM before timing starts. Weights rotate over >= 512 MiB of distinct copies
+(twice the 256 MiB last-level cache), one copy per step, so every step reads
+its weights from HBM as a real layer stack would.
+
+Timed steps are captured once into a HIP graph and replayed, so the timing
+is of GPU work, not of Python launch overhead. Output: one JSON line with
+the throughput of the whole step, the roofline of the dominant kernel (its
+algorithmic bytes or FLOPs per launch over its average launch time from HIP
+events), and the CPU oracle's rate on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode --m 8]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-scaled GEMM TFLOP/s (prefill) + HBM GB/s (decode), % roofline, 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
+FP4_PEAK_TFLOPS = 10100.0      # dense MXFP4 MFMA
+ROTATION_BYTES = 512 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=None)
+    p.add_argument("--workload", default="decode",
+                   choices=["tiny", "decode", "prefill", "ffn_up", "ffn_up_bias", "gate_up"])
+    p.add_argument("--m", type=int, default=None, help="token count (M) for sweep workloads")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="CPU oracle budget for the cpu_baseline leg (0 disables it)")
+    return p.parse_args()
+
+
+def algorithmic(wl, M):
+    """Bytes each kernel must move and the GEMM's FLOPs, by definition."""
+    N, K = wl.N, wl.K
+    quant = 2 * M * K + M * K + 4 * M                      # bf16 in, codes + scales out
+    w_bytes = N * K if wl.fmt == "fp8" else N * K // 2
+    ws_bytes = (N // 32) * (K // 32) if wl.fmt == "fp8" else N * (K // 32)
+    gemm = w_bytes + ws_bytes + M * K + 4 * M + 2 * M * N
+    if wl.epilogue:
+        gemm += 2 * N
+    return {"quant_bytes": quant, "gemm_bytes": gemm, "gemm_flops": 2 * M * N * K}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the layer's kernels run on one device and this "
+              "build has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mxfp4_gemm_transformer_amd as bs
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    M = args.m if args.m is not None else wl.M
+    big = 2 * M * wl.N * wl.K > 50e9
+    steps = args.steps if args.steps is not None else (50 if big else 1000)
+    warmup = args.warmup if args.warmup is not None else (5 if big else 50)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs, resident in HBM
+    d = synth.make(args.workload, M)
+    x = torch.from_numpy(d["a_bf16"].view(np.int16)).view(torch.bfloat16).to(dev)
+    w_host, ws_host = d["w"], d["w_scale"]
+    w_bytes = w_host.nbytes + ws_host.nbytes
+    copies = max(2, math.ceil(ROTATION_BYTES / w_bytes))
+    w0 = torch.from_numpy(w_host).to(dev)
+    ws0 = torch.from_numpy(ws_host).to(dev)
+    ws_list = [w0] + [w0.clone() for _ in range(copies - 1)]
+    wss_list = [ws0] + [ws0.clone() for _ in range(copies - 1)]
+    bias = None
+    if d["bias"] is not None:
+        bias = torch.from_numpy(d["bias"].view(np.int16)).view(torch.bfloat16).to(dev)
+    epi = d["epilogue"]
+    q = torch.empty((M, wl.K), dtype=torch.uint8, device=dev)
+    s = torch.empty((M,), dtype=torch.float32, device=dev)
+    y = torch.empty((M, wl.N), dtype=torch.bfloat16, device=dev)
+    gemm = bs.gemm_bs_fp8 if wl.fmt == "fp8" else bs.gemm_mxfp4_w4a8
+    work = None
+    need = bs.bs_workspace_bytes(0 if wl.fmt == "fp8" else 1, M, wl.N, wl.K)
+    if need:
+        work = torch.zeros((need,), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        bs.fp8_quant_rows(x, q, s)
+        gemm(q, s, ws_list[i % copies], wss_list[i % copies], bias, epi, y=y, workspace=work)
+
+    def gemm_only(i):
+        gemm(q, s, ws_list[i % copies], wss_list[i % copies], bias, epi, y=y, workspace=work)
+
+    def quant_only(i):
+        bs.fp8_quant_rows(x, q, s)
+
+    stream = torch.cuda.Stream()
+
+    def capture(fn, count, offset=0):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(count):
+                fn(offset + i)
+        return g
+
+    # ---- warmup: eager steps, then the captured graphs' first replays
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step(i)
+    torch.cuda.synchronize()
+    g_step = capture(step, steps)
+    g_gemm = capture(gemm_only, steps)
+    g_quant = capture(quant_only, steps)
+    for g in (g_step, g_gemm, g_quant):
+        g.replay()
+    torch.cuda.synchronize()
+
+    def timed(g):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3      # seconds
+
+    # ---- the timed K steps (whole path), then per-kernel averages
+    t0 = time.perf_counter()
+    step_s = timed(g_step)
+    wall_s = time.perf_counter() - t0
+    gemm_s = timed(g_gemm) / steps
+    quant_s = timed(g_quant) / steps
+
+    alg = algorithmic(wl, M)
+    step_bytes = alg["quant_bytes"] + alg["gemm_bytes"]
+    ms_per_step = step_s / steps * 1e3
+    compute_bound = alg["gemm_flops"] / alg["gemm_bytes"] > 1000.0
+    if compute_bound:
+        unit = "TFLOP/s"
+        value = alg["gemm_flops"] * steps / step_s / 1e12
+        peak = FP4_PEAK_TFLOPS if wl.fmt == "mxfp4" else FP8_PEAK_TFLOPS
+        achieved = alg["gemm_flops"] / gemm_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+        if wl.fmt == "mxfp4":
+            roof["frac_vs_fp8_rate"] = round(achieved / FP8_PEAK_TFLOPS, 4)
+    else:
+        unit = "GB/s"
+        value = step_bytes * steps / step_s / 1e9
+        achieved = alg["gemm_bytes"] / gemm_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = "gemm_mxfp4_w4a8" if wl.fmt == "mxfp4" else "gemm_bs_fp8"
+    roof["avg_launch_us"] = round(gemm_s * 1e6, 3)
+    roof["algorithmic_bytes_per_launch"] = alg["gemm_bytes"]
+    roof["algorithmic_flops_per_launch"] = alg["gemm_flops"]
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3" if wl.fmt == "fp8" else "fp8_e4m3 x fp4_e2m1",
+        "data": "synthetic",
+        "config": {"workload": "%s M=%d N=%d K=%d (%s weights, %s scales, epilogue %s)" % (
+            wl.name, M, wl.N, wl.K, "e4m3" if wl.fmt == "fp8" else "MXFP4 e2m1",
+            "32x32 E8M0" if wl.fmt == "fp8" else "1x32 E8M0",
+            ["none", "bias", "bias+tanh-GELU"][epi]),
+            "M": M, "N": wl.N, "K": wl.K, "weight_copies_rotated": copies,
+            "step": "fp8_quant_rows + %s" % roof["kernel"], "graph_replay": True},
+        "roofline": roof,
+        "kernels_us": {"fp8_quant_rows": round(quant_s * 1e6, 3), roof["kernel"]: round(gemm_s * 1e6, 3)},
+        "step_bytes": step_bytes, "wall_s_timed_region": round(wall_s, 6),
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(d, wl, M, alg, compute_bound, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+def cpu_baseline(d, wl, M, alg, compute_bound, budget_s):
+    """The CPU oracle, as it stands, on the same workload: quantization then
+    the GEMM in fp64 with OpenMP over outputs. Large workloads run a bounded
+    sample of output rows (all N columns of those rows)."""
+    import oracle
+    oracle.build()
+    a_bits = d["a_bf16"]
+    # rows so that one pass is about a second of work at ~1 GMAC/s/thread
+    macs_per_row = wl.N * wl.K
+    rows = max(1, min(M, int(2e9 / macs_per_row)))
+    sample = a_bits[:rows]
+    runs, t_total = 0, 0.0
+    while t_total < budget_s or runs == 0:
+        t0 = time.perf_counter()
+        q, s = oracle.quant_rows(sample)
+        if wl.fmt == "fp8":
+            oracle.gemm_bs_fp8(q, s, d["w"], d["w_scale"], d["bias"], d["epilogue"])
+        else:
+            oracle.gemm_mxfp4_w4a8(q, s, d["w"], d["w_scale"], d["bias"], d["epilogue"])
+        t_total += time.perf_counter() - t0
+        runs += 1
+        if t_total > 3 * budget_s:
+            break
+    frac = rows / M
+    if compute_bound:
+        value, unit = alg["gemm_flops"] * frac * runs / t_total / 1e12, "TFLOP/s"
+    else:
+        step_bytes = (alg["quant_bytes"] + alg["gemm_bytes"] - d["w"].nbytes - d["w_scale"].nbytes) \
+            * frac + d["w"].nbytes + d["w_scale"].nbytes
+        value, unit = step_bytes * runs / t_total / 1e9, "GB/s"
+    return {"value": round(value, 4), "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d token rows (all %d outputs each), %d passes of quantize + GEMM + "
+                      "epilogue in %.1f s" % (rows, M, wl.N, runs, t_total),
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+if __name__ == "__main__":
+    main()

@@ -4,84 +4,174 @@
 // per-lane scale operand, one per 32-element K block, so a K step is MFMAs
 // only, and the per-token fp32 activation scale is applied in the epilogue.
 //
-// Tiling: a BM x BN output tile per workgroup of 4 waves in a 2 x 2 grid,
-// each wave owning (BM/2) x (BN/2) as 32x32 MFMA tiles. K advances 128 at a
-// time through two LDS stages: while the MFMAs consume one stage, the next
-// step's A and W tiles are fetched into registers and written to the other
-// stage. LDS rows are 16-byte chunks XOR-swizzled by row so that the 32
-// lanes reading one chunk column hit different banks.
+// Tiling: a BM x BN output tile per workgroup of four waves in a WGM x WGN
+// grid; each wave owns (BM/WGM) x (BN/WGN) as 32x32 MFMA tiles, which keeps
+// the LDS bytes read per MFMA low. K advances 64 at a time through a
+// software pipeline: while the MFMAs of step s run, the wave reads step
+// s+1's fragments from LDS into a second register set, writes step s+2's
+// tiles (fetched into registers during step s-1) into the third LDS buffer,
+// and fetches step s+3; those instructions are interleaved with the MFMAs so
+// the matrix core stays fed, and one barrier per step publishes the writes.
+// The fetches are buffer loads whose range check turns reads past the last
+// row or past K into zeros, so ragged M, N and K need no special path.
+//
+// LDS rows hold 16-byte chunks XOR-swizzled by row, so that the 32 lanes of
+// a fragment read (32 consecutive rows, one chunk column) spread over all
+// banks whether the LDS has 32 or 64 banks.
+//
+// Workgroups are numbered so that consecutive tiles in a grouped order land
+// on the same XCD (workgroups are dispatched round-robin over the 8 XCDs),
+// which keeps the A and W panels a group shares in that XCD's L2.
 #include "bs_device.hpp"
 #include "bs_kernels.hpp"
 
 namespace bsg {
 namespace {
 
-constexpr int PBLOCK = 256;
-constexpr int BK = 128;
+constexpr int BK = 64;
+constexpr int NXCD = 8;
 
-template <bool FP4, int BM, int BN>
-struct PrefillCfg {
-    static constexpr int WBYTES = FP4 ? BK / 2 : BK;   // weight bytes per row per K step
-    static constexpr int ACH = BK / 16;                // 16-byte chunks per A row
-    static constexpr int WCH = WBYTES / 16;            // chunks per W row
-    static constexpr int A_STAGE = BM * BK;
-    static constexpr int W_STAGE = BN * WBYTES;
-    static constexpr int LDS = 2 * (A_STAGE + W_STAGE);
-    static constexpr int A_PER_T = BM * ACH / PBLOCK;  // chunks each thread copies
-    static constexpr int W_PER_T = BN * WCH / PBLOCK;
-    static constexpr int TM = BM / 2 / 32, TN = BN / 2 / 32;
-    static_assert(BM * ACH % PBLOCK == 0 && BN * WCH % PBLOCK == 0, "tile / block mismatch");
+template <bool FP4, int BM, int BN, int WGM, int WGN>
+struct Cfg {
+    static constexpr int NW = WGM * WGN;
+    static constexpr int NT = NW * 64;
+    static constexpr int AROW = BK;                   // A bytes per row per step
+    static constexpr int WROW = FP4 ? BK / 2 : BK;    // W bytes per row per step
+    static constexpr int A_STAGE = BM * AROW;
+    static constexpr int W_STAGE = BN * WROW;
+    static constexpr int STAGE = A_STAGE + W_STAGE;
+    static constexpr int A_LD = A_STAGE / 16 / NT;    // 16-byte chunks per thread per step
+    static constexpr int W_LD = W_STAGE / 16 / NT;
+    static constexpr int TM = BM / WGM / 32;
+    static constexpr int TN = BN / WGN / 32;
+    // E8M0 scales of this tile's weight rows for SC_KB consecutive K blocks
+    // (SC_KB * 32 = 4096 K) at a time: one byte per 32x32 block row for e4m3
+    // weights, one per row for MXFP4
+    static constexpr int SC_KB = 128;
+    static constexpr int SC_ROWS = FP4 ? BN : BN / 32;
+    static constexpr int SC_BYTES = SC_ROWS * SC_KB;
+    static constexpr int NBUF = 3;                    // LDS buffers in the ring
+    static constexpr int LDS = NBUF * STAGE + SC_BYTES;
+    static_assert(A_STAGE % (16 * NT) == 0 && W_STAGE % (16 * NT) == 0, "stage split");
+    static_assert(TM >= 1 && TN >= 1, "wave tile");
+    static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <bool FP4, int BM, int BN>
-__global__ __launch_bounds__(PBLOCK) void gemm_prefill_kernel(
+// Swizzle of the 16-byte chunk column within a 64-byte row (4 chunks) and a
+// 32-byte row (2 chunks).
+__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz2(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
+__device__ __forceinline__ uint4 lds16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+constexpr uint32_t OOB = 0x80000000u;  // an offset past every buffer: reads as zero
+
+template <bool FP4, int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
     const uint8_t *__restrict__ A, int64_t lda, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ W, int64_t ldw, const uint8_t *__restrict__ WS,
     const uint16_t *__restrict__ bias, int epi, uint16_t *__restrict__ Y, int64_t ldy, int M, int N,
-    int K) {
-    using C = PrefillCfg<FP4, BM, BN>;
-    extern __shared__ __align__(16) uint8_t lds[];
-    uint8_t *sA = lds;                      // [2][BM][BK]
-    uint8_t *sW = lds + 2 * C::A_STAGE;     // [2][BN][WBYTES]
+    int K, int group_m) {
+    using C = Cfg<FP4, BM, BN, WGM, WGN>;
+    static_assert(C::NT == 256, "launch bounds assume four waves");
+    __shared__ __align__(16) uint8_t lds[C::NBUF * C::STAGE];
+    __shared__ __align__(16) uint8_t sscale[C::SC_BYTES];
+
+    // ---- tile of this workgroup (XCD-aware grouped order)
+    const int Mt = (M + BM - 1) / BM, Nt = (N + BN - 1) / BN, T = Mt * Nt;
+    int t = blockIdx.x;
+    if (T % NXCD == 0) t = (t % NXCD) * (T / NXCD) + t / NXCD;
+    const int per_group = group_m * Nt;
+    const int first_m = (t / per_group) * group_m;
+    const int gm = min(Mt - first_m, group_m);
+    const int m0 = (first_m + (t % per_group) % gm) * BM;
+    const int n0 = ((t % per_group) / gm) * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     const int li = lane & 31, lg = lane >> 5;
-    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
     const int KB = K >> 5;
     const int nsteps = (K + BK - 1) / BK;
 
-    // ---- global -> register copy of one K step
-    uint4 ra[C::A_PER_T], rw[C::W_PER_T];
-    auto fetch = [&](int s) {
-        const int kbase = s * BK;
+    // buffer descriptors over the rows from this tile on; rows past M / N
+    // are outside num_records and read as zero
+    const int64_t a_bytes = (int64_t)(M - m0) * lda, w_bytes = (int64_t)(N - n0) * ldw;
+    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A + (int64_t)m0 * lda), (short)0, (int)(a_bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : a_bytes),
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(W + (int64_t)n0 * ldw), (short)0, (int)(w_bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : w_bytes),
+        0x00020000);
+
+    // This thread's 16-byte chunks of a step: physical chunk P = j*NT + tid of
+    // the LDS stage holds logical chunk c of row P / (chunks per row).
+    uint32_t a_off[C::A_LD], w_off[C::W_LD];
+    int a_k[C::A_LD], w_k[C::W_LD];
 #pragma unroll
-        for (int j = 0; j < C::A_PER_T; ++j) {
-            const int c = tid + j * PBLOCK, row = c / C::ACH, ch = c % C::ACH;
-            const int64_t m = m0 + row;
-            const int k = kbase + ch * 16;
-            ra[j] = (m < M && k < K) ? ldg16(A + m * lda + k) : make_uint4(0u, 0u, 0u, 0u);
-        }
+    for (int j = 0; j < C::A_LD; ++j) {
+        const int P = j * C::NT + tid;
+        const int row = P >> 2, c = (P & 3) ^ swz4(row);
+        a_off[j] = (uint32_t)(row * lda) + 16 * c;
+        a_k[j] = 16 * c;
+    }
 #pragma unroll
-        for (int j = 0; j < C::W_PER_T; ++j) {
-            const int c = tid + j * PBLOCK, row = c / C::WCH, ch = c % C::WCH;
-            const int64_t n = n0 + row;
-            const int k = kbase + ch * (FP4 ? 32 : 16);    // first element of the chunk
-            rw[j] = (n < N && k < K) ? ldg16(W + n * ldw + (FP4 ? k / 2 : k))
-                                     : make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < C::W_LD; ++j) {
+        const int P = j * C::NT + tid;
+        if (FP4) {
+            const int row = P >> 1, c = (P & 1) ^ swz2(row);
+            w_off[j] = (uint32_t)(row * ldw) + 16 * c;
+            w_k[j] = 32 * c;
+        } else {
+            const int row = P >> 2, c = (P & 3) ^ swz4(row);
+            w_off[j] = (uint32_t)(row * ldw) + 16 * c;
+            w_k[j] = 16 * c;
         }
+    }
+
+    struct Regs {
+        uint4 a[C::A_LD];
+        uint4 w[C::W_LD];
     };
-    auto stash = [&](int buf) {
+    // past the last step the offsets are out of range and read zeros, so the
+    // fetch is unconditional and the compiler can count its loads exactly
+    auto fetch = [&](Regs &r, int s) {
+        const int kbase = s < nsteps ? s * BK : K;   // past the end: zeros
 #pragma unroll
-        for (int j = 0; j < C::A_PER_T; ++j) {
-            const int c = tid + j * PBLOCK, row = c / C::ACH, ch = c % C::ACH;
-            *reinterpret_cast<uint4 *>(sA + buf * C::A_STAGE + row * BK + ((ch ^ (row & 7)) << 4)) = ra[j];
-        }
+        for (int j = 0; j < C::A_LD; ++j)
+            r.a[j] = bload16(rsA, kbase + a_k[j] < K ? a_off[j] + kbase : OOB);
 #pragma unroll
-        for (int j = 0; j < C::W_PER_T; ++j) {
-            const int c = tid + j * PBLOCK, row = c / C::WCH, ch = c % C::WCH;
-            *reinterpret_cast<uint4 *>(sW + buf * C::W_STAGE + row * C::WBYTES +
-                                       ((ch ^ (row & (C::WCH - 1))) << 4)) = rw[j];
+        for (int j = 0; j < C::W_LD; ++j)
+            r.w[j] = bload16(rsW, kbase + w_k[j] < K ? w_off[j] + (FP4 ? kbase / 2 : kbase) : OOB);
+    };
+    auto stash = [&](const Regs &r, uint8_t *dst) {
+#pragma unroll
+        for (int j = 0; j < C::A_LD; ++j)
+            *reinterpret_cast<uint4 *>(dst + 16 * (j * C::NT + tid)) = r.a[j];
+#pragma unroll
+        for (int j = 0; j < C::W_LD; ++j)
+            *reinterpret_cast<uint4 *>(dst + C::A_STAGE + 16 * (j * C::NT + tid)) = r.w[j];
+    };
+    // scales of K blocks [kb0, kb0 + SC_KB) for this tile's rows -> LDS
+    auto load_scales = [&](int kb0) {
+        const int cols = min(C::SC_KB, KB - kb0);
+        for (int i = tid; i < C::SC_ROWS * C::SC_KB; i += C::NT) {
+            const int r = i / C::SC_KB, c = i % C::SC_KB;
+            uint8_t v = E8M0_ONE;
+            if (c < cols) {
+                if (FP4) {
+                    const int n = min(n0 + r, N - 1);
+                    v = WS[(int64_t)n * KB + kb0 + c];
+                } else {
+                    const int nb = min((n0 >> 5) + r, (N >> 5) - 1);
+                    v = WS[(int64_t)nb * KB + kb0 + c];
+                }
+            }
+            sscale[i] = v;
         }
     };
 
@@ -93,99 +183,130 @@ __global__ __launch_bounds__(PBLOCK) void gemm_prefill_kernel(
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
-    // weight rows of this lane's B fragments, for the scale lookups
-    const uint8_t *wsrow[C::TN];
+    struct Frags {
+        v8i a[C::TM];
+        v8i b[C::TN];
+        int sc[C::TN];
+    };
+    // fragments of step s from its LDS buffer (s % 3) and the scale chunk
+    auto read_frags = [&](Frags &f, int s) {
+        const uint8_t *sa = lds + (s % C::NBUF) * C::STAGE;
+        const uint8_t *sw = sa + C::A_STAGE;
+        const int kbl = ((2 * s) % C::SC_KB) + lg;  // this lane's K block within the chunk
 #pragma unroll
-    for (int b = 0; b < C::TN; ++b) {
-        int64_t n = n0 + wn * (BN / 2) + b * 32 + li;
-        if (n >= N) n = N - 1;
-        wsrow[b] = FP4 ? WS + n * KB : WS + (n >> 5) * KB;
-    }
-
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nsteps) fetch(s + 1);
-        const uint8_t *tA = sA + buf * C::A_STAGE;
-        const uint8_t *tW = sW + buf * C::W_STAGE;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            // this lane's scale block: k = s*128 + kk*64 + 32*lg
-            const int kb = s * 4 + kk * 2 + lg;
-            v8i af[C::TM], bf[C::TN];
-            int sc[C::TN];
-#pragma unroll
-            for (int a = 0; a < C::TM; ++a) {
-                const int row = wm * (BM / 2) + a * 32 + li;
-                const int c0 = kk * 4 + lg, c1 = kk * 4 + 2 + lg;
-                const uint8_t *base = tA + row * BK;
-                af[a] = pack8(*reinterpret_cast<const uint4 *>(base + ((c0 ^ (row & 7)) << 4)),
-                              *reinterpret_cast<const uint4 *>(base + ((c1 ^ (row & 7)) << 4)));
-            }
-#pragma unroll
-            for (int b = 0; b < C::TN; ++b) {
-                const int row = wn * (BN / 2) + b * 32 + li;
-                const uint8_t *base = tW + row * C::WBYTES;
-                if (FP4) {
-                    const int c0 = kk * 2 + lg;
-                    bf[b] = pack8(*reinterpret_cast<const uint4 *>(base + ((c0 ^ (row & 3)) << 4)),
-                                  make_uint4(0u, 0u, 0u, 0u));
-                } else {
-                    const int c0 = kk * 4 + lg, c1 = kk * 4 + 2 + lg;
-                    bf[b] = pack8(*reinterpret_cast<const uint4 *>(base + ((c0 ^ (row & 7)) << 4)),
-                                  *reinterpret_cast<const uint4 *>(base + ((c1 ^ (row & 7)) << 4)));
-                }
-                sc[b] = kb < KB ? wsrow[b][kb] : E8M0_ONE;
-            }
-#pragma unroll
-            for (int a = 0; a < C::TM; ++a)
-#pragma unroll
-                for (int b = 0; b < C::TN; ++b)
-                    acc[a][b] = mfma32<FP4>(af[a], bf[b], acc[a][b], E8M0_ONE, sc[b]);
+        for (int a = 0; a < C::TM; ++a) {
+            const int row = wm * (BM / WGM) + a * 32 + li;
+            const int fz = swz4(row);
+            const uint8_t *base = sa + row * C::AROW;
+            f.a[a] = pack8(lds16(base + 16 * (lg ^ fz)), lds16(base + 16 * ((2 + lg) ^ fz)));
         }
-        if (s + 1 < nsteps) {
-            __syncthreads();  // everyone is done reading the other stage
-            stash(buf ^ 1);
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b) {
+            const int row = wn * (BN / WGN) + b * 32 + li;
+            if (FP4) {
+                f.b[b] = pack8(lds16(sw + row * C::WROW + 16 * (lg ^ swz2(row))),
+                               make_uint4(0u, 0u, 0u, 0u));
+                f.sc[b] = sscale[row * C::SC_KB + kbl];
+            } else {
+                const int fz = swz4(row);
+                const uint8_t *base = sw + row * C::WROW;
+                f.b[b] = pack8(lds16(base + 16 * (lg ^ fz)), lds16(base + 16 * ((2 + lg) ^ fz)));
+                f.sc[b] = sscale[(row >> 5) * C::SC_KB + kbl];
+            }
+        }
+    };
+    auto mfmas = [&](const Frags &f) {
+#pragma unroll
+        for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+            for (int b = 0; b < C::TN; ++b)
+                acc[a][b] = mfma32<FP4>(f.a[a], f.b[b], acc[a][b], E8M0_ONE, f.sc[b]);
+    };
+    // Interleave one MFMA with the memory instructions of the same step:
+    // LDS reads of the next fragments, LDS writes of the staged tile, and
+    // the global fetch that refills the staging registers.
+    auto interleave = [&]() {
+        constexpr int NM = C::TM * C::TN;
+        constexpr int NR = 2 * (C::TM + C::TN) + C::TN;   // ds reads (incl. scale bytes)
+        constexpr int NWR = C::A_LD + C::W_LD;             // ds writes == vmem reads
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, (NR + NM - 1) / NM, 0);  // DS read
+            if (i < NWR) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+            if (i < NWR) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        }
+    };
+    // scale chunks: the chunk for steps [t0, t0 + SC_KB/2) is read by the
+    // fragment reads of steps t0-1 .. ; reload it once every wave is done
+    // with step t0-1's MFMA inputs of the previous chunk
+    auto maybe_scales = [&](int s) {  // called at the top of step s
+        const int t = s + 1;           // the step whose fragments this step reads
+        if ((2 * t) % C::SC_KB == 0 && t < nsteps) {
+            load_scales(2 * t);
             __syncthreads();
         }
+    };
+
+    // prologue: stages 0 and 1 into LDS, stage 2 in the staging registers,
+    // step 0's fragments in registers
+    Regs r;
+    fetch(r, 0);
+    stash(r, lds);
+    fetch(r, 1);
+    stash(r, lds + C::STAGE);
+    fetch(r, 2);
+    load_scales(0);
+    __syncthreads();
+    Frags f0, f1;
+    read_frags(f0, 0);
+
+    // step s: MFMAs on step s's fragments; read step s+1's; write stage s+2
+    // (already in r) into buffer (s+2) % 3; fetch stage s+3 into r
+    auto step = [&](const Frags &cur, Frags &nxt, int s) {
+        maybe_scales(s);
+        mfmas(cur);
+        read_frags(nxt, s + 1);
+        stash(r, lds + ((s + 2) % C::NBUF) * C::STAGE);
+        fetch(r, s + 3);
+        interleave();
+        __syncthreads();
+    };
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {
+        step(f0, f1, s);
+        step(f1, f0, s + 1);
     }
+    if (s < nsteps) mfmas(f0);  // odd step count: the last step's fragments are in f0
 
     // ---- epilogue: D lane l = i + 32 g, VGPR v -> row 8 (v/4) + 4 g + v%4, column i
 #pragma unroll
-    for (int a = 0; a < C::TM; ++a) {
+    for (int b = 0; b < C::TN; ++b) {
+        const int n = n0 + wn * (BN / WGN) + b * 32 + li;
+        if (n >= N) continue;
+        const float bv = epi != EPI_NONE ? bf16_to_f32(bias[n]) : 0.f;
 #pragma unroll
-        for (int b = 0; b < C::TN; ++b) {
-            const int64_t n = n0 + wn * (BN / 2) + b * 32 + li;
-            if (n >= N) continue;
-            const float bv = epi != EPI_NONE ? bf16_to_f32(bias[n]) : 0.f;
+        for (int a = 0; a < C::TM; ++a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t m = m0 + wm * (BM / 2) + a * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
+                const int m = m0 + wm * (BM / WGM) + a * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
                 if (m < M)
-                    Y[m * ldy + n] = (uint16_t)f32_to_bf16(epilogue(acc[a][b][v], a_scale[m], bv, epi));
+                    Y[(int64_t)m * ldy + n] =
+                        (uint16_t)f32_to_bf16(epilogue(acc[a][b][v], a_scale[m], bv, epi));
             }
         }
     }
 }
 
-template <bool FP4, int BM, int BN>
+template <bool FP4, int BM, int BN, int WGM, int WGN>
 hipError_t launch_tile(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w,
                        int64_t ldw, const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y,
                        int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t st) {
-    using C = PrefillCfg<FP4, BM, BN>;
-    auto kern = gemm_prefill_kernel<FP4, BM, BN>;
-    static bool attr_set = false;   // per template instance; idempotent
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-    hipLaunchKernelGGL(kern, grid, dim3(PBLOCK), C::LDS, st, a, lda, as, w, ldw, ws, bias, epi, y,
-                       ldy, (int)M, (int)N, (int)K);
+    using C = Cfg<FP4, BM, BN, WGM, WGN>;
+    auto kern = gemm_prefill_kernel<FP4, BM, BN, WGM, WGN>;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(C::NT), 0, st, a, lda, as, w, ldw, ws,
+                       bias, epi, y, ldy, (int)M, (int)N, (int)K, 8);
     return hipGetLastError();
 }
 
@@ -195,10 +316,18 @@ hipError_t launch_gemm_prefill(bool fp4, const uint8_t *a, int64_t lda, const fl
                                const uint8_t *w, int64_t ldw, const uint8_t *ws,
                                const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
                                int64_t N, int64_t K, int num_cus, hipStream_t st) {
-    (void)num_cus;
-    if (fp4)
-        return launch_tile<true, 128, 128>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, st);
-    return launch_tile<false, 128, 128>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, st);
+    // Largest tile that still gives every CU a tile.
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t t128 = ((M + 255) / 256) * ((N + 127) / 128);
+#define BSG_PREFILL(BM_, BN_)                                                                      \
+    return fp4 ? launch_tile<true, BM_, BN_, 2, 2>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, \
+                                                   M, N, K, st)                                    \
+               : launch_tile<false, BM_, BN_, 2, 2>(a, lda, a_scale, w, ldw, ws, bias, epi, y,     \
+                                                    ldy, M, N, K, st)
+    if (t256 >= num_cus) BSG_PREFILL(256, 256);
+    if (t128 >= num_cus) BSG_PREFILL(256, 128);
+    BSG_PREFILL(128, 128);
+#undef BSG_PREFILL
 }
 
 }  // namespace bsg
