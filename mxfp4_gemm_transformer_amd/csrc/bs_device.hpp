@@ -100,6 +100,18 @@ __device__ __forceinline__ v16f mfma32(const v8i &a, const v8i &b, const v16f &c
                                                            sa, 0, sb);
 }
 
+// The same instruction with the weights as the A operand (their format and
+// E8M0 scale on the A side) and e4m3 activations as B with unit scales; the
+// result is the transposed tile: D row = weight row, D column = token.
+template <bool FP4>
+__device__ __forceinline__ v16f mfma32_wt(const v8i &w, const v8i &a, const v16f &c, int sw) {
+    if (FP4)
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, a, c, MFMA_FMT_FP4, MFMA_FMT_FP8, 0,
+                                                               sw, 0, E8M0_ONE);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, a, c, MFMA_FMT_FP8, MFMA_FMT_FP8, 0,
+                                                           sw, 0, E8M0_ONE);
+}
+
 __device__ __forceinline__ v8i pack8(const uint4 &lo, const uint4 &hi) {
     v8i r;
     r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;

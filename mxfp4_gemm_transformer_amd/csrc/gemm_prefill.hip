@@ -44,15 +44,15 @@ struct Cfg {
     static constexpr int W_LD = W_STAGE / 16 / NT;
     static constexpr int TM = BM / WGM / 32;
     static constexpr int TN = BN / WGN / 32;
-    // E8M0 scales of this tile's weight rows for SC_KB consecutive K blocks
-    // (SC_KB * 32 = 4096 K) at a time: one byte per 32x32 block row for e4m3
-    // weights, one per row for MXFP4
-    static constexpr int SC_KB = 128;
+    // E8M0 scales of the step's two K blocks travel with the step's tiles:
+    // two bytes per 32x32 block row (e4m3 weights) or per weight row (MXFP4)
     static constexpr int SC_ROWS = FP4 ? BN : BN / 32;
-    static constexpr int SC_BYTES = SC_ROWS * SC_KB;
+    static constexpr int SC_STAGE = 2 * NT;   // one 2-byte slot per thread (branch-free)
+    static constexpr int STAGE_ALL = STAGE + SC_STAGE;
     static constexpr int NBUF = 3;                    // LDS buffers in the ring
-    static constexpr int LDS = NBUF * STAGE + SC_BYTES;
+    static constexpr int LDS = NBUF * STAGE_ALL;
     static_assert(A_STAGE % (16 * NT) == 0 && W_STAGE % (16 * NT) == 0, "stage split");
+    static_assert(SC_ROWS <= NT, "one scale row per thread");
     static_assert(TM >= 1 && TN >= 1, "wave tile");
     static_assert(LDS <= 160 * 1024, "LDS");
 };
@@ -64,12 +64,14 @@ __device__ __forceinline__ int swz2(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
 __device__ __forceinline__ uint4 lds16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-constexpr uint32_t OOB = 0x80000000u;  // an offset past every buffer: reads as zero
+// A per-lane offset past every buffer: reads as zero. Scalar offsets stay
+// below 2^31, so their sum with it cannot wrap back into range.
+constexpr uint32_t OOB = 0x80000000u;
 
 template <bool FP4, int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
@@ -79,8 +81,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
     int K, int group_m) {
     using C = Cfg<FP4, BM, BN, WGM, WGN>;
     static_assert(C::NT == 256, "launch bounds assume four waves");
-    __shared__ __align__(16) uint8_t lds[C::NBUF * C::STAGE];
-    __shared__ __align__(16) uint8_t sscale[C::SC_BYTES];
+    __shared__ __align__(16) uint8_t lds[C::NBUF * C::STAGE_ALL];
 
     // ---- tile of this workgroup (XCD-aware grouped order)
     const int Mt = (M + BM - 1) / BM, Nt = (N + BN - 1) / BN, T = Mt * Nt;
@@ -108,45 +109,64 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
         (void *)(W + (int64_t)n0 * ldw), (short)0, (int)(w_bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : w_bytes),
         0x00020000);
 
+    // the scale rows of this tile: [N/32, KB] for e4m3 weights, [N, KB] for
+    // MXFP4; rows past the end and K blocks past KB read as zero (a zero
+    // E8M0 byte scales zero data there)
+    const int srow0 = FP4 ? n0 : (n0 >> 5);
+    const int64_t s_bytes = (int64_t)((FP4 ? N : (N >> 5)) - srow0) * KB;
+    const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(WS + (int64_t)srow0 * KB), (short)0,
+        (int)(s_bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : s_bytes), 0x00020000);
+    const uint32_t s_off = (uint32_t)(tid * KB);   // this thread's scale row
+
     // This thread's 16-byte chunks of a step: physical chunk P = j*NT + tid of
-    // the LDS stage holds logical chunk c of row P / (chunks per row).
-    uint32_t a_off[C::A_LD], w_off[C::W_LD];
-    int a_k[C::A_LD], w_k[C::W_LD];
-#pragma unroll
-    for (int j = 0; j < C::A_LD; ++j) {
-        const int P = j * C::NT + tid;
-        const int row = P >> 2, c = (P & 3) ^ swz4(row);
-        a_off[j] = (uint32_t)(row * lda) + 16 * c;
-        a_k[j] = 16 * c;
+    // the LDS stage holds logical chunk c of row P / (chunks per row). Rows
+    // advance by NT / (chunks per row) with j, which leaves the swizzled
+    // chunk column unchanged, so one per-thread offset serves every j and
+    // the row step goes into the scalar offset of the load.
+    constexpr int A_ROWS_PER_J = C::NT / 4;
+    constexpr int W_ROWS_PER_J = FP4 ? C::NT / 2 : C::NT / 4;
+    uint32_t a_off, w_off;
+    int a_k, w_k;
+    {
+        const int row = tid >> 2, c = (tid & 3) ^ swz4(row);
+        a_off = (uint32_t)(row * lda) + 16 * c;
+        a_k = 16 * c;
     }
-#pragma unroll
-    for (int j = 0; j < C::W_LD; ++j) {
-        const int P = j * C::NT + tid;
-        if (FP4) {
-            const int row = P >> 1, c = (P & 1) ^ swz2(row);
-            w_off[j] = (uint32_t)(row * ldw) + 16 * c;
-            w_k[j] = 32 * c;
-        } else {
-            const int row = P >> 2, c = (P & 3) ^ swz4(row);
-            w_off[j] = (uint32_t)(row * ldw) + 16 * c;
-            w_k[j] = 16 * c;
-        }
+    if (FP4) {
+        const int row = tid >> 1, c = (tid & 1) ^ swz2(row);
+        w_off = (uint32_t)(row * ldw) + 16 * c;
+        w_k = 32 * c;
+    } else {
+        const int row = tid >> 2, c = (tid & 3) ^ swz4(row);
+        w_off = (uint32_t)(row * ldw) + 16 * c;
+        w_k = 16 * c;
     }
 
     struct Regs {
         uint4 a[C::A_LD];
         uint4 w[C::W_LD];
+        uint32_t sc;   // the two scale bytes of this thread's row, if any
     };
     // past the last step the offsets are out of range and read zeros, so the
     // fetch is unconditional and the compiler can count its loads exactly
     auto fetch = [&](Regs &r, int s) {
         const int kbase = s < nsteps ? s * BK : K;   // past the end: zeros
+        const uint32_t va = kbase + a_k < K ? a_off : OOB;
+        const uint32_t vw = kbase + w_k < K ? w_off : OOB;
 #pragma unroll
         for (int j = 0; j < C::A_LD; ++j)
-            r.a[j] = bload16(rsA, kbase + a_k[j] < K ? a_off[j] + kbase : OOB);
+            r.a[j] = bload16(rsA, va, (uint32_t)(j * A_ROWS_PER_J * lda) + kbase);
 #pragma unroll
         for (int j = 0; j < C::W_LD; ++j)
-            r.w[j] = bload16(rsW, kbase + w_k[j] < K ? w_off[j] + (FP4 ? kbase / 2 : kbase) : OOB);
+            r.w[j] = bload16(rsW, vw, (uint32_t)(j * W_ROWS_PER_J * ldw) + (FP4 ? kbase / 2 : kbase));
+        {   // threads past the tile's scale rows read zeros into unused slots
+            const int kb = kbase >> 5;
+            const bool row_ok = tid < C::SC_ROWS;
+            const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(rsS, row_ok && kb < KB ? s_off : OOB, kb, 0);
+            const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b8(rsS, row_ok && kb + 1 < KB ? s_off : OOB, kb + 1, 0);
+            r.sc = b0 | (b1 << 8);
+        }
     };
     auto stash = [&](const Regs &r, uint8_t *dst) {
 #pragma unroll
@@ -155,26 +175,8 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
 #pragma unroll
         for (int j = 0; j < C::W_LD; ++j)
             *reinterpret_cast<uint4 *>(dst + C::A_STAGE + 16 * (j * C::NT + tid)) = r.w[j];
+        *reinterpret_cast<uint16_t *>(dst + C::STAGE + 2 * tid) = (uint16_t)r.sc;
     };
-    // scales of K blocks [kb0, kb0 + SC_KB) for this tile's rows -> LDS
-    auto load_scales = [&](int kb0) {
-        const int cols = min(C::SC_KB, KB - kb0);
-        for (int i = tid; i < C::SC_ROWS * C::SC_KB; i += C::NT) {
-            const int r = i / C::SC_KB, c = i % C::SC_KB;
-            uint8_t v = E8M0_ONE;
-            if (c < cols) {
-                if (FP4) {
-                    const int n = min(n0 + r, N - 1);
-                    v = WS[(int64_t)n * KB + kb0 + c];
-                } else {
-                    const int nb = min((n0 >> 5) + r, (N >> 5) - 1);
-                    v = WS[(int64_t)nb * KB + kb0 + c];
-                }
-            }
-            sscale[i] = v;
-        }
-    };
-
     v16f acc[C::TM][C::TN];
 #pragma unroll
     for (int a = 0; a < C::TM; ++a)
@@ -190,9 +192,9 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
     };
     // fragments of step s from its LDS buffer (s % 3) and the scale chunk
     auto read_frags = [&](Frags &f, int s) {
-        const uint8_t *sa = lds + (s % C::NBUF) * C::STAGE;
+        const uint8_t *sa = lds + (s % C::NBUF) * C::STAGE_ALL;
         const uint8_t *sw = sa + C::A_STAGE;
-        const int kbl = ((2 * s) % C::SC_KB) + lg;  // this lane's K block within the chunk
+        const uint8_t *ss = sa + C::STAGE;
 #pragma unroll
         for (int a = 0; a < C::TM; ++a) {
             const int row = wm * (BM / WGM) + a * 32 + li;
@@ -206,12 +208,12 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
             if (FP4) {
                 f.b[b] = pack8(lds16(sw + row * C::WROW + 16 * (lg ^ swz2(row))),
                                make_uint4(0u, 0u, 0u, 0u));
-                f.sc[b] = sscale[row * C::SC_KB + kbl];
+                f.sc[b] = ss[2 * row + lg];
             } else {
                 const int fz = swz4(row);
                 const uint8_t *base = sw + row * C::WROW;
                 f.b[b] = pack8(lds16(base + 16 * (lg ^ fz)), lds16(base + 16 * ((2 + lg) ^ fz)));
-                f.sc[b] = sscale[(row >> 5) * C::SC_KB + kbl];
+                f.sc[b] = ss[2 * (row >> 5) + lg];
             }
         }
     };
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
         for (int a = 0; a < C::TM; ++a)
 #pragma unroll
             for (int b = 0; b < C::TN; ++b)
-                acc[a][b] = mfma32<FP4>(f.a[a], f.b[b], acc[a][b], E8M0_ONE, f.sc[b]);
+                acc[a][b] = mfma32_wt<FP4>(f.b[b], f.a[a], acc[a][b], f.sc[b]);
     };
     // Interleave one MFMA with the memory instructions of the same step:
     // LDS reads of the next fragments, LDS writes of the staged tile, and
@@ -237,26 +239,14 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
             if (i < NWR) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
         }
     };
-    // scale chunks: the chunk for steps [t0, t0 + SC_KB/2) is read by the
-    // fragment reads of steps t0-1 .. ; reload it once every wave is done
-    // with step t0-1's MFMA inputs of the previous chunk
-    auto maybe_scales = [&](int s) {  // called at the top of step s
-        const int t = s + 1;           // the step whose fragments this step reads
-        if ((2 * t) % C::SC_KB == 0 && t < nsteps) {
-            load_scales(2 * t);
-            __syncthreads();
-        }
-    };
-
     // prologue: stages 0 and 1 into LDS, stage 2 in the staging registers,
     // step 0's fragments in registers
     Regs r;
     fetch(r, 0);
     stash(r, lds);
     fetch(r, 1);
-    stash(r, lds + C::STAGE);
+    stash(r, lds + C::STAGE_ALL);
     fetch(r, 2);
-    load_scales(0);
     __syncthreads();
     Frags f0, f1;
     read_frags(f0, 0);
@@ -264,10 +254,9 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
     // step s: MFMAs on step s's fragments; read step s+1's; write stage s+2
     // (already in r) into buffer (s+2) % 3; fetch stage s+3 into r
     auto step = [&](const Frags &cur, Frags &nxt, int s) {
-        maybe_scales(s);
         mfmas(cur);
         read_frags(nxt, s + 1);
-        stash(r, lds + ((s + 2) % C::NBUF) * C::STAGE);
+        stash(r, lds + ((s + 2) % C::NBUF) * C::STAGE_ALL);
         fetch(r, s + 3);
         interleave();
         __syncthreads();
@@ -279,20 +268,32 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
     }
     if (s < nsteps) mfmas(f0);  // odd step count: the last step's fragments are in f0
 
-    // ---- epilogue: D lane l = i + 32 g, VGPR v -> row 8 (v/4) + 4 g + v%4, column i
+    // ---- epilogue. The MFMAs computed transposed tiles: lane l = i + 32 g,
+    // VGPR v holds token m = tile row i and weight column n = 8 (v/4) + 4 g
+    // + v%4, so VGPRs 4q..4q+3 are four consecutive columns of one output
+    // row: one 8-byte store each.
 #pragma unroll
-    for (int b = 0; b < C::TN; ++b) {
-        const int n = n0 + wn * (BN / WGN) + b * 32 + li;
-        if (n >= N) continue;
-        const float bv = epi != EPI_NONE ? bf16_to_f32(bias[n]) : 0.f;
+    for (int a = 0; a < C::TM; ++a) {
+        const int m = m0 + wm * (BM / WGM) + a * 32 + li;
+        if (m >= M) continue;
+        const float as = a_scale[m];
+        uint16_t *yrow = Y + (int64_t)m * ldy;
 #pragma unroll
-        for (int a = 0; a < C::TM; ++a) {
+        for (int b = 0; b < C::TN; ++b) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = m0 + wm * (BM / WGM) + a * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
-                if (m < M)
-                    Y[(int64_t)m * ldy + n] =
-                        (uint16_t)f32_to_bf16(epilogue(acc[a][b][v], a_scale[m], bv, epi));
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * (BN / WGN) + b * 32 + 8 * q + 4 * lg;
+                if (n >= N) continue;
+                float bv[4] = {0.f, 0.f, 0.f, 0.f};
+                if (epi != EPI_NONE) {  // bias is only 2-byte aligned
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bv[j] = bf16_to_f32(bias[n + j]);
+                }
+                uint32_t h[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    h[j] = f32_to_bf16(epilogue(acc[a][b][4 * q + j], as, bv[j], epi));
+                *reinterpret_cast<uint2 *>(yrow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
             }
         }
     }
