@@ -146,12 +146,14 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
     struct Regs {
         uint4 a[C::A_LD];
         uint4 w[C::W_LD];
-        uint32_t sc;   // the two scale bytes of this thread's row, if any
+        uint32_t sc0, sc1;   // the two scale bytes of this thread's row, if any; kept
+                             // apart so nothing waits on them before the LDS write
     };
     // past the last step the offsets are out of range and read zeros, so the
     // fetch is unconditional and the compiler can count its loads exactly
     auto fetch = [&](Regs &r, int s) {
-        const int kbase = s < nsteps ? s * BK : K;   // past the end: zeros
+        // past the end: zeros; readfirstlane keeps the scalar offsets in SGPRs
+        const int kbase = __builtin_amdgcn_readfirstlane(s < nsteps ? s * BK : K);
         const uint32_t va = kbase + a_k < K ? a_off : OOB;
         const uint32_t vw = kbase + w_k < K ? w_off : OOB;
 #pragma unroll
@@ -162,10 +164,13 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
             r.w[j] = bload16(rsW, vw, (uint32_t)(j * W_ROWS_PER_J * ldw) + (FP4 ? kbase / 2 : kbase));
         {   // threads past the tile's scale rows read zeros into unused slots
             const int kb = kbase >> 5;
+            // bitwise conditions: a short-circuit here becomes a branch that
+            // splits the scheduling region and stalls the MFMA stream
             const bool row_ok = tid < C::SC_ROWS;
-            const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(rsS, row_ok && kb < KB ? s_off : OOB, kb, 0);
-            const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b8(rsS, row_ok && kb + 1 < KB ? s_off : OOB, kb + 1, 0);
-            r.sc = b0 | (b1 << 8);
+            const uint32_t o0 = (row_ok & (kb < KB)) ? s_off + kb : OOB;
+            const uint32_t o1 = (row_ok & (kb + 1 < KB)) ? s_off + kb + 1 : OOB;
+            r.sc0 = __builtin_amdgcn_raw_buffer_load_b8(rsS, o0, 0, 0);
+            r.sc1 = __builtin_amdgcn_raw_buffer_load_b8(rsS, o1, 0, 0);
         }
     };
     auto stash = [&](const Regs &r, uint8_t *dst) {
@@ -175,7 +180,8 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
 #pragma unroll
         for (int j = 0; j < C::W_LD; ++j)
             *reinterpret_cast<uint4 *>(dst + C::A_STAGE + 16 * (j * C::NT + tid)) = r.w[j];
-        *reinterpret_cast<uint16_t *>(dst + C::STAGE + 2 * tid) = (uint16_t)r.sc;
+        dst[C::STAGE + 2 * tid] = (uint8_t)r.sc0;
+        dst[C::STAGE + 2 * tid + 1] = (uint8_t)r.sc1;
     };
     v16f acc[C::TM][C::TN];
 #pragma unroll
