@@ -23,10 +23,29 @@ __device__ __forceinline__ uint32_t absmax8(const uint4 &c) {
     return m;
 }
 
+// e4m3 code of fl32(x / s), without a division in the common case. With
+// r = fl32(1/s), q = fl32(x * r) is within 2.5 fp32 ulps of fl32(x / s)
+// (two roundings of 2^-24 relative error each, plus the 1/2 ulp of the exact
+// quotient's own rounding). The e4m3 rounding of a normal value only changes
+// at midpoints between codes, whose low 20 significand bits are exactly
+// 0x80000, and no midpoint lies within 2^19 ulps of a binade edge; so if q's
+// low 20 bits are more than 4 away from 0x80000, q and fl32(x / s) round to
+// the same code. Otherwise, in the subnormal e4m3 range, and for rows whose
+// scale is so small (subnormal) that 1/s overflows, divide.
+__device__ __forceinline__ uint32_t quant_one(float x, float s, float r, bool r_ok) {
+    float q = x * r;
+    const uint32_t mag = __float_as_uint(q) & 0x7FFFFFFFu;
+    const uint32_t d = (mag & 0xFFFFFu) - 0x80000u + 4u;   // in [0, 8] near a midpoint
+    if (!r_ok | (mag < 0x3C800000u) | (d <= 8u)) q = x / s;  // |q| < 2^-6, or close to a tie
+    return e4m3_encode(q);
+}
+
 // Codes of the 16 bf16 values in two 16-byte chunks, packed little-endian.
 __device__ __forceinline__ uint4 encode16(const uint4 &c0, const uint4 &c1, float s) {
     const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
     uint32_t out[4] = {0u, 0u, 0u, 0u};
+    const float r = 1.0f / s;  // correctly rounded
+    const bool r_ok = (__float_as_uint(r) & 0x7FFFFFFFu) < 0x7F800000u;   // finite
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const uint32_t lo = w[i] & 0xFFFFu, hi = w[i] >> 16;
@@ -35,8 +54,8 @@ __device__ __forceinline__ uint4 encode16(const uint4 &c0, const uint4 &c1, floa
             clo = (lo >> 8) & 0x80u;
             chi = (hi >> 8) & 0x80u;
         } else {
-            clo = e4m3_encode(bf16_to_f32(lo) / s);
-            chi = e4m3_encode(bf16_to_f32(hi) / s);
+            clo = quant_one(bf16_to_f32(lo), s, r, r_ok);
+            chi = quant_one(bf16_to_f32(hi), s, r, r_ok);
         }
         out[i >> 1] |= (clo | (chi << 8)) << (16 * (i & 1));
     }
@@ -49,14 +68,14 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v, int width) {
     return v;
 }
 
-// TPR threads per row (16, 64 or 256); each holds NCH chunks of 16 values
+// TPR threads per row (16, 64, 256 or 1024); each holds NCH chunks of 16 values
 // in registers between the max reduction and the encode.
-template <int TPR, int NCH>
-__global__ __launch_bounds__(QBLOCK) void quant_rows_kernel(const uint16_t *__restrict__ x,
+template <int QB, int TPR, int NCH>
+__global__ __launch_bounds__(QB) void quant_rows_kernel(const uint16_t *__restrict__ x,
                                                             int64_t ldx, uint8_t *__restrict__ q,
                                                             int64_t ldq, float *__restrict__ scale,
                                                             int64_t M, int K) {
-    constexpr int RPB = QBLOCK / TPR;
+    constexpr int RPB = QB / TPR;
     const int tid = threadIdx.x;
     const int t = tid % TPR;
     const int64_t m = (int64_t)blockIdx.x * RPB + tid / TPR;
@@ -80,13 +99,13 @@ __global__ __launch_bounds__(QBLOCK) void quant_rows_kernel(const uint16_t *__re
     if (TPR <= 64) {
         amax = group_max(amax, TPR);
     } else {
-        __shared__ uint32_t red[QBLOCK / 64];
+        __shared__ uint32_t red[QB / 64];
         amax = group_max(amax, 64);
         if ((tid & 63) == 0) red[tid >> 6] = amax;
         __syncthreads();
         amax = red[0];
 #pragma unroll
-        for (int i = 1; i < QBLOCK / 64; ++i) amax = max(amax, red[i]);
+        for (int i = 1; i < QB / 64; ++i) amax = max(amax, red[i]);
     }
     const float s = bf16_to_f32(amax) / 448.0f;  // correctly rounded fp32 division
     if (!active) return;
@@ -128,23 +147,26 @@ __global__ __launch_bounds__(QBLOCK) void quant_rows_long_kernel(const uint16_t 
             encode16(ldg16(xr + 16 * c), ldg16(xr + 16 * c + 8), s);
 }
 
-template <int TPR, int NCH>
+template <int QB, int TPR, int NCH>
 void launch(const uint16_t *x, int64_t ldx, uint8_t *q, int64_t ldq, float *s, int64_t M, int K,
             hipStream_t st) {
-    constexpr int RPB = QBLOCK / TPR;
+    constexpr int RPB = QB / TPR;
     const dim3 grid((unsigned)((M + RPB - 1) / RPB));
-    hipLaunchKernelGGL((quant_rows_kernel<TPR, NCH>), grid, dim3(QBLOCK), 0, st, x, ldx, q, ldq, s,
+    hipLaunchKernelGGL((quant_rows_kernel<QB, TPR, NCH>), grid, dim3(QB), 0, st, x, ldx, q, ldq, s,
                        M, K);
 }
 
-template <int TPR>
+// Register budget: 1024-thread blocks get 128 VGPRs per lane, enough for 4
+// chunks; 256-thread blocks hold up to 16.
+template <int QB, int TPR>
 bool launch_tpr(int nch_per_thread, const uint16_t *x, int64_t ldx, uint8_t *q, int64_t ldq,
                 float *s, int64_t M, int K, hipStream_t st) {
-    if (nch_per_thread <= 1) launch<TPR, 1>(x, ldx, q, ldq, s, M, K, st);
-    else if (nch_per_thread <= 2) launch<TPR, 2>(x, ldx, q, ldq, s, M, K, st);
-    else if (nch_per_thread <= 4) launch<TPR, 4>(x, ldx, q, ldq, s, M, K, st);
-    else if (nch_per_thread <= 8) launch<TPR, 8>(x, ldx, q, ldq, s, M, K, st);
-    else if (nch_per_thread <= 16) launch<TPR, 16>(x, ldx, q, ldq, s, M, K, st);
+    constexpr int CAP = QB > 256 ? 4 : 16;
+    if (nch_per_thread <= 1) launch<QB, TPR, 1>(x, ldx, q, ldq, s, M, K, st);
+    else if (nch_per_thread <= 2) launch<QB, TPR, 2>(x, ldx, q, ldq, s, M, K, st);
+    else if (nch_per_thread <= 4) launch<QB, TPR, 4>(x, ldx, q, ldq, s, M, K, st);
+    else if (nch_per_thread <= 8 && CAP >= 8) launch<QB, TPR, (CAP >= 8 ? 8 : 1)>(x, ldx, q, ldq, s, M, K, st);
+    else if (nch_per_thread <= 16 && CAP >= 16) launch<QB, TPR, (CAP >= 16 ? 16 : 1)>(x, ldx, q, ldq, s, M, K, st);
     else return false;
     return true;
 }
@@ -156,15 +178,22 @@ hipError_t launch_quant_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_
     const int k = (int)K;
     const int nch = k / 16;
     // Many rows: a few threads per row is enough to fill the chip; few
-    // rows: spread each row over a whole block to cut latency.
-    int tpr = M >= 512 ? 64 : 256;
+    // rows: spread each row over a whole block (up to 1024 threads) to cut
+    // the per-row latency, which is all a decode-sized call costs.
+    int tpr = M >= 512 ? 64 : (M <= 64 ? 1024 : 256);
     if (nch <= 16) tpr = 16;
     else if (nch <= 64) tpr = 64;
+    else if (nch <= 256 && tpr > 256) tpr = 256;
     const int per = (nch + tpr - 1) / tpr;
     bool ok;
-    if (tpr == 16) ok = launch_tpr<16>(per, x, ld_x, q, ld_q, scale, M, k, stream);
-    else if (tpr == 64) ok = launch_tpr<64>(per, x, ld_x, q, ld_q, scale, M, k, stream);
-    else ok = launch_tpr<256>(per, x, ld_x, q, ld_q, scale, M, k, stream);
+    if (tpr == 16) ok = launch_tpr<QBLOCK, 16>(per, x, ld_x, q, ld_q, scale, M, k, stream);
+    else if (tpr == 64) ok = launch_tpr<QBLOCK, 64>(per, x, ld_x, q, ld_q, scale, M, k, stream);
+    else if (tpr == 256) ok = launch_tpr<QBLOCK, 256>(per, x, ld_x, q, ld_q, scale, M, k, stream);
+    else {
+        ok = launch_tpr<1024, 1024>(per, x, ld_x, q, ld_q, scale, M, k, stream);
+        if (!ok)   // long rows: 256 threads each hold more chunks
+            ok = launch_tpr<QBLOCK, 256>((nch + 255) / 256, x, ld_x, q, ld_q, scale, M, k, stream);
+    }
     if (!ok)
         hipLaunchKernelGGL(quant_rows_long_kernel, dim3((unsigned)M), dim3(QBLOCK), 0, stream, x,
                            ld_x, q, ld_q, scale, M, k);
