@@ -46,7 +46,45 @@ def parse():
     p.add_argument("--m", type=int, default=None, help="token count (M) for sweep workloads")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU oracle budget for the cpu_baseline leg (0 disables it)")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                   help="only run a plain device copy of BYTES bytes three times (the "
+                        "reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+def kernel_source(kernel: str, M: int) -> str:
+    import mxfp4_gemm_transformer_amd as bs
+    csrc = os.path.join(os.path.dirname(bs.library_path()), "csrc")
+    return os.path.join(csrc, "gemm_decode.hip" if M <= 64 else "gemm_prefill.hip")
+
+
+def measured_traffic(kernel: str, workload: str, M: int):
+    """HBM bytes per launch from the committed counter record, if it was taken
+    on the kernel source as it stands (same sha256), else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get("%s %s M=%d" % (kernel, workload, M))
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    with open(kernel_source(kernel, M), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec.get("source_sha256"):
+            return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def calibrate_copy(nbytes: int):
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "copies": 3}))
 
 
 def algorithmic(wl, M):
@@ -67,6 +105,10 @@ def main():
         print("bench.py measures one GPU: the layer's kernels run on one device and this "
               "build has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import torch
     import mxfp4_gemm_transformer_amd as bs
@@ -171,8 +213,8 @@ def main():
         achieved = alg["gemm_bytes"] / gemm_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = None
     roof["kernel"] = "gemm_mxfp4_w4a8" if wl.fmt == "mxfp4" else "gemm_bs_fp8"
+    roof["traffic"] = measured_traffic(roof["kernel"], wl.name, M)
     roof["avg_launch_us"] = round(gemm_s * 1e6, 3)
     roof["algorithmic_bytes_per_launch"] = alg["gemm_bytes"]
     roof["algorithmic_flops_per_launch"] = alg["gemm_flops"]
