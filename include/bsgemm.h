@@ -10,9 +10,9 @@
  *
  * Sources (web pages bundled as the reference):
  *   - formats and scale grids: vLLM DeepSeek-V4 AMD mono runner page,
- *     AttnWeights ("wqkv [2048, 7168] e4m3", "wqkv_scale [64, 224] uint8
- *     E8M0 (32 x 32 blocks)") and MonoLayerWeights.check (fp4x2 weights
- *     [.., N, K/2] with uint8 scales [N, K/32], "AITER's A8W4 layout");
+ *     AttnWeights (an e4m3 [2048, 7168] projection weight with a [64, 224]
+ *     uint8 E8M0 grid, one byte per 32x32 block) and MonoLayerWeights.check
+ *     (fp4x2 expert weights [.., N, K/2] with uint8 scales [N, K/32]);
  *   - per-token (q_fp8, scale) pairs feeding the W4A8 GEMM: sly-radiance
  *     README, fused norm/quant rows of its file table;
  *   - bias / bias+GELU fused into the FP8 GEMM epilogue: flash-rt

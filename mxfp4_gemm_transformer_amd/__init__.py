@@ -21,7 +21,8 @@ import torch
 
 __all__ = ["fp8_quant_rows", "gemm_bs_fp8", "gemm_mxfp4_w4a8", "bs_workspace_bytes",
            "bs_status_string", "BsError", "EPI_NONE", "EPI_BIAS", "EPI_BIAS_GELU_TANH",
-           "library_path", "load_library", "EXPORTED_SYMBOLS"]
+           "weight_shape", "w_scale_shape", "library_path", "load_library",
+           "EXPORTED_SYMBOLS"]
 
 EPI_NONE, EPI_BIAS, EPI_BIAS_GELU_TANH = 0, 1, 2
 BS_OK, BS_EINVAL, BS_EALIGN, BS_EARCH, BS_EWORKSPACE, BS_ELAUNCH = 0, -1, -2, -3, -4, -5
@@ -126,19 +127,32 @@ def fp8_quant_rows(x: torch.Tensor, q: torch.Tensor | None = None,
     return q, scale
 
 
-def _gemm(fn_name, op, a, a_scale, w, w_scale, bias, epilogue, y, workspace, stream, w_cols,
-          ws_shape):
+def weight_shape(op: int, N: int, K: int) -> tuple:
+    """Byte shape of the weight operand: e4m3 [N, K] (op 0) or fp4 e2m1
+    packed two per byte [N, K/2] (op 1)."""
+    return (N, K) if op == 0 else (N, K // 2)
+
+
+def w_scale_shape(op: int, N: int, K: int) -> tuple:
+    """Shape of the uint8 E8M0 scale grid, row-major: one scale per 32x32
+    block [N/32, K/32] for e4m3 weights (op 0), one per row per 32 along K
+    [N, K/32] for MXFP4 weights (op 1)."""
+    return (N // 32, K // 32) if op == 0 else (N, K // 32)
+
+
+def _gemm(fn_name, op, a, a_scale, w, w_scale, bias, epilogue, y, workspace, stream):
     a = _u8(a, "a")
     w = _u8(w, "w")
     M, K = a.shape
     N = w.shape[0]
     lda = _matrix(a, "a", M, K)
-    ldw = _matrix(w, "w", N, w_cols(K))
+    ldw = _matrix(w, "w", N, weight_shape(op, N, K)[1])
     if a_scale.dtype != torch.float32 or a_scale.shape != (M,) or not a_scale.is_contiguous():
         raise ValueError("a_scale must be a contiguous fp32 [M] tensor")
-    if w_scale.dtype != torch.uint8 or tuple(w_scale.shape) != ws_shape(N, K) \
+    if w_scale.dtype != torch.uint8 or tuple(w_scale.shape) != w_scale_shape(op, N, K) \
             or not w_scale.is_contiguous():
-        raise ValueError("w_scale must be a contiguous uint8 %s tensor" % (ws_shape(N, K),))
+        raise ValueError("w_scale must be a contiguous uint8 %s tensor"
+                         % (w_scale_shape(op, N, K),))
     if epilogue != EPI_NONE:
         if bias is None or bias.dtype != torch.bfloat16 or bias.shape != (N,) \
                 or not bias.is_contiguous():
@@ -165,8 +179,7 @@ def gemm_bs_fp8(a, a_scale, w, w_scale, bias=None, epilogue=EPI_NONE, y=None, wo
                 stream=None):
     """y [M, N] bf16 = epilogue(a_scale[m] * sum_k a[m,k] w[n,k] 2^(S[n/32,k/32]-127) (+ bias)).
     a: e4m3 [M, K]; w: e4m3 [N, K]; w_scale: uint8 E8M0 [N/32, K/32]."""
-    return _gemm("gemm_bs_fp8", 0, a, a_scale, w, w_scale, bias, epilogue, y, workspace, stream,
-                 lambda K: K, lambda N, K: (N // 32, K // 32))
+    return _gemm("gemm_bs_fp8", 0, a, a_scale, w, w_scale, bias, epilogue, y, workspace, stream)
 
 
 def gemm_mxfp4_w4a8(a, a_scale, w, w_scale, bias=None, epilogue=EPI_NONE, y=None,
@@ -174,4 +187,4 @@ def gemm_mxfp4_w4a8(a, a_scale, w, w_scale, bias=None, epilogue=EPI_NONE, y=None
     """As gemm_bs_fp8 with fp4 e2m1 weights packed [N, K/2] (low nibble = even
     k) and one E8M0 scale per row per 32 k, w_scale [N, K/32]."""
     return _gemm("gemm_mxfp4_w4a8", 1, a, a_scale, w, w_scale, bias, epilogue, y, workspace,
-                 stream, lambda K: K // 2, lambda N, K: (N, K // 32))
+                 stream)

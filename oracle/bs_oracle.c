@@ -16,11 +16,12 @@
  *     saturation are the workload's own definition);
  *   - Y = dequant(A) . dequant(W)^T (+ bias) with e4m3 weights carrying one
  *     E8M0 scale per 32x32 block, row-major [N/32, K/32]
- *     (vLLM DeepSeek-V4 AMD mono runner page, AttnWeights: "wqkv_scale
- *     [64, 224] uint8 E8M0 (32 x 32 blocks)");
+ *     (vLLM DeepSeek-V4 AMD mono runner page, AttnWeights: the fused
+ *     q/kv projection's [2048, 7168] e4m3 weight carries a [64, 224] uint8
+ *     E8M0 grid, one byte per 32x32 block);
  *   - the same with fp4 e2m1 weights packed two per byte and one E8M0 scale
- *     per row per 32 along K, [N, K/32] (same page, MonoLayerWeights.check,
- *     "AITER's A8W4 layout");
+ *     per row per 32 along K, [N, K/32] (same page, MonoLayerWeights.check:
+ *     the routed experts' fp4x2 weights and their uint8 scale rows);
  *   - the optional bias / tanh-GELU epilogue (flash-rt groot_n17 frontend,
  *     module docstring: bias and bias+GELU fused into the FP8 GEMM epilogue;
  *     the tanh GELU is the cortiq vit.rs ACT_SRC shader, act == 2 branch).
@@ -229,7 +230,7 @@ static void one_bs_fp8(const uint8_t *a, float a_scale, const uint8_t *w,
     *absum = fabs((double)a_scale) * abs_acc;
 }
 
-/* One output of the MXFP4-weight GEMM ("A8W4", mono runner page,
+/* One output of the MXFP4-weight GEMM (A8W4 on the mono runner page,
  * MonoLayerWeights.check): `w` is one row of fp4 e2m1 codes packed two per
  * byte [K/2], element k in byte k/2, low nibble for even k; `ws` is that
  * row's E8M0 scales [K/32], one per 32 consecutive k.
