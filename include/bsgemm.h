@@ -55,6 +55,10 @@ enum bs_status {
     BS_ELAUNCH = -5      /* the kernel launch failed (hipGetLastError) */
 };
 
+/* Largest row stride (bytes) of A and W the GEMMs accept (4 MiB): tile
+ * offsets are 32-bit buffer offsets. */
+#define BS_MAX_LD_BYTES ((int64_t)1 << 22)
+
 enum bs_epilogue {
     BS_EPI_NONE = 0,            /* y = s[m] * acc                               */
     BS_EPI_BIAS = 1,            /* y = s[m] * acc + bias[n]                     */
@@ -89,7 +93,7 @@ int fp8_quant_rows(const void *x_bf16, int64_t ld_x, void *q_e4m3, int64_t ld_q,
  *   w_scale  [N/32, K/32] uint8 E8M0, row-major, dense (row stride K/32)
  *   bias     [N] bf16, required iff epilogue != BS_EPI_NONE, else ignored
  *   y_bf16   [M, N] bf16 out, row stride ld_y elements
- *   M >= 1; N, K >= 32 and multiples of 32.
+ *   M >= 1; N, K >= 32 and multiples of 32; ld_a, ld_w <= BS_MAX_LD_BYTES.
  *   workspace / workspace_bytes: scratch the call may use, at least
  *   bs_workspace_bytes(0, M, N, K) bytes (may be NULL when that is 0).
  */

@@ -67,11 +67,15 @@ __device__ __forceinline__ float gelu_tanh(float v) {
     return v - v * __builtin_amdgcn_rcpf(e + 1.0f);
 }
 
-__device__ __forceinline__ float epilogue(float acc, float a_scale, float bias, int epi) {
-    float v = a_scale * acc;
+// The epilogue after the per-token scale: + bias, then GELU.
+__device__ __forceinline__ float epilogue_rest(float v, float bias, int epi) {
     if (epi != EPI_NONE) v += bias;
     if (epi == EPI_BIAS_GELU_TANH) v = gelu_tanh(v);
     return v;
+}
+
+__device__ __forceinline__ float epilogue(float acc, float a_scale, float bias, int epi) {
+    return epilogue_rest(a_scale * acc, bias, epi);
 }
 
 // ------------------------------------------------------ MFMA operand layout

@@ -51,6 +51,8 @@ int check_gemm(const void *a, int64_t ld_a, const float *a_scale, const void *w,
     if (epilogue < BS_EPI_NONE || epilogue > BS_EPI_BIAS_GELU_TANH) return BS_EINVAL;
     if (epilogue != BS_EPI_NONE && !bias) return BS_EINVAL;
     if (ld_a < K || ld_w < w_row_bytes || ld_y < N) return BS_EINVAL;
+    // tile offsets (up to 256 rows of A or W plus K) are 32-bit buffer offsets
+    if (ld_a > BS_MAX_LD_BYTES || ld_w > BS_MAX_LD_BYTES) return BS_EINVAL;
     if (!aligned16(a) || !aligned16(w) || !aligned16(y)) return BS_EALIGN;
     if (ld_a % 16 || ld_w % 16 || (2 * ld_y) % 16) return BS_EALIGN;
     if ((reinterpret_cast<uintptr_t>(a_scale) & 3u) != 0) return BS_EALIGN;

@@ -17,7 +17,11 @@
 //
 // LDS rows hold 16-byte chunks XOR-swizzled by row, so that the 32 lanes of
 // a fragment read (32 consecutive rows, one chunk column) spread over all
-// banks whether the LDS has 32 or 64 banks.
+// banks. For 64-byte rows the chunk column is xor-ed with row bits 2-3:
+// measured on gfx950 with this fragment pattern, that reads at the full
+// ds_read_b128 rate, while xor-ing with row bits 1 and 3 (which also puts
+// every 16 lanes on distinct 16-byte slots of a 256-byte window) reads
+// 1.26x slower.
 //
 // Workgroups are numbered so that consecutive tiles in a grouped order land
 // on the same XCD (workgroups are dispatched round-robin over the 8 XCDs),
@@ -59,7 +63,7 @@ struct Cfg {
 
 // Swizzle of the 16-byte chunk column within a 64-byte row (4 chunks) and a
 // 32-byte row (2 chunks).
-__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int swz2(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
 __device__ __forceinline__ uint4 lds16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
@@ -317,6 +321,304 @@ hipError_t launch_tile(const uint8_t *a, int64_t lda, const float *as, const uin
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// DMA-staged variant, for K a multiple of 64 (whole steps, and E8M0 byte pairs
+// that start on even offsets). The tiles of a K step go from HBM/L2 straight
+// into LDS with buffer loads in LDS mode, which write each lane's 16 bytes at
+// M0 + 16 * lane, so the waves never hold tile data in registers and never
+// write LDS themselves. A ring of NBUF stages keeps NBUF - 1 steps of loads
+// in flight; one wait on the vector-memory counter and one barrier per step
+// publish the stage the next step reads. The weight scales of a step travel
+// as one 2-byte load per scale row into a 4-byte slot per thread.
+//
+// The waits are written out because the compiler does not track LDS-mode
+// loads issued from inline assembly: every thread issues the same loads in
+// the same order (past the end they read zeros from outside the buffer's
+// range), so a count of loads per stage states exactly which stages are done.
+
+// The helpers below write M0, which the compiler reserves; nothing else in
+// these kernels uses M0, so clobbering it is safe here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+
+// One 16-byte LDS-mode buffer load: lane l's bytes land at m0 + 16 l.
+// (One wait state between the M0 write and the load that reads it.)
+__device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t rs, uint32_t m0, uint32_t voff,
+                                         uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
+                 : "memory", "m0");
+}
+
+// One 2-byte LDS-mode buffer load: lane l's two bytes land zero-extended in
+// the 4-byte slot m0 + 4 l.
+__device__ __forceinline__ void dma_u16(__amdgpu_buffer_rsrc_t rs, uint32_t m0, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ushort %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rs)
+                 : "memory", "m0");
+}
+
+#pragma clang diagnostic pop
+
+// Wait until at most N of this wave's vector-memory loads are in flight,
+// then meet the other waves.
+template <int N>
+__device__ __forceinline__ void wait_loads_and_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+template <bool FP4, int BM, int BN, int NBUF>
+struct DCfg {
+    static constexpr int NT = 256;                    // four waves, 2 x 2
+    static constexpr int WROW = FP4 ? BK / 2 : BK;    // W bytes per row per step
+    static constexpr int A_STAGE = BM * BK;
+    static constexpr int W_STAGE = BN * WROW;
+    static constexpr int SC_OFF = A_STAGE + W_STAGE;  // one 4-byte scale slot per thread
+    static constexpr int STAGE = SC_OFF + 4 * NT;
+    static constexpr int A_LD = A_STAGE / 16 / NT;    // 16-byte loads per thread per step
+    static constexpr int W_LD = W_STAGE / 16 / NT;
+    static constexpr int LPS = A_LD + W_LD + 1;       // loads per thread per stage
+    static constexpr int TM = BM / 64;
+    static constexpr int TN = BN / 64;
+    static constexpr int SC_ROWS = FP4 ? BN : BN / 32;
+    // epilogue staging: each wave's 32 x (32 TN) fp32 slab, rows padded by 16 bytes
+    static constexpr int EP_ROW = TN * 32 * 4 + 16;
+    static constexpr int EP_WAVE = 32 * EP_ROW;
+    static constexpr int LDS = NBUF * STAGE > 4 * EP_WAVE ? NBUF * STAGE : 4 * EP_WAVE;
+    static_assert(A_STAGE % (16 * NT) == 0 && W_STAGE % (16 * NT) == 0, "stage split");
+    static_assert(SC_ROWS <= NT, "one scale row per thread");
+    static_assert(NBUF >= 4, "the ring needs NBUF - 1 >= 3 stages in flight");
+    static_assert(LPS * (NBUF - 3) <= 63, "vmcnt range");
+    static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+template <bool FP4, int BM, int BN, int NBUF>
+__global__ __launch_bounds__(256, 1) void gemm_prefill_dma_kernel(
+    const uint8_t *__restrict__ A, int64_t lda, const float *__restrict__ a_scale,
+    const uint8_t *__restrict__ W, int64_t ldw, const uint8_t *__restrict__ WS,
+    const uint16_t *__restrict__ bias, int epi, uint16_t *__restrict__ Y, int64_t ldy, int M, int N,
+    int K, int group_m) {
+    using C = DCfg<FP4, BM, BN, NBUF>;
+    __shared__ __align__(16) uint8_t lds[C::LDS];
+
+    // ---- tile of this workgroup (XCD-aware grouped order)
+    const int Mt = (M + BM - 1) / BM, Nt = (N + BN - 1) / BN, T = Mt * Nt;
+    int t = blockIdx.x;
+    if (T % NXCD == 0) t = (t % NXCD) * (T / NXCD) + t / NXCD;
+    const int per_group = group_m * Nt;
+    const int first_m = (t / per_group) * group_m;
+    const int gm = min(Mt - first_m, group_m);
+    const int m0 = (first_m + (t % per_group) % gm) * BM;
+    const int n0 = ((t % per_group) / gm) * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int li = lane & 31, lg = lane >> 5;
+    const int KB = K >> 5;
+    const int nsteps = K / BK;
+
+    const int64_t a_bytes = (int64_t)(M - m0) * lda, w_bytes = (int64_t)(N - n0) * ldw;
+    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A + (int64_t)m0 * lda), (short)0, (int)(a_bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : a_bytes),
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(W + (int64_t)n0 * ldw), (short)0, (int)(w_bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : w_bytes),
+        0x00020000);
+    const int srow0 = FP4 ? n0 : (n0 >> 5);
+    const int64_t s_bytes = (int64_t)((FP4 ? N : (N >> 5)) - srow0) * KB;
+    const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(WS + (int64_t)srow0 * KB), (short)0,
+        (int)(s_bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : s_bytes), 0x00020000);
+
+    // This thread's 16-byte chunk of each load: physical chunk j*NT + tid of
+    // a stage (where the LDS-mode load of wave w, lane l, puts its bytes)
+    // holds logical chunk c of its row, c = physical column ^ swizzle(row).
+    constexpr int A_ROWS_PER_J = C::NT / 4;
+    constexpr int W_ROWS_PER_J = FP4 ? C::NT / 2 : C::NT / 4;
+    uint32_t a_off, w_off;
+    {
+        const int row = tid >> 2, c = (tid & 3) ^ swz4(row);
+        a_off = (uint32_t)(row * lda) + 16 * c;
+    }
+    if (FP4) {
+        const int row = tid >> 1, c = (tid & 1) ^ swz2(row);
+        w_off = (uint32_t)(row * ldw) + 16 * c;
+    } else {
+        const int row = tid >> 2, c = (tid & 3) ^ swz4(row);
+        w_off = (uint32_t)(row * ldw) + 16 * c;
+    }
+    const uint32_t s_off = tid < C::SC_ROWS ? (uint32_t)(tid * KB) : OOB;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t *)lds);
+
+    // LDS-mode loads of step s into ring buffer s % NBUF; past the last step
+    // every lane reads outside the buffers' ranges, which writes zeros.
+    auto issue = [&](int s) {
+        const bool live = s < nsteps;
+        const uint32_t kbase = (uint32_t)__builtin_amdgcn_readfirstlane(live ? s * BK : 0);
+        const uint32_t base = lds0 + (uint32_t)((s % NBUF) * C::STAGE) + (uint32_t)wave * 1024u;
+        const uint32_t va = live ? a_off : OOB, vw = live ? w_off : OOB;
+#pragma unroll
+        for (int j = 0; j < C::A_LD; ++j)
+            dma_b128(rsA, base + j * C::NT * 16, va, (uint32_t)(j * A_ROWS_PER_J * lda) + kbase);
+#pragma unroll
+        for (int j = 0; j < C::W_LD; ++j)
+            dma_b128(rsW, base + C::A_STAGE + j * C::NT * 16, vw,
+                     (uint32_t)(j * W_ROWS_PER_J * ldw) + (FP4 ? kbase / 2 : kbase));
+        dma_u16(rsS, lds0 + (uint32_t)((s % NBUF) * C::STAGE + C::SC_OFF) + (uint32_t)wave * 256u,
+                live ? s_off + (kbase >> 5) : OOB);
+    };
+
+    v16f acc[C::TM][C::TN];
+#pragma unroll
+    for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+
+    struct Frags {
+        v8i a[C::TM];
+        v8i b[C::TN];
+        int sc[C::TN];
+    };
+    auto read_frags = [&](Frags &f, int s) {
+        const uint8_t *sa = lds + (s % NBUF) * C::STAGE;
+        const uint8_t *sw = sa + C::A_STAGE;
+        const uint8_t *ss = sa + C::SC_OFF;
+#pragma unroll
+        for (int a = 0; a < C::TM; ++a) {
+            const int row = wm * (BM / 2) + a * 32 + li;
+            const int fz = swz4(row);
+            const uint8_t *p = sa + row * BK;
+            f.a[a] = pack8(lds16(p + 16 * (lg ^ fz)), lds16(p + 16 * ((2 + lg) ^ fz)));
+        }
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b) {
+            const int row = wn * (BN / 2) + b * 32 + li;
+            if (FP4) {
+                f.b[b] = pack8(lds16(sw + row * C::WROW + 16 * (lg ^ swz2(row))),
+                               make_uint4(0u, 0u, 0u, 0u));
+                f.sc[b] = ss[4 * row + lg];
+            } else {
+                const int fz = swz4(row);
+                const uint8_t *p = sw + row * C::WROW;
+                f.b[b] = pack8(lds16(p + 16 * (lg ^ fz)), lds16(p + 16 * ((2 + lg) ^ fz)));
+                f.sc[b] = ss[4 * (row >> 5) + lg];
+            }
+        }
+    };
+    auto mfmas = [&](const Frags &f) {
+#pragma unroll
+        for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+            for (int b = 0; b < C::TN; ++b)
+                acc[a][b] = mfma32_wt<FP4>(f.b[b], f.a[a], acc[a][b], f.sc[b]);
+    };
+    auto interleave = [&]() {
+        constexpr int NM = C::TM * C::TN;
+        constexpr int NR = 2 * (C::TM + C::TN) + C::TN;
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, (NR + NM - 1) / NM, 0);  // DS read
+        }
+    };
+
+    // prologue: steps 0 .. NBUF-2 in flight; wait for steps 0 and 1
+#pragma unroll
+    for (int s = 0; s < NBUF - 1; ++s) issue(s);
+    wait_loads_and_barrier<C::LPS * (NBUF - 3)>();
+    Frags f0, f1;
+    read_frags(f0, 0);
+
+    // step s: loads of step s + NBUF - 1; MFMAs on step s's fragments; reads
+    // of step s + 1's; then wait until step s + 2's stage has landed.
+    auto step = [&](const Frags &cur, Frags &nxt, int s) {
+        issue(s + NBUF - 1);
+        mfmas(cur);
+        read_frags(nxt, s + 1);
+        interleave();
+        wait_loads_and_barrier<C::LPS * (NBUF - 3)>();
+    };
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {
+        step(f0, f1, s);
+        step(f1, f0, s + 1);
+    }
+    if (s < nsteps) mfmas(f0);
+
+    // ---- epilogue: every load has landed and every wave is done with the
+    // ring. Each wave scales one 32-row slab of its tile by the per-token
+    // scales (in the accumulator layout, where a lane holds one row), stages
+    // it in LDS as fp32, and reads it back with each lane on 4 fixed columns
+    // of a row, where it adds the bias, applies GELU, rounds to bf16 and
+    // writes whole 256-byte row segments.
+    wait_loads_and_barrier<0>();
+    uint8_t *slab = lds + wave * C::EP_WAVE;
+    constexpr int LPR = C::TN * 32 / 4;   // lanes per slab row in the store phase
+    constexpr int RPI = 64 / LPR;         // slab rows per store instruction
+    const int scol = 4 * (lane % LPR);    // this lane's first column in the wave's half
+    const int nst = n0 + wn * (BN / 2) + scol;
+    float bst[4] = {0.f, 0.f, 0.f, 0.f};
+    if (epi != EPI_NONE) {   // uniform; columns past N read column 0 and are not stored
+        const int nn = nst < N ? nst : 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bst[j] = bf16_to_f32(bias[nn + j]);
+    }
+    float asv[C::TM];
+#pragma unroll
+    for (int a = 0; a < C::TM; ++a) {
+        const int m = m0 + wm * (BM / 2) + a * 32 + li;
+        asv[a] = a_scale[m < M ? m : 0];   // rows past M are not stored
+    }
+#pragma unroll
+    for (int a = 0; a < C::TM; ++a) {
+#pragma unroll
+        for (int b = 0; b < C::TN; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = b * 32 + 8 * q + 4 * lg;
+                float4 v;
+                v.x = asv[a] * acc[a][b][4 * q + 0];
+                v.y = asv[a] * acc[a][b][4 * q + 1];
+                v.z = asv[a] * acc[a][b][4 * q + 2];
+                v.w = asv[a] * acc[a][b][4 * q + 3];
+                *reinterpret_cast<float4 *>(slab + li * C::EP_ROW + 4 * col) = v;
+            }
+        __syncthreads();
+        const int mrow = m0 + wm * (BM / 2) + a * 32;
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+            const int rr = it * RPI + lane / LPR;
+            const float4 v = *reinterpret_cast<const float4 *>(slab + rr * C::EP_ROW + 4 * scol);
+            const uint32_t h0 = f32_to_bf16(epilogue_rest(v.x, bst[0], epi));
+            const uint32_t h1 = f32_to_bf16(epilogue_rest(v.y, bst[1], epi));
+            const uint32_t h2 = f32_to_bf16(epilogue_rest(v.z, bst[2], epi));
+            const uint32_t h3 = f32_to_bf16(epilogue_rest(v.w, bst[3], epi));
+            const int m = mrow + rr;
+            if (m < M && nst < N)
+                *reinterpret_cast<uint2 *>(Y + (int64_t)m * ldy + nst) =
+                    make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        }
+        __syncthreads();
+    }
+}
+
+template <bool FP4, int BM, int BN, int NBUF>
+hipError_t launch_tile_dma(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w,
+                           int64_t ldw, const uint8_t *ws, const uint16_t *bias, int epi,
+                           uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                           hipStream_t st) {
+    auto kern = gemm_prefill_dma_kernel<FP4, BM, BN, NBUF>;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), 0, st, a, lda, as, w, ldw, ws, bias,
+                       epi, y, ldy, (int)M, (int)N, (int)K, 8);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_prefill(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
@@ -331,10 +633,21 @@ hipError_t launch_gemm_prefill(bool fp4, const uint8_t *a, int64_t lda, const fl
                                                    M, N, K, st)                                    \
                : launch_tile<false, BM_, BN_, 2, 2>(a, lda, a_scale, w, ldw, ws, bias, epi, y,     \
                                                     ldy, M, N, K, st)
+#define BSG_PREFILL_DMA(BM_, BN_)                                                              \
+    return fp4 ? launch_tile_dma<true, BM_, BN_, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, \
+                                                    M, N, K, st)                                    \
+               : launch_tile_dma<false, BM_, BN_, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y,     \
+                                                     ldy, M, N, K, st)
+    if (K % 64 == 0) {
+        if (t256 >= num_cus) BSG_PREFILL_DMA(256, 256);
+        if (t128 >= num_cus) BSG_PREFILL_DMA(256, 128);
+        BSG_PREFILL_DMA(128, 128);
+    }
     if (t256 >= num_cus) BSG_PREFILL(256, 256);
     if (t128 >= num_cus) BSG_PREFILL(256, 128);
     BSG_PREFILL(128, 128);
 #undef BSG_PREFILL
+#undef BSG_PREFILL_DMA
 }
 
 }  // namespace bsg

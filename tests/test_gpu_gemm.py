@@ -62,6 +62,37 @@ def test_prefill_shapes(fmt, M, N, K):
         _full_check(fmt, M, N, K, epi, seed=M + N + K + epi)
 
 
+# ---- prefill with K a multiple of 64 (tiles staged by LDS-mode loads):
+# ragged M and N on each tile size, outputs past M / N untouched
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("M,N,K", [(65, 96, 64), (200, 320, 640), (129, 416, 128),
+                                   (300, 288, 1024)])
+def test_prefill_dma_shapes(fmt, M, N, K):
+    for epi in EPIS:
+        _full_check(fmt, M, N, K, epi, seed=M + N + K + epi)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("M,N,K", [(4000, 2016, 192), (3900, 4064, 128)])
+def test_prefill_dma_large_tiles(fmt, M, N, K):
+    # 256x128 and 256x256 tiles (the tile count reaches the CU count), ragged
+    # in M and N; y is a view into a larger NaN-filled buffer
+    for epi in (synth.EPI_NONE, synth.EPI_BIAS_GELU_TANH):
+        a, s, w, ws, b = _random_problem(fmt, M, N, K, seed=M + N + epi)
+        y_full = torch.full((M + 3, N + 64), float("nan"), dtype=torch.bfloat16, device=DEV)
+        fn = bs.gemm_bs_fp8 if fmt == "fp8" else bs.gemm_mxfp4_w4a8
+        fn(u8_dev(a), f32_dev(s), u8_dev(w), u8_dev(ws), bf16_dev(b) if epi else None, epi,
+           y=y_full[:M, :N])
+        full = y_host(y_full)
+        assert np.isnan(full[M:, :]).all() and np.isnan(full[:, N:]).all()
+        ms, ns = _sample_positions(M, N, 5000, epi)
+        edge_m = np.concatenate([np.full(N, M - 1), np.arange(M)])
+        edge_n = np.concatenate([np.arange(N), np.full(M, N - 1)])
+        ms, ns = np.concatenate([ms, edge_m]), np.concatenate([ns, edge_n])
+        ref, absum = oracle.gemm_sampled(fmt, a, s, w, ws, b if epi else None, epi, ms, ns)
+        assert_within(full[ms, ns], ref, absum, "%s M=%d N=%d K=%d epi=%d" % (fmt, M, N, K, epi))
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
 @pytest.mark.parametrize("M", [8, 40, 300])
 def test_padded_leading_dims(fmt, M):

@@ -67,6 +67,8 @@ def test_gemm_argument_checks(name):
     assert _gemm(fn, lda=32) == E                  # ld_a < K
     assert _gemm(fn, ldy=32) == E                  # ld_y < N
     assert _gemm(fn, ldw=16) == E                  # ld_w < row bytes
+    assert _gemm(fn, lda=(1 << 22) + 16) == E      # row strides above 4 MiB
+    assert _gemm(fn, ldw=(1 << 22) + 16) == E
     A = bs.BS_EALIGN
     assert _gemm(fn, a=ctypes.c_void_p(0x10008)) == A
     assert _gemm(fn, w=ctypes.c_void_p(0x10004)) == A
