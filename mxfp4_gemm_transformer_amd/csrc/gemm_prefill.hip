@@ -453,22 +453,24 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_dma_kernel(
     const uint32_t s_off = tid < C::SC_ROWS ? (uint32_t)(tid * KB) : OOB;
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t *)lds);
 
-    // LDS-mode loads of step s into ring buffer s % NBUF; past the last step
-    // every lane reads outside the buffers' ranges, which writes zeros.
-    auto issue = [&](int s) {
+    // Load i (0 .. LPS-1) of step s into ring buffer s % NBUF: the A chunks,
+    // the W chunks, then the scale pairs. Past the last step every lane
+    // reads outside the buffers' ranges, which writes zeros.
+    auto issue_one = [&](int s, int i) {
         const bool live = s < nsteps;
         const uint32_t kbase = (uint32_t)__builtin_amdgcn_readfirstlane(live ? s * BK : 0);
         const uint32_t base = lds0 + (uint32_t)((s % NBUF) * C::STAGE) + (uint32_t)wave * 1024u;
-        const uint32_t va = live ? a_off : OOB, vw = live ? w_off : OOB;
-#pragma unroll
-        for (int j = 0; j < C::A_LD; ++j)
-            dma_b128(rsA, base + j * C::NT * 16, va, (uint32_t)(j * A_ROWS_PER_J * lda) + kbase);
-#pragma unroll
-        for (int j = 0; j < C::W_LD; ++j)
-            dma_b128(rsW, base + C::A_STAGE + j * C::NT * 16, vw,
+        if (i < C::A_LD) {
+            dma_b128(rsA, base + i * C::NT * 16, live ? a_off : OOB,
+                     (uint32_t)(i * A_ROWS_PER_J * lda) + kbase);
+        } else if (i < C::A_LD + C::W_LD) {
+            const int j = i - C::A_LD;
+            dma_b128(rsW, base + C::A_STAGE + j * C::NT * 16, live ? w_off : OOB,
                      (uint32_t)(j * W_ROWS_PER_J * ldw) + (FP4 ? kbase / 2 : kbase));
-        dma_u16(rsS, lds0 + (uint32_t)((s % NBUF) * C::STAGE + C::SC_OFF) + (uint32_t)wave * 256u,
-                live ? s_off + (kbase >> 5) : OOB);
+        } else {
+            dma_u16(rsS, lds0 + (uint32_t)((s % NBUF) * C::STAGE + C::SC_OFF) + (uint32_t)wave * 256u,
+                    live ? s_off + (kbase >> 5) : OOB);
+        }
     };
 
     v16f acc[C::TM][C::TN];
@@ -484,31 +486,47 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_dma_kernel(
         v8i b[C::TN];
         int sc[C::TN];
     };
-    auto read_frags = [&](Frags &f, int s) {
+    // fragments of step s (ring buffer s % NBUF): A tile a, W tile b (+ its scales)
+    auto read_a = [&](Frags &f, int s, int a) {
         const uint8_t *sa = lds + (s % NBUF) * C::STAGE;
-        const uint8_t *sw = sa + C::A_STAGE;
-        const uint8_t *ss = sa + C::SC_OFF;
+        const int row = wm * (BM / 2) + a * 32 + li;
+        const int fz = swz4(row);
+        const uint8_t *p = sa + row * BK;
+        f.a[a] = pack8(lds16(p + 16 * (lg ^ fz)), lds16(p + 16 * ((2 + lg) ^ fz)));
+    };
+    auto read_b = [&](Frags &f, int s, int b) {
+        const uint8_t *sw = lds + (s % NBUF) * C::STAGE + C::A_STAGE;
+        const uint8_t *ss = lds + (s % NBUF) * C::STAGE + C::SC_OFF;
+        const int row = wn * (BN / 2) + b * 32 + li;
+        if (FP4) {
+            f.b[b] = pack8(lds16(sw + row * C::WROW + 16 * (lg ^ swz2(row))),
+                           make_uint4(0u, 0u, 0u, 0u));
+            f.sc[b] = ss[4 * row + lg];
+        } else {
+            const int fz = swz4(row);
+            const uint8_t *p = sw + row * C::WROW;
+            f.b[b] = pack8(lds16(p + 16 * (lg ^ fz)), lds16(p + 16 * ((2 + lg) ^ fz)));
+            f.sc[b] = ss[4 * (row >> 5) + lg];
+        }
+    };
+    // The loads of a step go one before each fragment read, so that with the
+    // MFMAs interleaved between the reads they spread over the whole step:
+    // issued as one block they stall the wave's instruction stream, which
+    // (one wave per SIMD) is the MFMA stream.
+    auto reads_and_loads = [&](Frags &f, int s_read, int s_load) {
+        int k = 0;
 #pragma unroll
         for (int a = 0; a < C::TM; ++a) {
-            const int row = wm * (BM / 2) + a * 32 + li;
-            const int fz = swz4(row);
-            const uint8_t *p = sa + row * BK;
-            f.a[a] = pack8(lds16(p + 16 * (lg ^ fz)), lds16(p + 16 * ((2 + lg) ^ fz)));
+            if (k < C::LPS) issue_one(s_load, k++);
+            read_a(f, s_read, a);
         }
 #pragma unroll
         for (int b = 0; b < C::TN; ++b) {
-            const int row = wn * (BN / 2) + b * 32 + li;
-            if (FP4) {
-                f.b[b] = pack8(lds16(sw + row * C::WROW + 16 * (lg ^ swz2(row))),
-                               make_uint4(0u, 0u, 0u, 0u));
-                f.sc[b] = ss[4 * row + lg];
-            } else {
-                const int fz = swz4(row);
-                const uint8_t *p = sw + row * C::WROW;
-                f.b[b] = pack8(lds16(p + 16 * (lg ^ fz)), lds16(p + 16 * ((2 + lg) ^ fz)));
-                f.sc[b] = ss[4 * (row >> 5) + lg];
-            }
+            if (k < C::LPS) issue_one(s_load, k++);
+            read_b(f, s_read, b);
         }
+#pragma unroll
+        for (; k < C::LPS; ++k) issue_one(s_load, k);
     };
     auto mfmas = [&](const Frags &f) {
 #pragma unroll
@@ -529,17 +547,22 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_dma_kernel(
 
     // prologue: steps 0 .. NBUF-2 in flight; wait for steps 0 and 1
 #pragma unroll
-    for (int s = 0; s < NBUF - 1; ++s) issue(s);
+    for (int s = 0; s < NBUF - 1; ++s)
+#pragma unroll
+        for (int i = 0; i < C::LPS; ++i) issue_one(s, i);
     wait_loads_and_barrier<C::LPS * (NBUF - 3)>();
     Frags f0, f1;
-    read_frags(f0, 0);
+#pragma unroll
+    for (int a = 0; a < C::TM; ++a) read_a(f0, 0, a);
+#pragma unroll
+    for (int b = 0; b < C::TN; ++b) read_b(f0, 0, b);
 
-    // step s: loads of step s + NBUF - 1; MFMAs on step s's fragments; reads
-    // of step s + 1's; then wait until step s + 2's stage has landed.
+    // step s: MFMAs on step s's fragments, interleaved with the reads of
+    // step s + 1's and the loads of step s + NBUF - 1; then wait until step
+    // s + 2's stage has landed.
     auto step = [&](const Frags &cur, Frags &nxt, int s) {
-        issue(s + NBUF - 1);
         mfmas(cur);
-        read_frags(nxt, s + 1);
+        reads_and_loads(nxt, s + 1, s + NBUF - 1);
         interleave();
         wait_loads_and_barrier<C::LPS * (NBUF - 3)>();
     };
