@@ -662,8 +662,17 @@ hipError_t launch_gemm_prefill(bool fp4, const uint8_t *a, int64_t lda, const fl
                : launch_tile_dma<false, BM_, BN_, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y,     \
                                                      ldy, M, N, K, st)
     if (K % 64 == 0) {
-        if (t256 >= num_cus) BSG_PREFILL_DMA(256, 256);
-        if (t128 >= num_cus) BSG_PREFILL_DMA(256, 128);
+        // Tile size by a round-aware cost: workgroups run in rounds of one
+        // per CU, and a round costs c * K + e, where c is a tile's time per
+        // unit of K and e its fixed part (prologue, epilogue), both relative
+        // to a 256x256 tile, fitted to timings on MI355X: smaller tiles do
+        // less work per round but at a lower MFMA efficiency.
+        const int64_t t64 = ((M + 127) / 128) * ((N + 127) / 128);
+        const double cost256 = (double)((t256 + num_cus - 1) / num_cus) * (1.0 * K + 930.0);
+        const double cost128 = (double)((t128 + num_cus - 1) / num_cus) * (0.73 * K + 465.0);
+        const double cost64 = (double)((t64 + num_cus - 1) / num_cus) * (0.415 * K + 236.0);
+        if (cost256 <= cost128 && cost256 <= cost64) BSG_PREFILL_DMA(256, 256);
+        if (cost128 <= cost64) BSG_PREFILL_DMA(256, 128);
         BSG_PREFILL_DMA(128, 128);
     }
     if (t256 >= num_cus) BSG_PREFILL(256, 256);
