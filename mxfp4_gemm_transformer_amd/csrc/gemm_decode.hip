@@ -27,6 +27,20 @@
 namespace bsg {
 namespace {
 
+constexpr uint32_t OOB_OFF = 0x80000000u;   // a per-lane offset past every buffer: reads zero
+
+// A raw buffer descriptor over [base, base + bytes), bytes clipped to 2^31 - 16.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                             (int)(bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes),
+                                             0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t rs, uint32_t voff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <bool FP4, bool FOLD, int MT, int NW, int SPW>
 __global__ __launch_bounds__(NW * 64) void gemm_decode_kernel(
     const uint8_t *__restrict__ A, int64_t lda, const float *__restrict__ a_scale,
@@ -47,6 +61,27 @@ __global__ __launch_bounds__(NW * 64) void gemm_decode_kernel(
     const int nsteps = (K + KSTEP - 1) / KSTEP;
     const uint8_t *wrow = W + n * ldw;
     const uint8_t *wsrow = FP4 ? WS + n * KB : WS + (n >> 5) * KB;
+
+    // the epilogue's per-token scales and bias, fetched first so that the
+    // epilogue waits for no global load (entries idx = tid, tid + NW*64)
+    constexpr int EPI_IT = (ROWS * COLS + NW * 64 - 1) / (NW * 64);
+    float ep_as[EPI_IT], ep_b[EPI_IT];
+    {
+        const __amdgpu_buffer_rsrc_t rsT = make_rsrc(a_scale, (int64_t)M * 4);
+        const __amdgpu_buffer_rsrc_t rsB =
+            epi != EPI_NONE ? make_rsrc(bias + (int64_t)blockIdx.x * COLS, COLS * 2)
+                            : make_rsrc(bias, 0);
+#pragma unroll
+        for (int it = 0; it < EPI_IT; ++it) {
+            const int idx = threadIdx.x + it * NW * 64;
+            const int r = idx / COLS, c = idx % COLS;
+            const bool ok = idx < ROWS * COLS;
+            ep_as[it] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rsT, (ok & (r < M)) ? (uint32_t)(4 * r) : OOB_OFF, 0, 0));
+            ep_b[it] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
+                rsB, ok ? (uint32_t)(2 * c) : OOB_OFF, 0, 0));
+        }
+    }
 
     v4f acc[MT];
 #pragma unroll
@@ -111,15 +146,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_decode_kernel(
             for (int v = 0; v < 4; ++v) red[wave][mt * 16 + 4 * g + v][i] = acc[mt][v];
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < ROWS * COLS; idx += NW * 64) {
+#pragma unroll
+    for (int it = 0; it < EPI_IT; ++it) {
+        const int idx = threadIdx.x + it * NW * 64;
         const int r = idx / COLS, c = idx % COLS;
-        if (r < M) {
+        if ((idx < ROWS * COLS) & (r < M)) {
             float sum = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) sum += red[w][r][c];
             const int64_t nn = (int64_t)blockIdx.x * COLS + c;
-            const float b = epi != EPI_NONE ? bf16_to_f32(bias[nn]) : 0.f;
-            Y[(int64_t)r * ldy + nn] = (uint16_t)f32_to_bf16(epilogue(sum, a_scale[r], b, epi));
+            Y[(int64_t)r * ldy + nn] = (uint16_t)f32_to_bf16(epilogue(sum, ep_as[it], ep_b[it], epi));
         }
     }
 }
@@ -154,14 +190,281 @@ void launch_spw(int per_wave, const uint8_t *a, int64_t lda, const float *as, co
                                                           ldy, M, N, K, st);
 }
 
+
+// Balanced variant: one workgroup of 16 waves per CU, all of it resident at
+// once. Workgroup b owns `gpw` consecutive groups of 8 weight rows; its work
+// is the list of (group, 256-k step) units in group-major order, cut into 16
+// equal contiguous ranges, one per wave, so every wave has the same number
+// of weight loads in flight from the start whatever N / 8 / CUs is. The
+// activations (a padded row per token) and the workgroup's E8M0 scales are
+// read once per workgroup into LDS, ahead of the weights, so waiting for
+// them does not wait for the weight stream. Tokens are folded as in the
+// kernel above, MT groups of 8 sharing each weight fragment. Group sums go
+// through LDS: a group a wave covers whole as that wave's sum, a group cut
+// between waves (a wave's first and last group) as partial sums added in
+// wave order; the epilogue runs after every weight has been consumed.
+// Needs K % 128 == 0 (scale rows in whole 4-byte words).
+constexpr int UNIT_WAVES = 16;
+
+template <bool FP4, int MT>
+struct UnitsLds {
+    static constexpr int TOK = 8 * MT;
+    __host__ __device__ static size_t a_bytes(int K) { return (size_t)TOK * (K + 16); }
+    // scale rows of the workgroup: one per weight row (fp4) or per 32 rows
+    __host__ __device__ static int scale_rows(int gpw) { return FP4 ? 8 * gpw : (8 * gpw + 31) / 32 + 1; }
+    // then the sums: one slot per group (groups a wave covers whole) and
+    // two per wave (its first and last group, when cut between waves)
+    // and the per-token scales and the bias of the workgroup's rows
+    static size_t bytes(int K, int gpw) {
+        return a_bytes(K) + (size_t)scale_rows(gpw) * (K / 32) +
+               (size_t)(gpw + UNIT_WAVES * 2) * 64 * MT * sizeof(float) +
+               (size_t)(TOK + 8 * gpw) * sizeof(float);
+    }
+};
+
+template <bool FP4, int MT, int P>
+__global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
+    const uint8_t *__restrict__ A, int64_t lda, const float *__restrict__ a_scale,
+    const uint8_t *__restrict__ W, int64_t ldw, const uint8_t *__restrict__ WS,
+    const uint16_t *__restrict__ bias, int epi, uint16_t *__restrict__ Y, int64_t ldy, int M,
+    int N, int K, int gpw) {
+    using L = UnitsLds<FP4, MT>;
+    extern __shared__ __align__(16) uint8_t lds[];
+    constexpr int KSTEP = 256;
+    constexpr int TOK = L::TOK;
+    constexpr int PE = 64 * MT;                     // partial sums per group (tokens x rows)
+    const int lds_row = K + 16;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i = lane & 15, g = lane >> 4;
+    const int col = i & 7, half = i >> 3;
+    const int KB = K >> 5;
+    const int S = (K + KSTEP - 1) / KSTEP;           // units per group
+    const int G = N >> 3;
+    const int gb = blockIdx.x * gpw;                 // first group of this workgroup
+    const int ng = min(gpw, G - gb);
+    const int U = ng * S;
+    const int upw = (U + UNIT_WAVES - 1) / UNIT_WAVES;
+    const int u0 = min(U, wave * upw), u1 = min(U, u0 + upw);
+    const int row0 = gb * 8;                         // the workgroup's first weight row
+    const int srow0 = FP4 ? row0 : (row0 >> 5);
+    const int nsrows = FP4 ? ng * 8 : ((row0 + ng * 8 - 1) >> 5) - srow0 + 1;
+    uint8_t *s_lds = lds + L::a_bytes(K);
+    float *gsum = reinterpret_cast<float *>(s_lds + (size_t)L::scale_rows(gpw) * KB);
+    float *part = gsum + gpw * PE;
+    float *tok_scale = part + UNIT_WAVES * 2 * PE;   // [TOK]
+    float *row_bias = tok_scale + TOK;               // [8 gpw]
+
+    // ---- activations and scales into registers first, then the weights,
+    // then the LDS writes (which wait only for the first two groups of
+    // loads). Every load is a range-checked buffer load (reads past a
+    // buffer's range return zeros), issued unconditionally, so the compiler
+    // counts them exactly and waits for no more than it needs.
+    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(A, (int64_t)M * lda);
+    const __amdgpu_buffer_rsrc_t rsS =
+        make_rsrc(WS + (int64_t)srow0 * KB, (int64_t)nsrows * KB);
+    const __amdgpu_buffer_rsrc_t rsW = make_rsrc(W + (int64_t)row0 * ldw, (int64_t)ng * 8 * ldw);
+    constexpr int ACH = 8 * MT * 8192 / 16 / 1024;   // 16-byte chunks per thread for K <= 8192
+    const int kc = K >> 4, chunks = TOK * kc;
+    uint4 av[ACH];
+#pragma unroll
+    for (int j = 0; j < ACH; ++j) {
+        const int c = threadIdx.x + j * 1024;
+        const int t = c / kc, k = 16 * (c % kc);
+        av[j] = bload16(rsA, ((c < chunks) & (t < M)) ? (uint32_t)(t * lda + k) : OOB_OFF);
+    }
+    // the epilogue's per-token scales and bias, fetched now so that the
+    // epilogue waits for no global load (one value per thread at most)
+    // (range-checked buffer loads: branch-free, so the compiler counts them)
+    float ep_val;
+    {
+        const __amdgpu_buffer_rsrc_t rsT = make_rsrc(a_scale, (int64_t)M * 4);
+        // bias of this workgroup's rows (no bias: an empty range, nothing read)
+        const __amdgpu_buffer_rsrc_t rsB =
+            epi != EPI_NONE ? make_rsrc(bias + row0, (int64_t)(N - row0) * 2) : make_rsrc(bias, 0);
+        const int t = threadIdx.x;
+        const uint32_t ts = __builtin_amdgcn_raw_buffer_load_b32(
+            rsT, t < TOK ? (uint32_t)(4 * t) : OOB_OFF, 0, 0);
+        const uint32_t bb = __builtin_amdgcn_raw_buffer_load_b16(
+            rsB, ((t >= TOK) & (t < TOK + 8 * ng)) ? (uint32_t)(2 * (t - TOK)) : OOB_OFF, 0, 0);
+        ep_val = t < TOK ? __uint_as_float(ts) : bf16_to_f32(bb);
+    }
+    const int words = nsrows * (KB >> 2);
+    constexpr int SCW = 8;                           // scale words per thread (the launcher checks the bound)
+    uint32_t sv[SCW];
+#pragma unroll
+    for (int j = 0; j < SCW; ++j) {
+        const int c = threadIdx.x + j * 1024;
+        sv[j] = __builtin_amdgcn_raw_buffer_load_b32(rsS, c < words ? (uint32_t)(4 * c) : OOB_OFF,
+                                                     0, 0);
+    }
+
+    // keep the weight loads behind the activation and scale loads, so that
+    // waiting for those two does not wait for any weights
+    __builtin_amdgcn_sched_barrier(0);
+
+    // weights: a rolling window of WIN units in flight per wave (slot q % WIN);
+    // (gl, st) of the next unit to load, advanced without division
+    constexpr int WIN = FP4 ? 12 : 6;   // 12 KB (fp4) or 12 KB (e4m3) per wave
+    uint4 wlo[WIN], whi[FP4 ? 1 : WIN];
+    const int gl0 = u0 / S, st0 = u0 - gl0 * S;
+    int lgl = gl0, lst = st0;
+    auto load_unit = [&](int q) {
+        const bool on = u0 + q < u1;
+        const int k0 = lst * KSTEP + half * 128;
+        const int kblk = k0 + 32 * g, klo = k0 + 16 * g, khi = k0 + 64 + 16 * g;
+        const uint32_t rowoff = (uint32_t)((lgl * 8 + col) * ldw);
+        if (FP4) {
+            wlo[q % WIN] = bload16(rsW, (on & (kblk < K)) ? rowoff + (kblk >> 1) : OOB_OFF);
+        } else {
+            wlo[q % WIN] = bload16(rsW, (on & (klo < K)) ? rowoff + klo : OOB_OFF);
+            whi[q % WIN] = bload16(rsW, (on & (khi < K)) ? rowoff + khi : OOB_OFF);
+        }
+        if (++lst == S) { lst = 0; ++lgl; }
+    };
+#pragma unroll
+    for (int q = 0; q < (P < WIN ? P : WIN); ++q) load_unit(q);
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int j = 0; j < ACH; ++j) {
+        const int c = threadIdx.x + j * 1024;
+        const int t = c / kc, k = 16 * (c % kc);
+        if (c < chunks) *reinterpret_cast<uint4 *>(lds + t * lds_row + k) = av[j];
+    }
+#pragma unroll
+    for (int j = 0; j < SCW; ++j) {
+        const int c = threadIdx.x + j * 1024;
+        if (c < words) *reinterpret_cast<uint32_t *>(s_lds + 4 * c) = sv[j];
+    }
+    if (threadIdx.x < TOK + 8 * ng) tok_scale[threadIdx.x] = ep_val;   // row_bias follows tok_scale
+    __syncthreads();
+
+    // ---- this wave's units; a group's sum is flushed when the next group
+    // starts and at the end
+    v4f acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    auto flush = [&](int gl, int cover0, int cover1) {
+        // fold: lanes g < 2, i < 8 hold tokens 8 mt + 4 g + v of row 8 gl + i
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[mt][v] += __shfl_down(acc[mt][v], 40, 64);
+        // sums only go to LDS here: an epilogue's global loads (scales,
+        // bias) would make the compiler wait for the whole weight window
+        const bool whole = cover0 == gl * S && cover1 == (gl + 1) * S;
+        if ((g < 2) & (i < 8)) {
+            float *dst = whole ? gsum + gl * PE : part + (wave * 2 + (gl == gl0 ? 0 : 1)) * PE;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) dst[(mt * 8 + 4 * g + v) * 8 + i] = acc[mt][v];
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    };
+    int cgl = gl0, cst = st0, start = u0;   // (group, step) of the unit consumed next
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int u = u0 + q;
+        if (u < u1) {
+            if (cst == 0 && u != u0) {   // uniform: the previous group ended
+                flush(cgl - 1, start, u);
+                start = u;
+            }
+            const int k0 = cst * KSTEP + half * 128;
+            const int kblk = k0 + 32 * g, klo = k0 + 16 * g, khi = k0 + 64 + 16 * g;
+            const int srl = FP4 ? cgl * 8 + col : ((row0 + cgl * 8 + col) >> 5) - srow0;
+            const int sc = kblk < K ? s_lds[srl * KB + (kblk >> 5)] : E8M0_ONE;
+            const v8i wv = pack8(wlo[q % WIN], FP4 ? make_uint4(0u, 0u, 0u, 0u) : whi[FP4 ? 0 : q % WIN]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const uint8_t *arow = lds + (mt * 8 + col) * lds_row;
+                uint4 alo = make_uint4(0u, 0u, 0u, 0u), ahi = alo;
+                if (klo < K) alo = *reinterpret_cast<const uint4 *>(arow + klo);
+                if (khi < K) ahi = *reinterpret_cast<const uint4 *>(arow + khi);
+                acc[mt] = mfma16<FP4>(pack8(alo, ahi), wv, acc[mt], E8M0_ONE, sc);
+            }
+            if (++cst == S) { cst = 0; ++cgl; }
+        }
+        if (q + WIN < P) load_unit(q + WIN);   // refill the slot just used
+    }
+    if (u0 < u1) flush(cst == 0 ? cgl - 1 : cgl, start, u1);
+    __syncthreads();
+
+    // ---- epilogue: a group's sum is its whole-owner's, or the partial sums
+    // of the waves it was cut between, added in wave order
+    // The waves holding group gl's units [gl S, gl S + S) are w0 .. w1 (the
+    // ranges are contiguous, upw units each); if w0 == w1 it is whole. A cut
+    // group is the first group of waves w0 + 1 .. w1 (slot 0), and of w0 too
+    // if w0's range starts at the group's first unit, else w0's last (slot 1).
+    for (int t = threadIdx.x; t < ng * PE; t += 1024) {
+        const int gl = t / PE, e = t % PE;
+        const int w0 = (gl * S) / upw, w1 = (gl * S + S - 1) / upw;
+        float sum;
+        if (w0 == w1) {
+            sum = gsum[gl * PE + e];
+        } else {
+            sum = part[(w0 * 2 + (w0 * upw >= gl * S ? 0 : 1)) * PE + e];
+            for (int w = w0 + 1; w <= w1; ++w) sum += part[(w * 2) * PE + e];
+        }
+        const int m = e / 8, r = e % 8;
+        if (m >= M) continue;
+        const int64_t nn = (int64_t)row0 + gl * 8 + r;
+        Y[(int64_t)m * ldy + nn] =
+            (uint16_t)f32_to_bf16(epilogue(sum, tok_scale[m], row_bias[gl * 8 + r], epi));
+    }
+}
+
+template <bool FP4, int MT, int P>
+void launch_units(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w, int64_t ldw,
+                  const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y, int64_t ldy,
+                  int64_t M, int64_t N, int64_t K, int gpw, hipStream_t st) {
+    const size_t lds = UnitsLds<FP4, MT>::bytes((int)K, gpw);
+    const int64_t groups = N / 8;
+    hipLaunchKernelGGL((gemm_decode_units_kernel<FP4, MT, P>),
+                       dim3((unsigned)((groups + gpw - 1) / gpw)), dim3(1024), lds, st, a, lda, as,
+                       w, ldw, ws, bias, epi, y, ldy, (int)M, (int)N, (int)K, gpw);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
                               const uint8_t *w, int64_t ldw, const uint8_t *ws,
                               const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
                               int64_t N, int64_t K, int num_cus, hipStream_t st) {
-    (void)num_cus;
     constexpr int NW = 8;
+    // Balanced units kernel for wide layers (at least two 8-row groups per
+    // CU; below that the split-K kernel, which reads its activations straight
+    // into registers, is faster): one workgroup per CU, groups split evenly,
+    // when the activations and scales fit in LDS and the scale rows are
+    // whole, aligned 4-byte words.
+    const int64_t groups = N / 8;
+    const int gpw = (int)((groups + num_cus - 1) / num_cus);
+    if (M <= 16 && gpw >= 2 && K % 128 == 0 && K <= 8192 &&
+        (reinterpret_cast<uintptr_t>(ws) & 3u) == 0) {
+        const int64_t S = (K + 255) / 256;
+        const int64_t upw = (gpw * S + UNIT_WAVES - 1) / UNIT_WAVES;
+        const int mt = M <= 8 ? 1 : 2;
+        const size_t lds = mt == 1 ? UnitsLds<true, 1>::bytes((int)K, gpw)
+                                   : UnitsLds<true, 2>::bytes((int)K, gpw);
+        const size_t lds8 = mt == 1 ? UnitsLds<false, 1>::bytes((int)K, gpw)
+                                    : UnitsLds<false, 2>::bytes((int)K, gpw);
+        const int64_t scale_words = (fp4 ? 8 * gpw : (8 * gpw + 31) / 32 + 1) * (K / 128);
+        if (upw <= (fp4 ? 32 : 16) && (fp4 ? lds : lds8) <= 160 * 1024 && scale_words <= 8 * 1024) {
+#define BSG_UNITS(FP4_, MT_)                                                                       \
+    if (upw <= 4) launch_units<FP4_, MT_, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, gpw, st); \
+    else if (upw <= 8) launch_units<FP4_, MT_, 8>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, gpw, st); \
+    else if (upw <= 16) launch_units<FP4_, MT_, 16>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, gpw, st); \
+    else if (upw <= 24) launch_units<true, MT_, 24>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, gpw, st); \
+    else launch_units<true, MT_, 32>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, gpw, st);
+            if (fp4) { if (mt == 1) { BSG_UNITS(true, 1) } else { BSG_UNITS(true, 2) } }
+            else { if (mt == 1) { BSG_UNITS(false, 1) } else { BSG_UNITS(false, 2) } }
+#undef BSG_UNITS
+            return hipGetLastError();
+        }
+    }
     if (M <= 8) {
         const int per = (int)(((K + 255) / 256 + NW - 1) / NW);
         if (fp4)

@@ -46,6 +46,16 @@ def test_decode_shapes(fmt, M):
     _full_check(fmt, M, 96, 1056, synth.EPI_BIAS_GELU_TANH, seed=M)
 
 
+# wide layers (N >= 32768): one 8-row group per wave, activations and
+# scales staged in LDS; N % 64 == 32 leaves the last workgroup half full
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("M,K", [(1, 5120), (5, 640), (8, 128), (9, 640), (16, 1024)])
+def test_decode_wide_rows(fmt, M, K):
+    N = 32768 + 32
+    epi = synth.EPI_BIAS_GELU_TANH if M in (5, 9) else synth.EPI_NONE
+    _full_check(fmt, M, N, K, epi, seed=M + K)
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
 @pytest.mark.parametrize("K", [32, 96, 128, 160, 256, 288, 2080])
 def test_decode_k_tails(fmt, K):
