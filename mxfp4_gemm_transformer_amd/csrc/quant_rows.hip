@@ -23,43 +23,69 @@ __device__ __forceinline__ uint32_t absmax8(const uint4 &c) {
     return m;
 }
 
-// e4m3 code of fl32(x / s), without a division in the common case. With
+// The e4m3 codes of fl32(x / s) for the 8 bf16 values x of a 16-byte chunk,
+// packed little-endian, without a division in the common case. With
 // r = fl32(1/s), q = fl32(x * r) is within 2.5 fp32 ulps of fl32(x / s)
-// (two roundings of 2^-24 relative error each, plus the 1/2 ulp of the exact
-// quotient's own rounding). The e4m3 rounding of a normal value only changes
-// at midpoints between codes, whose low 20 significand bits are exactly
-// 0x80000, and no midpoint lies within 2^19 ulps of a binade edge; so if q's
-// low 20 bits are more than 4 away from 0x80000, q and fl32(x / s) round to
-// the same code. Otherwise, in the subnormal e4m3 range, and for rows whose
-// scale is so small (subnormal) that 1/s overflows, divide.
-__device__ __forceinline__ uint32_t quant_one(float x, float s, float r, bool r_ok) {
-    float q = x * r;
-    const uint32_t mag = __float_as_uint(q) & 0x7FFFFFFFu;
-    const uint32_t d = (mag & 0xFFFFFu) - 0x80000u + 4u;   // in [0, 8] near a midpoint
-    if (!r_ok | (mag < 0x3C800000u) | (d <= 8u)) q = x / s;  // |q| < 2^-6, or close to a tie
-    return e4m3_encode(q);
+// (two roundings of 2^-24 relative error each, plus the 1/2 ulp of the
+// exact quotient's own rounding). The e4m3 rounding of a normal value only
+// changes at midpoints between codes, whose low 20 significand bits are
+// exactly 0x80000, and no midpoint lies within 2^19 ulps of a binade edge;
+// so if q's low 20 bits are more than 4 away from 0x80000, q and fl32(x / s)
+// round to the same code. When any of the 8 products is closer, is in the
+// e4m3 subnormal range (|q| < 2^-6), or 1/s overflowed (s subnormal), the
+// chunk divides instead (one branch per chunk; rare for any real row).
+// The rounding itself is the hardware conversion to e4m3fn after clamping
+// to +-448 (round to nearest even, saturating): on gfx950 that equals the
+// nearest-even saturating encode for every finite fp32 value.
+template <bool HIGH>
+__device__ __forceinline__ uint32_t cvt2_e4m3(float a, float b, uint32_t old) {
+    const float ca = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    const float cb = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, (int)old, HIGH);
 }
 
-// Codes of the 16 bf16 values in two 16-byte chunks, packed little-endian.
-__device__ __forceinline__ uint4 encode16(const uint4 &c0, const uint4 &c1, float s) {
-    const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    uint32_t out[4] = {0u, 0u, 0u, 0u};
-    const float r = 1.0f / s;  // correctly rounded
-    const bool r_ok = (__float_as_uint(r) & 0x7FFFFFFFu) < 0x7F800000u;   // finite
+__device__ __forceinline__ uint2 encode8(const uint4 &c, float s, float r, bool r_ok) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    if (s == 0.0f) {   // an all-zero row (uniform): signed zeros
+        uint32_t out[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t a = w[2 * i], b = w[2 * i + 1];
+            out[i] = ((a >> 8) & 0x80u) | ((a >> 16) & 0x8000u) | ((b << 8) & 0x800000u) |
+                     (b & 0x80000000u);
+        }
+        return make_uint2(out[0], out[1]);
+    }
+    float xv[8], q[8];
+    bool exact = r_ok;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        xv[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+        xv[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint32_t lo = w[i] & 0xFFFFu, hi = w[i] >> 16;
-        uint32_t clo, chi;
-        if (s == 0.0f) {  // an all-zero row: signed zeros
-            clo = (lo >> 8) & 0x80u;
-            chi = (hi >> 8) & 0x80u;
-        } else {
-            clo = quant_one(bf16_to_f32(lo), s, r, r_ok);
-            chi = quant_one(bf16_to_f32(hi), s, r, r_ok);
-        }
-        out[i >> 1] |= (clo | (chi << 8)) << (16 * (i & 1));
+        q[i] = xv[i] * r;
+        const uint32_t mag = __float_as_uint(q[i]) & 0x7FFFFFFFu;
+        const uint32_t d = (mag & 0xFFFFFu) - 0x80000u + 4u;   // in [0, 8] near a midpoint
+        exact &= (mag >= 0x3C800000u) & (d > 8u);
     }
-    return make_uint4(out[0], out[1], out[2], out[3]);
+    if (!exact) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = xv[i] / s;   // correctly rounded fp32 division
+    }
+    uint32_t lo = cvt2_e4m3<false>(q[0], q[1], 0u);
+    lo = cvt2_e4m3<true>(q[2], q[3], lo);
+    uint32_t hi = cvt2_e4m3<false>(q[4], q[5], 0u);
+    hi = cvt2_e4m3<true>(q[6], q[7], hi);
+    return make_uint2(lo, hi);
+}
+
+// 1/s rounded once per row, and whether it is finite (s subnormal: no)
+__device__ __forceinline__ float recip_of(float s, bool &r_ok) {
+    const float r = 1.0f / s;  // correctly rounded
+    r_ok = (__float_as_uint(r) & 0x7FFFFFFFu) < 0x7F800000u;
+    return r;
 }
 
 __device__ __forceinline__ uint32_t group_max(uint32_t v, int width) {
@@ -68,10 +94,13 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v, int width) {
     return v;
 }
 
-// TPR threads per row (16, 64, 256 or 1024); each holds NCH chunks of 16 values
-// in registers between the max reduction and the encode.
+// TPR threads per row (16, 64, 256 or 1024); each holds NCH chunks of 8
+// values (16 bytes) in registers between the max reduction and the encode.
+// Chunk c of a row is handled by thread c % TPR, so each load instruction
+// of a wave reads 64 consecutive chunks (1 KiB) and each store writes 512
+// consecutive code bytes.
 template <int QB, int TPR, int NCH>
-__global__ __launch_bounds__(QB) void quant_rows_kernel(const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(QB, (QB <= 256 && NCH <= 8) ? 4 : 1) void quant_rows_kernel(const uint16_t *__restrict__ x,
                                                             int64_t ldx, uint8_t *__restrict__ q,
                                                             int64_t ldq, float *__restrict__ scale,
                                                             int64_t M, int K) {
@@ -80,41 +109,43 @@ __global__ __launch_bounds__(QB) void quant_rows_kernel(const uint16_t *__restri
     const int t = tid % TPR;
     const int64_t m = (int64_t)blockIdx.x * RPB + tid / TPR;
     const bool active = m < M;
-    const int nch = K >> 4;
+    const int nch = K >> 3;
     const uint16_t *xr = x + (active ? m : 0) * ldx;
 
-    uint4 v[NCH][2];
+    uint4 v[NCH];
     uint32_t amax = 0;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         const int c = t + i * TPR;
         if (active && c < nch) {
-            v[i][0] = ldg16(xr + 16 * c);
-            v[i][1] = ldg16(xr + 16 * c + 8);
-            amax = max(amax, max(absmax8(v[i][0]), absmax8(v[i][1])));
+            v[i] = ldg16(xr + 8 * c);
+            amax = max(amax, absmax8(v[i]));
         } else {
-            v[i][0] = v[i][1] = make_uint4(0u, 0u, 0u, 0u);
+            v[i] = make_uint4(0u, 0u, 0u, 0u);
         }
     }
     if (TPR <= 64) {
         amax = group_max(amax, TPR);
-    } else {
+    } else {   // the TPR / 64 waves of this row meet in LDS
         __shared__ uint32_t red[QB / 64];
         amax = group_max(amax, 64);
         if ((tid & 63) == 0) red[tid >> 6] = amax;
         __syncthreads();
-        amax = red[0];
+        const int w0 = (tid / TPR) * (TPR / 64);
+        amax = red[w0];
 #pragma unroll
-        for (int i = 1; i < QB / 64; ++i) amax = max(amax, red[i]);
+        for (int i = 1; i < TPR / 64; ++i) amax = max(amax, red[w0 + i]);
     }
     const float s = bf16_to_f32(amax) / 448.0f;  // correctly rounded fp32 division
     if (!active) return;
     if (t == 0) scale[m] = s;
+    bool r_ok;
+    const float r = recip_of(s, r_ok);
     uint8_t *qr = q + m * ldq;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         const int c = t + i * TPR;
-        if (c < nch) *reinterpret_cast<uint4 *>(qr + 16 * c) = encode16(v[i][0], v[i][1], s);
+        if (c < nch) *reinterpret_cast<uint2 *>(qr + 8 * c) = encode8(v[i], s, r, r_ok);
     }
 }
 
@@ -128,11 +159,10 @@ __global__ __launch_bounds__(QBLOCK) void quant_rows_long_kernel(const uint16_t 
                                                                  int64_t M, int K) {
     const int64_t m = blockIdx.x;
     const int tid = threadIdx.x;
-    const int nch = K >> 4;
+    const int nch = K >> 3;
     const uint16_t *xr = x + m * ldx;
     uint32_t amax = 0;
-    for (int c = tid; c < nch; c += QBLOCK)
-        amax = max(amax, max(absmax8(ldg16(xr + 16 * c)), absmax8(ldg16(xr + 16 * c + 8))));
+    for (int c = tid; c < nch; c += QBLOCK) amax = max(amax, absmax8(ldg16(xr + 8 * c)));
     __shared__ uint32_t red[QBLOCK / 64];
     amax = group_max(amax, 64);
     if ((tid & 63) == 0) red[tid >> 6] = amax;
@@ -141,10 +171,11 @@ __global__ __launch_bounds__(QBLOCK) void quant_rows_long_kernel(const uint16_t 
     for (int i = 1; i < QBLOCK / 64; ++i) amax = max(amax, red[i]);
     const float s = bf16_to_f32(amax) / 448.0f;
     if (tid == 0) scale[m] = s;
+    bool r_ok;
+    const float r = recip_of(s, r_ok);
     uint8_t *qr = q + m * ldq;
     for (int c = tid; c < nch; c += QBLOCK)
-        *reinterpret_cast<uint4 *>(qr + 16 * c) =
-            encode16(ldg16(xr + 16 * c), ldg16(xr + 16 * c + 8), s);
+        *reinterpret_cast<uint2 *>(qr + 8 * c) = encode8(ldg16(xr + 8 * c), s, r, r_ok);
 }
 
 template <int QB, int TPR, int NCH>
@@ -176,11 +207,14 @@ bool launch_tpr(int nch_per_thread, const uint16_t *x, int64_t ldx, uint8_t *q, 
 hipError_t launch_quant_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_t ld_q,
                              float *scale, int64_t M, int64_t K, hipStream_t stream) {
     const int k = (int)K;
-    const int nch = k / 16;
+    const int nch = k / 8;
     // Many rows: a few threads per row is enough to fill the chip; few
     // rows: spread each row over a whole block (up to 1024 threads) to cut
     // the per-row latency, which is all a decode-sized call costs.
-    int tpr = M >= 512 ? 64 : (M <= 64 ? 1024 : 256);
+    // Many rows with long K: two waves per row keep 8 chunks a thread, few
+    // enough registers for four waves per SIMD to overlap loads with the
+    // (ALU-heavy) encoding.
+    int tpr = M >= 512 ? (nch > 512 ? 128 : 64) : (M <= 64 ? 1024 : 256);
     if (nch <= 16) tpr = 16;
     else if (nch <= 64) tpr = 64;
     else if (nch <= 256 && tpr > 256) tpr = 256;
@@ -188,6 +222,7 @@ hipError_t launch_quant_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_
     bool ok;
     if (tpr == 16) ok = launch_tpr<QBLOCK, 16>(per, x, ld_x, q, ld_q, scale, M, k, stream);
     else if (tpr == 64) ok = launch_tpr<QBLOCK, 64>(per, x, ld_x, q, ld_q, scale, M, k, stream);
+    else if (tpr == 128) ok = launch_tpr<QBLOCK, 128>(per, x, ld_x, q, ld_q, scale, M, k, stream);
     else if (tpr == 256) ok = launch_tpr<QBLOCK, 256>(per, x, ld_x, q, ld_q, scale, M, k, stream);
     else {
         ok = launch_tpr<1024, 1024>(per, x, ld_x, q, ld_q, scale, M, k, stream);
