@@ -369,9 +369,10 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-template <bool FP4, int BM, int BN, int NBUF>
+template <bool FP4, int BM, int BN, int NBUF, int WGM, int WGN>
 struct DCfg {
-    static constexpr int NT = 256;                    // four waves, 2 x 2
+    static constexpr int NW = WGM * WGN;              // waves, WGM x WGN
+    static constexpr int NT = NW * 64;
     static constexpr int WROW = FP4 ? BK / 2 : BK;    // W bytes per row per step
     static constexpr int A_STAGE = BM * BK;
     static constexpr int W_STAGE = BN * WROW;
@@ -380,13 +381,13 @@ struct DCfg {
     static constexpr int A_LD = A_STAGE / 16 / NT;    // 16-byte loads per thread per step
     static constexpr int W_LD = W_STAGE / 16 / NT;
     static constexpr int LPS = A_LD + W_LD + 1;       // loads per thread per stage
-    static constexpr int TM = BM / 64;
-    static constexpr int TN = BN / 64;
+    static constexpr int TM = BM / WGM / 32;
+    static constexpr int TN = BN / WGN / 32;
     static constexpr int SC_ROWS = FP4 ? BN : BN / 32;
     // epilogue staging: each wave's 32 x (32 TN) fp32 slab, rows padded by 16 bytes
     static constexpr int EP_ROW = TN * 32 * 4 + 16;
     static constexpr int EP_WAVE = 32 * EP_ROW;
-    static constexpr int LDS = NBUF * STAGE > 4 * EP_WAVE ? NBUF * STAGE : 4 * EP_WAVE;
+    static constexpr int LDS = NBUF * STAGE > NW * EP_WAVE ? NBUF * STAGE : NW * EP_WAVE;
     static_assert(A_STAGE % (16 * NT) == 0 && W_STAGE % (16 * NT) == 0, "stage split");
     static_assert(SC_ROWS <= NT, "one scale row per thread");
     static_assert(NBUF >= 4, "the ring needs NBUF - 1 >= 3 stages in flight");
@@ -394,13 +395,13 @@ struct DCfg {
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <bool FP4, int BM, int BN, int NBUF>
-__global__ __launch_bounds__(256, 1) void gemm_prefill_dma_kernel(
+template <bool FP4, int BM, int BN, int NBUF, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     const uint8_t *__restrict__ A, int64_t lda, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ W, int64_t ldw, const uint8_t *__restrict__ WS,
     const uint16_t *__restrict__ bias, int epi, uint16_t *__restrict__ Y, int64_t ldy, int M, int N,
     int K, int group_m) {
-    using C = DCfg<FP4, BM, BN, NBUF>;
+    using C = DCfg<FP4, BM, BN, NBUF, WGM, WGN>;
     __shared__ __align__(16) uint8_t lds[C::LDS];
 
     // ---- tile of this workgroup (XCD-aware grouped order)
@@ -415,7 +416,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_dma_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     const int li = lane & 31, lg = lane >> 5;
     const int KB = K >> 5;
     const int nsteps = K / BK;
@@ -489,7 +490,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_dma_kernel(
     // fragments of step s (ring buffer s % NBUF): A tile a, W tile b (+ its scales)
     auto read_a = [&](Frags &f, int s, int a) {
         const uint8_t *sa = lds + (s % NBUF) * C::STAGE;
-        const int row = wm * (BM / 2) + a * 32 + li;
+        const int row = wm * (BM / WGM) + a * 32 + li;
         const int fz = swz4(row);
         const uint8_t *p = sa + row * BK;
         f.a[a] = pack8(lds16(p + 16 * (lg ^ fz)), lds16(p + 16 * ((2 + lg) ^ fz)));
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_dma_kernel(
     auto read_b = [&](Frags &f, int s, int b) {
         const uint8_t *sw = lds + (s % NBUF) * C::STAGE + C::A_STAGE;
         const uint8_t *ss = lds + (s % NBUF) * C::STAGE + C::SC_OFF;
-        const int row = wn * (BN / 2) + b * 32 + li;
+        const int row = wn * (BN / WGN) + b * 32 + li;
         if (FP4) {
             f.b[b] = pack8(lds16(sw + row * C::WROW + 16 * (lg ^ swz2(row))),
                            make_uint4(0u, 0u, 0u, 0u));
@@ -584,7 +585,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_dma_kernel(
     constexpr int LPR = C::TN * 32 / 4;   // lanes per slab row in the store phase
     constexpr int RPI = 64 / LPR;         // slab rows per store instruction
     const int scol = 4 * (lane % LPR);    // this lane's first column in the wave's half
-    const int nst = n0 + wn * (BN / 2) + scol;
+    const int nst = n0 + wn * (BN / WGN) + scol;
     float bst[4] = {0.f, 0.f, 0.f, 0.f};
     if (epi != EPI_NONE) {   // uniform; columns past N read column 0 and are not stored
         const int nn = nst < N ? nst : 0;
@@ -594,7 +595,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_dma_kernel(
     float asv[C::TM];
 #pragma unroll
     for (int a = 0; a < C::TM; ++a) {
-        const int m = m0 + wm * (BM / 2) + a * 32 + li;
+        const int m = m0 + wm * (BM / WGM) + a * 32 + li;
         asv[a] = a_scale[m < M ? m : 0];   // rows past M are not stored
     }
 #pragma unroll
@@ -612,7 +613,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_dma_kernel(
                 *reinterpret_cast<float4 *>(slab + li * C::EP_ROW + 4 * col) = v;
             }
         __syncthreads();
-        const int mrow = m0 + wm * (BM / 2) + a * 32;
+        const int mrow = m0 + wm * (BM / WGM) + a * 32;
 #pragma unroll
         for (int it = 0; it < 32 / RPI; ++it) {
             const int rr = it * RPI + lane / LPR;
@@ -630,15 +631,15 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_dma_kernel(
     }
 }
 
-template <bool FP4, int BM, int BN, int NBUF>
+template <bool FP4, int BM, int BN, int NBUF, int WGM = 2, int WGN = 2>
 hipError_t launch_tile_dma(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w,
                            int64_t ldw, const uint8_t *ws, const uint16_t *bias, int epi,
                            uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                            hipStream_t st) {
-    auto kern = gemm_prefill_dma_kernel<FP4, BM, BN, NBUF>;
+    auto kern = gemm_prefill_dma_kernel<FP4, BM, BN, NBUF, WGM, WGN>;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), 0, st, a, lda, as, w, ldw, ws, bias,
-                       epi, y, ldy, (int)M, (int)N, (int)K, 8);
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(WGM * WGN * 64), 0, st, a, lda, as, w,
+                       ldw, ws, bias, epi, y, ldy, (int)M, (int)N, (int)K, 8);
     return hipGetLastError();
 }
 
@@ -671,7 +672,14 @@ hipError_t launch_gemm_prefill(bool fp4, const uint8_t *a, int64_t lda, const fl
         const double cost256 = (double)((t256 + num_cus - 1) / num_cus) * (1.0 * K + 930.0);
         const double cost128 = (double)((t128 + num_cus - 1) / num_cus) * (0.73 * K + 465.0);
         const double cost64 = (double)((t64 + num_cus - 1) / num_cus) * (0.415 * K + 236.0);
-        if (cost256 <= cost128 && cost256 <= cost64) BSG_PREFILL_DMA(256, 256);
+        if (cost256 <= cost128 && cost256 <= cost64) {
+            // MXFP4 weights: eight waves (4 x 2, each 64 x 128) measured
+            // faster than four for 256x256 tiles; e4m3 weights: four
+            if (fp4)
+                return launch_tile_dma<true, 256, 256, 4, 4, 2>(a, lda, a_scale, w, ldw, ws, bias,
+                                                                epi, y, ldy, M, N, K, st);
+            BSG_PREFILL_DMA(256, 256);
+        }
         if (cost128 <= cost64) BSG_PREFILL_DMA(256, 128);
         BSG_PREFILL_DMA(128, 128);
     }
