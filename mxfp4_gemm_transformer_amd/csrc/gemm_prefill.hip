@@ -387,7 +387,9 @@ struct DCfg {
     // epilogue staging: each wave's 32 x (32 TN) fp32 slab, rows padded by 16 bytes
     static constexpr int EP_ROW = TN * 32 * 4 + 16;
     static constexpr int EP_WAVE = 32 * EP_ROW;
-    static constexpr int LDS = NBUF * STAGE > NW * EP_WAVE ? NBUF * STAGE : NW * EP_WAVE;
+    static constexpr int EP_BIAS = NW * EP_WAVE;      // then each wave's TN*32 bias values
+    static constexpr int EP_ALL = EP_BIAS + NW * TN * 32 * 4;
+    static constexpr int LDS = NBUF * STAGE > EP_ALL ? NBUF * STAGE : EP_ALL;
     static_assert(A_STAGE % (16 * NT) == 0 && W_STAGE % (16 * NT) == 0, "stage split");
     static_assert(SC_ROWS <= NT, "one scale row per thread");
     static_assert(NBUF >= 4, "the ring needs NBUF - 1 >= 3 stages in flight");
@@ -577,20 +579,21 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     // ---- epilogue: every load has landed and every wave is done with the
     // ring. Each wave scales one 32-row slab of its tile by the per-token
     // scales (in the accumulator layout, where a lane holds one row), stages
-    // it in LDS as fp32, and reads it back with each lane on 4 fixed columns
-    // of a row, where it adds the bias, applies GELU, rounds to bf16 and
-    // writes whole 256-byte row segments.
+    // it in LDS as fp32, and reads it back as 4-column chunks in row-major
+    // order, adding the bias, applying GELU and rounding to bf16, so that
+    // consecutive lanes write consecutive 8-byte pieces of an output row.
     wait_loads_and_barrier<0>();
     uint8_t *slab = lds + wave * C::EP_WAVE;
-    constexpr int LPR = C::TN * 32 / 4;   // lanes per slab row in the store phase
-    constexpr int RPI = 64 / LPR;         // slab rows per store instruction
-    const int scol = 4 * (lane % LPR);    // this lane's first column in the wave's half
-    const int nst = n0 + wn * (BN / WGN) + scol;
-    float bst[4] = {0.f, 0.f, 0.f, 0.f};
-    if (epi != EPI_NONE) {   // uniform; columns past N read column 0 and are not stored
-        const int nn = nst < N ? nst : 0;
+    float *bias_w = reinterpret_cast<float *>(lds + C::EP_BIAS) + wave * C::TN * 32;
+    constexpr int WCOLS = C::TN * 32;               // the wave's columns
+    constexpr int CPR = WCOLS / 4;                  // 4-column chunks per slab row
+    const int ncol0 = n0 + wn * (BN / WGN);         // the wave's first column
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bst[j] = bf16_to_f32(bias[nn + j]);
+    for (int c = lane; c < WCOLS; c += 64) {        // bias of the wave's columns (0 past N)
+        const int n = ncol0 + c;
+        float bv = 0.f;
+        if ((epi != EPI_NONE) & (n < N)) bv = bf16_to_f32(bias[n]);
+        bias_w[c] = bv;
     }
     float asv[C::TM];
 #pragma unroll
@@ -615,16 +618,18 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         __syncthreads();
         const int mrow = m0 + wm * (BM / WGM) + a * 32;
 #pragma unroll
-        for (int it = 0; it < 32 / RPI; ++it) {
-            const int rr = it * RPI + lane / LPR;
-            const float4 v = *reinterpret_cast<const float4 *>(slab + rr * C::EP_ROW + 4 * scol);
-            const uint32_t h0 = f32_to_bf16(epilogue_rest(v.x, bst[0], epi));
-            const uint32_t h1 = f32_to_bf16(epilogue_rest(v.y, bst[1], epi));
-            const uint32_t h2 = f32_to_bf16(epilogue_rest(v.z, bst[2], epi));
-            const uint32_t h3 = f32_to_bf16(epilogue_rest(v.w, bst[3], epi));
-            const int m = mrow + rr;
-            if (m < M && nst < N)
-                *reinterpret_cast<uint2 *>(Y + (int64_t)m * ldy + nst) =
+        for (int it = 0; it < 32 * CPR / 64; ++it) {
+            const int ch = it * 64 + lane;
+            const int rr = ch / CPR, cc = 4 * (ch % CPR);
+            const float4 v = *reinterpret_cast<const float4 *>(slab + rr * C::EP_ROW + 4 * cc);
+            const float4 bv = *reinterpret_cast<const float4 *>(bias_w + cc);
+            const uint32_t h0 = f32_to_bf16(epilogue_rest(v.x, bv.x, epi));
+            const uint32_t h1 = f32_to_bf16(epilogue_rest(v.y, bv.y, epi));
+            const uint32_t h2 = f32_to_bf16(epilogue_rest(v.z, bv.z, epi));
+            const uint32_t h3 = f32_to_bf16(epilogue_rest(v.w, bv.w, epi));
+            const int m = mrow + rr, n = ncol0 + cc;
+            if (m < M && n < N)
+                *reinterpret_cast<uint2 *>(Y + (int64_t)m * ldy + n) =
                     make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
         }
         __syncthreads();
@@ -643,13 +648,106 @@ hipError_t launch_tile_dma(const uint8_t *a, int64_t lda, const float *as, const
     return hipGetLastError();
 }
 
+
+// ---- DMA-path planning. Workgroups run in rounds of one per CU; a round of
+// tiles of one shape costs c * K + e (in units of one k of a 256x256 tile),
+// c and e fitted to MI355X timings per tile shape: smaller tiles do less work
+// per round at a lower MFMA efficiency.
+struct TileShape {
+    int bm, bn;
+    double c, e;
+};
+constexpr TileShape SHAPES[] = {
+    {256, 256, 1.0, 930.0},
+    {256, 128, 0.73, 465.0},
+    {128, 128, 0.415, 236.0},
+};
+constexpr double LAUNCH_COST = 200.0;   // a second launch, same units
+
+double shape_cost(const TileShape &t, int64_t M, int64_t N, int64_t K, int num_cus) {
+    const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+    return (double)((tiles + num_cus - 1) / num_cus) * (t.c * (double)K + t.e);
+}
+
+int best_shape(bool fp4, int64_t M, int64_t N, int64_t K, int num_cus, double *cost) {
+    int best = -1;
+    for (int i = 0; i < (int)(sizeof(SHAPES) / sizeof(SHAPES[0])); ++i) {
+        const double c = shape_cost(SHAPES[i], M, N, K, num_cus);
+        if (best < 0 || c < *cost) { best = i; *cost = c; }
+    }
+    return best;
+}
+
+hipError_t launch_shape(int shape, bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
+                        const uint8_t *w, int64_t ldw, const uint8_t *ws, const uint16_t *bias,
+                        int epi, uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                        hipStream_t st) {
+    switch (shape) {
+    case 0:
+        // MXFP4 weights: eight waves (4 x 2, each 64 x 128) measured faster
+        // than four for 256x256 tiles; e4m3 weights: four
+        if (fp4)
+            return launch_tile_dma<true, 256, 256, 4, 4, 2>(a, lda, a_scale, w, ldw, ws, bias, epi,
+                                                            y, ldy, M, N, K, st);
+        return launch_tile_dma<false, 256, 256, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy,
+                                                   M, N, K, st);
+    case 1:
+        return fp4 ? launch_tile_dma<true, 256, 128, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y,
+                                                        ldy, M, N, K, st)
+                   : launch_tile_dma<false, 256, 128, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y,
+                                                         ldy, M, N, K, st);
+    default:
+        return fp4 ? launch_tile_dma<true, 128, 128, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y,
+                                                        ldy, M, N, K, st)
+                   : launch_tile_dma<false, 128, 128, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y,
+                                                         ldy, M, N, K, st);
+    }
+}
+
+// One launch of the cheapest tile shape, or two launches over column ranges
+// [0, N1) and [N1, N): 256x256 tiles in whole rounds over the first, the
+// cheapest shape over the rest (a last round that 256x256 tiles would leave
+// part idle can be filled by smaller tiles). The two write disjoint columns.
+hipError_t launch_prefill_dma(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
+                              const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                              const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
+                              int64_t N, int64_t K, int num_cus, hipStream_t st) {
+    double one_cost = 0.0;
+    const int one = best_shape(fp4, M, N, K, num_cus, &one_cost);
+    const int64_t mt = (M + 255) / 256, t256 = mt * ((N + 255) / 256);
+    const int64_t rounds = t256 / num_cus;
+    const int64_t nt1 = rounds > 0 ? rounds * num_cus / mt : 0;
+    const int64_t n1 = nt1 * 256;
+    if (n1 > 0 && n1 < N) {
+        const double c1 = shape_cost(SHAPES[0], M, n1, K, num_cus);
+        double c2 = 0.0;
+        const int two = best_shape(fp4, M, N - n1, K, num_cus, &c2);
+        if (c1 + c2 + LAUNCH_COST < one_cost) {
+            hipError_t e = launch_shape(0, fp4, a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M,
+                                        n1, K, st);
+            if (e != hipSuccess) return e;
+            const int64_t kb = K / 32;
+            const uint8_t *w2 = w + n1 * ldw;
+            const uint8_t *ws2 = ws + (fp4 ? n1 * kb : (n1 / 32) * kb);
+            const uint16_t *bias2 = bias ? bias + n1 : nullptr;
+            return launch_shape(two, fp4, a, lda, a_scale, w2, ldw, ws2, bias2, epi, y + n1, ldy, M,
+                                N - n1, K, st);
+        }
+    }
+    return launch_shape(one, fp4, a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, st);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_prefill(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
                                const uint8_t *w, int64_t ldw, const uint8_t *ws,
                                const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
                                int64_t N, int64_t K, int num_cus, hipStream_t st) {
-    // Largest tile that still gives every CU a tile.
+    if (K % 64 == 0)   // whole steps: LDS-mode staging
+        return launch_prefill_dma(fp4, a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K,
+                                  num_cus, st);
+    // K % 64 == 32: register-staged kernel; the largest tile that still
+    // gives every CU a tile
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
     const int64_t t128 = ((M + 255) / 256) * ((N + 127) / 128);
 #define BSG_PREFILL(BM_, BN_)                                                                      \
@@ -657,37 +755,10 @@ hipError_t launch_gemm_prefill(bool fp4, const uint8_t *a, int64_t lda, const fl
                                                    M, N, K, st)                                    \
                : launch_tile<false, BM_, BN_, 2, 2>(a, lda, a_scale, w, ldw, ws, bias, epi, y,     \
                                                     ldy, M, N, K, st)
-#define BSG_PREFILL_DMA(BM_, BN_)                                                              \
-    return fp4 ? launch_tile_dma<true, BM_, BN_, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, \
-                                                    M, N, K, st)                                    \
-               : launch_tile_dma<false, BM_, BN_, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y,     \
-                                                     ldy, M, N, K, st)
-    if (K % 64 == 0) {
-        // Tile size by a round-aware cost: workgroups run in rounds of one
-        // per CU, and a round costs c * K + e, where c is a tile's time per
-        // unit of K and e its fixed part (prologue, epilogue), both relative
-        // to a 256x256 tile, fitted to timings on MI355X: smaller tiles do
-        // less work per round but at a lower MFMA efficiency.
-        const int64_t t64 = ((M + 127) / 128) * ((N + 127) / 128);
-        const double cost256 = (double)((t256 + num_cus - 1) / num_cus) * (1.0 * K + 930.0);
-        const double cost128 = (double)((t128 + num_cus - 1) / num_cus) * (0.73 * K + 465.0);
-        const double cost64 = (double)((t64 + num_cus - 1) / num_cus) * (0.415 * K + 236.0);
-        if (cost256 <= cost128 && cost256 <= cost64) {
-            // MXFP4 weights: eight waves (4 x 2, each 64 x 128) measured
-            // faster than four for 256x256 tiles; e4m3 weights: four
-            if (fp4)
-                return launch_tile_dma<true, 256, 256, 4, 4, 2>(a, lda, a_scale, w, ldw, ws, bias,
-                                                                epi, y, ldy, M, N, K, st);
-            BSG_PREFILL_DMA(256, 256);
-        }
-        if (cost128 <= cost64) BSG_PREFILL_DMA(256, 128);
-        BSG_PREFILL_DMA(128, 128);
-    }
     if (t256 >= num_cus) BSG_PREFILL(256, 256);
     if (t128 >= num_cus) BSG_PREFILL(256, 128);
     BSG_PREFILL(128, 128);
 #undef BSG_PREFILL
-#undef BSG_PREFILL_DMA
 }
 
 }  // namespace bsg
