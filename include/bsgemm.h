@@ -94,8 +94,9 @@ int fp8_quant_rows(const void *x_bf16, int64_t ld_x, void *q_e4m3, int64_t ld_q,
  *   bias     [N] bf16, required iff epilogue != BS_EPI_NONE, else ignored
  *   y_bf16   [M, N] bf16 out, row stride ld_y elements
  *   M >= 1; N, K >= 32 and multiples of 32; ld_a, ld_w <= BS_MAX_LD_BYTES.
- *   workspace / workspace_bytes: scratch the call may use, at least
- *   bs_workspace_bytes(0, M, N, K) bytes (may be NULL when that is 0).
+ *   workspace / workspace_bytes: scratch the call uses, at least
+ *   bs_workspace_bytes(0, M, N, K) bytes, 16-byte aligned (may be NULL when
+ *   that is 0); BS_EWORKSPACE if too small, BS_EALIGN if misaligned.
  */
 int gemm_bs_fp8(const void *a_e4m3, int64_t ld_a, const float *a_scale,
                 const void *w_e4m3, int64_t ld_w, const uint8_t *w_scale,
@@ -121,7 +122,12 @@ int gemm_mxfp4_w4a8(const void *a_e4m3, int64_t ld_a, const float *a_scale,
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Scratch bytes gemm_bs_fp8 (op 0) or gemm_mxfp4_w4a8 (op 1) needs for this
- * shape; 0 means none. */
+ * shape; 0 means none. Nonzero for 8 < M <= 64, where K is split across
+ * workgroups and fp32 partial sums [S][M][N] go through the workspace
+ * (S depends only on N and K). The workspace must then be 16-byte aligned;
+ * its contents on entry do not matter (every byte read is written first by
+ * the same call), so one buffer serves every call of a shape. Calls that
+ * share a workspace must not overlap in time. */
 size_t bs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
 
 /* A static, human-readable string for a bs_status value. */

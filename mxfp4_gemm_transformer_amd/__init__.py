@@ -164,7 +164,7 @@ def _gemm(fn_name, op, a, a_scale, w, w_scale, bias, epilogue, y, workspace, str
     ldy = _matrix(y, "y", M, N)
     need = bs_workspace_bytes(op, M, N, K)
     if need and workspace is None:
-        workspace = torch.zeros((need,), dtype=torch.uint8, device=a.device)
+        workspace = torch.empty((need,), dtype=torch.uint8, device=a.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     fn = getattr(load_library(), fn_name)
     st = fn(_ptr(a), lda, _ptr(a_scale), _ptr(w), ldw, _ptr(w_scale),

@@ -14,10 +14,14 @@ hipError_t launch_quant_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_
 // M <= DECODE_MAX_M: the bandwidth-bound small-M GEMM.
 constexpr int64_t DECODE_MAX_M = 64;
 
+// `workspace` holds decode_workspace_bytes(M, N, K) bytes (fp32 partial sums
+// of the split-K path, 8 < M <= 64), 4-byte aligned; unused otherwise.
 hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
                               const uint8_t *w, int64_t ldw, const uint8_t *ws,
                               const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
-                              int64_t N, int64_t K, int num_cus, hipStream_t stream);
+                              int64_t N, int64_t K, void *workspace, int num_cus,
+                              hipStream_t stream);
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_gemm_prefill(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
                                const uint8_t *w, int64_t ldw, const uint8_t *ws,

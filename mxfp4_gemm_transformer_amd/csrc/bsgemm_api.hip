@@ -65,12 +65,13 @@ int gemm_common(bool fp4, const void *a_e4m3, int64_t ld_a, const float *a_scale
                 int64_t ld_w, const uint8_t *w_scale, const void *bias_bf16, int epilogue,
                 void *y_bf16, int64_t ld_y, int64_t M, int64_t N, int64_t K, void *workspace,
                 size_t workspace_bytes, void *stream) {
-    (void)workspace;
     const int64_t w_row = fp4 ? K / 2 : K;
+    const size_t ws_need = bs_workspace_bytes(fp4 ? 1 : 0, M, N, K);
     int st = check_gemm(a_e4m3, ld_a, a_scale, w, ld_w, w_row, w_scale, bias_bf16, epilogue,
-                        y_bf16, ld_y, M, N, K, workspace_bytes,
-                        bs_workspace_bytes(fp4 ? 1 : 0, M, N, K));
+                        y_bf16, ld_y, M, N, K, workspace_bytes, ws_need);
     if (st != BS_OK) return st;
+    if (ws_need && (!workspace || !aligned16(workspace)))
+        return workspace ? BS_EALIGN : BS_EWORKSPACE;
     int num_cus = 0;
     if ((st = device_check(&num_cus)) != BS_OK) return st;
     const auto *a = static_cast<const uint8_t *>(a_e4m3);
@@ -81,7 +82,7 @@ int gemm_common(bool fp4, const void *a_e4m3, int64_t ld_a, const float *a_scale
     hipError_t e;
     if (M <= bsg::DECODE_MAX_M)
         e = bsg::launch_gemm_decode(fp4, a, ld_a, a_scale, wb, ld_w, w_scale, bias, epilogue, y,
-                                    ld_y, M, N, K, num_cus, s);
+                                    ld_y, M, N, K, workspace, num_cus, s);
     else
         e = bsg::launch_gemm_prefill(fp4, a, ld_a, a_scale, wb, ld_w, w_scale, bias, epilogue, y,
                                      ld_y, M, N, K, num_cus, s);
@@ -126,8 +127,9 @@ int gemm_mxfp4_w4a8(const void *a_e4m3, int64_t ld_a, const float *a_scale, cons
 }
 
 size_t bs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
-    (void)op; (void)M; (void)N; (void)K;
-    return 0;  // every kernel reduces within a workgroup
+    (void)op;
+    if (M < 1 || N < 1 || K < 1) return 0;
+    return bsg::decode_workspace_bytes(M, N, K);   // split-K decode partial sums, else 0
 }
 
 const char *bs_status_string(int status) {

@@ -7,8 +7,11 @@
 // layout below); its waves split K between them, each issuing every load of
 // its share before the first MFMA so that the whole share is in flight at
 // once. The waves' partial tiles meet in LDS, in a fixed order, and the
-// bias / GELU epilogue writes bf16. No workspace, no inter-workgroup
-// synchronisation.
+// bias / GELU epilogue writes bf16. Two more shapes of the same idea follow:
+// for wide layers, one workgroup per CU with (row group, K step) units dealt
+// evenly to its waves; for 8 < M <= 64 on narrow layers, K split across
+// workgroups with fp32 partial sums in the caller's workspace, added in a
+// fixed order by a second kernel. No inter-workgroup synchronisation.
 //
 // The MFMA is V_MFMA_SCALE_F32_16X16X128_F8F6F4: tokens on the A side
 // (padded with zeros to 16), weight rows on the B side, the weights' E8M0
@@ -428,12 +431,182 @@ void launch_units(const uint8_t *a, int64_t lda, const float *as, const uint8_t 
                        w, ldw, ws, bias, epi, y, ldy, (int)M, (int)N, (int)K, gpw);
 }
 
+
+// ---------------------------------------------------------------------------
+// Split-K decode for 8 < M <= 64 on narrow layers. With every workgroup on
+// all of K, each one would read all M x K activations (M/8 times the bytes
+// of its 8-row weight slice at M = 64); here a workgroup takes 64 weight
+// rows and a 1/S slice of K, with the activations' slice staged once in LDS,
+// so activations and weights cost about the same. Partial sums go to the
+// caller's workspace as fp32 [S][M][N]; a second kernel adds the S slices
+// in order and applies the epilogue.
+constexpr int SPLIT_MAX_STEPS = 8;   // 128-k steps per split at most
+
+// Splits of K: enough workgroups to cover the CUs for a 256-CU part, and at
+// most SPLIT_MAX_STEPS steps of 128 k each.
+__host__ __device__ inline int64_t decode_splits(int64_t N, int64_t K) {
+    const int64_t steps = (K + 127) / 128, blocks = (N + 63) / 64;
+    int64_t s = blocks >= 256 ? 1 : 256 / blocks;
+    const int64_t min_s = (steps + SPLIT_MAX_STEPS - 1) / SPLIT_MAX_STEPS;
+    if (s < min_s) s = min_s;
+    if (s > steps) s = steps;
+    return s;
+}
+
+template <bool FP4, int MT>
+__global__ __launch_bounds__(256) void gemm_decode_splitk_kernel(
+    const uint8_t *__restrict__ A, int64_t lda, const uint8_t *__restrict__ W, int64_t ldw,
+    const uint8_t *__restrict__ WS, float *__restrict__ part, int M, int N, int K, int S) {
+    extern __shared__ __align__(16) uint8_t lds[];   // [16 MT][span + 16] activations
+    constexpr int TOK = 16 * MT;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i = lane & 15, g = lane >> 4;
+    const int KB = K >> 5;
+    const int steps = (K + 127) / 128;
+    const int per = (steps + S - 1) / S;
+    const int sp = blockIdx.y;
+    const int st0 = min(steps, sp * per), st1 = min(steps, st0 + per);
+    const int kbeg = st0 * 128;
+    const int span = per * 128;                       // bytes of k per token staged
+    const int lds_row = span + 16;
+    const int row0 = blockIdx.x * 64;
+    const int n = row0 + 16 * wave + i;               // this lane's weight row
+
+    // ---- activations' K slice: registers first, weights next, then LDS
+    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(A, (int64_t)M * lda);
+    constexpr int ACH = TOK * SPLIT_MAX_STEPS * 128 / 16 / 256;   // 16-byte chunks per thread
+    const int kc = span >> 4, chunks = TOK * kc;
+    uint4 av[ACH];
+#pragma unroll
+    for (int j = 0; j < ACH; ++j) {
+        const int c = threadIdx.x + j * 256;
+        const int t = c / kc, k = kbeg + 16 * (c % kc);
+        av[j] = bload16(rsA, ((c < chunks) & (t < M) & (k < K)) ? (uint32_t)(t * lda + k) : OOB_OFF);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- this wave's weights: SPLIT_MAX_STEPS steps (16x16x128 B operand)
+    const __amdgpu_buffer_rsrc_t rsW = make_rsrc(W + (int64_t)row0 * ldw, (int64_t)(N - row0) * ldw);
+    const __amdgpu_buffer_rsrc_t rsS =
+        FP4 ? make_rsrc(WS + (int64_t)row0 * KB, (int64_t)(N - row0) * KB)
+            : make_rsrc(WS + (int64_t)(row0 >> 5) * KB, (int64_t)((N >> 5) - (row0 >> 5)) * KB);
+    const uint32_t wrow = (uint32_t)((16 * wave + i) * ldw);
+    const uint32_t srow = (uint32_t)((FP4 ? (16 * wave + i) : ((n >> 5) - (row0 >> 5))) * KB);
+    uint4 wlo[SPLIT_MAX_STEPS], whi[FP4 ? 1 : SPLIT_MAX_STEPS];
+    uint32_t wsc[SPLIT_MAX_STEPS];
+#pragma unroll
+    for (int u = 0; u < SPLIT_MAX_STEPS; ++u) {
+        const int kk = (st0 + u) * 128;
+        const bool on = (st0 + u < st1) & (n < N);
+        const int kblk = kk + 32 * g, klo = kk + 16 * g, khi = kk + 64 + 16 * g;
+        if (FP4) {
+            wlo[u] = bload16(rsW, (on & (kblk < K)) ? wrow + (kblk >> 1) : OOB_OFF);
+        } else {
+            wlo[u] = bload16(rsW, (on & (klo < K)) ? wrow + klo : OOB_OFF);
+            whi[u] = bload16(rsW, (on & (khi < K)) ? wrow + khi : OOB_OFF);
+        }
+        wsc[u] = __builtin_amdgcn_raw_buffer_load_b8(rsS, (on & (kblk < K)) ? srow + (kblk >> 5) : OOB_OFF,
+                                                     0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int j = 0; j < ACH; ++j) {
+        const int c = threadIdx.x + j * 256;
+        const int t = c / kc, k = 16 * (c % kc);
+        if (c < chunks) *reinterpret_cast<uint4 *>(lds + t * lds_row + k) = av[j];
+    }
+    __syncthreads();
+
+    v4f acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < SPLIT_MAX_STEPS; ++u) {
+        if (st0 + u < st1) {   // uniform
+            const int kl = u * 128;                       // offset in the staged slice
+            const v8i wv = pack8(wlo[u], FP4 ? make_uint4(0u, 0u, 0u, 0u) : whi[FP4 ? 0 : u]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const uint8_t *arow = lds + (mt * 16 + i) * lds_row + kl;
+                const v8i a8 = pack8(*reinterpret_cast<const uint4 *>(arow + 16 * g),
+                                     *reinterpret_cast<const uint4 *>(arow + 64 + 16 * g));
+                acc[mt] = mfma16<FP4>(a8, wv, acc[mt], E8M0_ONE, (int)wsc[u]);
+            }
+        }
+    }
+    // D: lane l = i + 16 g, VGPR v -> token 16 mt + 4 g + v, weight row n
+    if (n < N) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = mt * 16 + 4 * g + v;
+                if (t < M) part[((int64_t)sp * M + t) * N + n] = acc[mt][v];
+            }
+    }
+}
+
+// Y[m, n] = epilogue(sum over the S slices in order (fp32), a_scale[m], bias[n]);
+// four columns per thread, eight slices' loads in flight before their adds.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part,
+                                                            const float *__restrict__ a_scale,
+                                                            const uint16_t *__restrict__ bias,
+                                                            int epi, uint16_t *__restrict__ Y,
+                                                            int64_t ldy, int M, int N, int S) {
+    const int n4 = N >> 2;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)M * n4) return;
+    const int t = (int)(idx / n4), c0 = 4 * (int)(idx % n4);
+    const int64_t slice = (int64_t)M * N;
+    const float *p = part + (int64_t)t * N + c0;
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4 *>(p + (s + u) * slice);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) { sum.x += v[u].x; sum.y += v[u].y; sum.z += v[u].z; sum.w += v[u].w; }
+    }
+    for (; s < S; ++s) {
+        const float4 v = *reinterpret_cast<const float4 *>(p + s * slice);
+        sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+    }
+    float4 bq = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (epi != EPI_NONE)   // bias is only 2-byte aligned
+        bq = make_float4(bf16_to_f32(bias[c0]), bf16_to_f32(bias[c0 + 1]),
+                         bf16_to_f32(bias[c0 + 2]), bf16_to_f32(bias[c0 + 3]));
+    const float as = a_scale[t];
+    const uint32_t o0 = f32_to_bf16(epilogue(sum.x, as, bq.x, epi));
+    const uint32_t o1 = f32_to_bf16(epilogue(sum.y, as, bq.y, epi));
+    const uint32_t o2 = f32_to_bf16(epilogue(sum.z, as, bq.z, epi));
+    const uint32_t o3 = f32_to_bf16(epilogue(sum.w, as, bq.w, epi));
+    *reinterpret_cast<uint2 *>(Y + (int64_t)t * ldy + c0) = make_uint2(o0 | (o1 << 16), o2 | (o3 << 16));
+}
+
+template <bool FP4, int MT>
+hipError_t launch_splitk(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w,
+                         int64_t ldw, const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y,
+                         int64_t ldy, int64_t M, int64_t N, int64_t K, float *part,
+                         hipStream_t st) {
+    const int64_t S = decode_splits(N, K);
+    const int64_t steps = (K + 127) / 128, per = (steps + S - 1) / S;
+    const size_t lds = (size_t)16 * MT * (per * 128 + 16);
+    hipLaunchKernelGGL((gemm_decode_splitk_kernel<FP4, MT>), dim3((unsigned)((N + 63) / 64), (unsigned)S),
+                       dim3(256), lds, st, a, lda, w, ldw, ws, part, (int)M, (int)N, (int)K, (int)S);
+    const int64_t quads = M * N / 4;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st,
+                       part, as, bias, epi, y, ldy, (int)M, (int)N, (int)S);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
                               const uint8_t *w, int64_t ldw, const uint8_t *ws,
                               const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
-                              int64_t N, int64_t K, int num_cus, hipStream_t st) {
+                              int64_t N, int64_t K, void *workspace, int num_cus, hipStream_t st) {
     constexpr int NW = 8;
     // Balanced units kernel for wide layers (at least two 8-row groups per
     // CU; below that the split-K kernel, which reads its activations straight
@@ -473,23 +646,23 @@ hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const flo
             launch_spw<false, true, 1>(per, a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, st);
         return hipGetLastError();
     }
-    const int mt = (int)((M + 15) / 16);
-    const int per = (int)(((K + 127) / 128 + NW - 1) / NW);
-#define BSG_DECODE_MT(MT)                                                                          \
-    if (fp4)                                                                                       \
-        launch_spw<true, false, MT>(per, a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K,  \
-                                    st);                                                           \
-    else                                                                                           \
-        launch_spw<false, false, MT>(per, a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, \
-                                     st);
-    switch (mt) {
-    case 1: BSG_DECODE_MT(1) break;
-    case 2: BSG_DECODE_MT(2) break;
-    case 3: BSG_DECODE_MT(3) break;
-    default: BSG_DECODE_MT(4) break;
+    // 8 < M <= 64: split K over workgroups, partial sums in the workspace
+    float *part = static_cast<float *>(workspace);
+    switch ((M + 15) / 16) {
+    case 1: return fp4 ? launch_splitk<true, 1>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st)
+                       : launch_splitk<false, 1>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st);
+    case 2: return fp4 ? launch_splitk<true, 2>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st)
+                       : launch_splitk<false, 2>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st);
+    case 3: return fp4 ? launch_splitk<true, 3>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st)
+                       : launch_splitk<false, 3>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st);
+    default: return fp4 ? launch_splitk<true, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st)
+                        : launch_splitk<false, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st);
     }
-#undef BSG_DECODE_MT
-    return hipGetLastError();
+}
+
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 8 || M > DECODE_MAX_M) return 0;
+    return (size_t)decode_splits(N, K) * (size_t)M * (size_t)N * sizeof(float);
 }
 
 }  // namespace bsg

@@ -56,6 +56,15 @@ def test_decode_wide_rows(fmt, M, K):
     _full_check(fmt, M, N, K, epi, seed=M + K)
 
 
+# split-K (8 < M <= 64, narrow layers): K cut into S slices of whole 128-k
+# steps; (2048, 1152) leaves the last three slices empty, (2080, 1184) adds
+# a half-full last column block and a 32-wide K tail
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("M,N,K", [(40, 2048, 1152), (12, 2080, 1184), (64, 512, 4096)])
+def test_decode_split_k(fmt, M, N, K):
+    _full_check(fmt, M, N, K, synth.EPI_BIAS_GELU_TANH if M == 12 else synth.EPI_BIAS, seed=M + K)
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
 @pytest.mark.parametrize("K", [32, 96, 128, 160, 256, 288, 2080])
 def test_decode_k_tails(fmt, K):

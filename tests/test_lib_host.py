@@ -39,6 +39,11 @@ def test_status_strings_and_workspace():
     assert bs.bs_status_string(7) == "unknown status"
     assert bs.bs_workspace_bytes(0, 8, 2048, 7168) == 0
     assert bs.bs_workspace_bytes(1, 4096, 34816, 5120) == 0
+    # split-K decode (8 < M <= 64): S fp32 partial sums [S][M][N], S from N and K
+    assert bs.bs_workspace_bytes(0, 64, 2048, 7168) == 8 * 64 * 2048 * 4
+    assert bs.bs_workspace_bytes(1, 16, 2048, 7168) == 8 * 16 * 2048 * 4
+    assert bs.bs_workspace_bytes(0, 9, 32, 32) == 1 * 9 * 32 * 4
+    assert bs.bs_workspace_bytes(0, 65, 2048, 7168) == 0
 
 
 def _gemm(fn, a=FAKE, lda=64, s=FAKE, w=FAKE, ldw=64, ws=FAKE, bias=None, epi=0, y=FAKE, ldy=64,
@@ -78,6 +83,14 @@ def test_gemm_argument_checks(name):
     assert _gemm(fn, ldy=68) == A
     assert _gemm(fn, s=ctypes.c_void_p(0x10002)) == A
     assert _gemm(fn, bias=ctypes.c_void_p(0x10001), epi=1) == A
+    # 8 < M <= 64 needs the split-K workspace: too small, missing, misaligned
+    need = bs.bs_workspace_bytes(0 if name == "gemm_bs_fp8" else 1, 16, 64, 64)
+    assert need > 0
+    W = bs.BS_EWORKSPACE
+    assert _gemm(fn, M=16) == W
+    assert _gemm(fn, M=16, work=FAKE, work_bytes=need - 4) == W
+    assert _gemm(fn, M=16, work=None, work_bytes=need) == W
+    assert _gemm(fn, M=16, work=ctypes.c_void_p(0x10008), work_bytes=need) == A
 
 
 def test_quant_argument_checks():
