@@ -42,7 +42,11 @@ def parse():
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", default="decode",
-                   choices=["tiny", "decode", "prefill", "ffn_up", "ffn_up_bias", "gate_up"])
+                   choices=["tiny", "decode", "prefill", "ffn_up", "ffn_up_bias", "gate_up",
+                            "add_rms", "silu_mul"],
+                   help="a GEMM workload (quantize + GEMM per step), or a fused producer "
+                        "(add_rms: residual add + RMSNorm + quantize on [M, 5120]; silu_mul: "
+                        "SiLU(gate) * up + quantize on [M, 2 x 17408])")
     p.add_argument("--m", type=int, default=None, help="token count (M) for sweep workloads")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU oracle budget for the cpu_baseline leg (0 disables it)")
@@ -113,6 +117,10 @@ def main():
     import torch
     import mxfp4_gemm_transformer_amd as bs
     import synth
+
+    if args.workload in synth.PRODUCERS:
+        bench_producer(args)
+        return
 
     wl = synth.WORKLOADS[args.workload]
     M = args.m if args.m is not None else wl.M
@@ -273,6 +281,114 @@ def cpu_baseline(d, wl, M, alg, compute_bound, budget_s):
     return {"value": round(value, 4), "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "%d of %d token rows (all %d outputs each), %d passes of quantize + GEMM + "
                       "epilogue in %.1f s" % (rows, M, wl.N, runs, t_total),
+            "cpu_model": _cpu_model()}
+
+
+def producer_bytes(name, M, width):
+    """HBM bytes a fused producer must move: bf16 inputs read, the new
+    residual written (add_rms), codes and scales written."""
+    if name == "add_rms":
+        return 2 * M * width * 3 + 2 * width + M * width + 4 * M
+    return 2 * M * 2 * width + M * width + 4 * M
+
+
+def bench_producer(args):
+    """One step = one fused producer call (add_rms_norm_quant_fp8 or
+    silu_mul_quant_fp8) over [M, width] rows; input copies rotate over
+    >= 512 MiB so each step reads its rows from HBM."""
+    import torch
+    import mxfp4_gemm_transformer_amd as bs
+    import synth
+
+    name = args.workload
+    width, sweep = synth.PRODUCERS[name]
+    M = args.m if args.m is not None else 16
+    steps = args.steps if args.steps is not None else (100 if M >= 512 else 1000)
+    warmup = args.warmup if args.warmup is not None else 20
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = synth.producer_inputs(name, M)
+    to_dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)) \
+        .view(torch.bfloat16).to(dev)
+    if name == "add_rms":
+        per_copy = 2 * d["x"].nbytes
+        copies = max(2, math.ceil(ROTATION_BYTES / per_copy))
+        xs = [to_dev(d["x"]) for _ in range(copies)]
+        rs = [to_dev(d["residual"]) for _ in range(copies)]
+        w = to_dev(d["weight"])
+        call = lambda i: bs.add_rms_norm_quant_fp8(xs[i % copies], rs[i % copies], w, d["eps"],
+                                                   q=q, scale=s)
+        kernel = "add_rms_norm_quant_fp8"
+    else:
+        per_copy = d["gate_up"].nbytes
+        copies = max(2, math.ceil(ROTATION_BYTES / per_copy))
+        gus = [to_dev(d["gate_up"]) for _ in range(copies)]
+        call = lambda i: bs.silu_mul_quant_fp8(gus[i % copies], q=q, scale=s)
+        kernel = "silu_mul_quant_fp8"
+    q = torch.empty((M, width), dtype=torch.uint8, device=dev)
+    s = torch.empty((M,), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            call(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    step_s = e0.elapsed_time(e1) * 1e-3 / steps
+    nbytes = producer_bytes(name, M, width)
+    gbs = nbytes / step_s / 1e9
+    result = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(step_s * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 -> fp8_e4m3", "data": "synthetic",
+        "config": {"workload": "%s M=%d width=%d (fused %s + per-token e4m3 quantization)" % (
+            name, M, width, "residual add + RMSNorm" if name == "add_rms" else "SiLU(gate) * up"),
+            "M": M, "width": width, "input_copies_rotated": copies, "step": kernel,
+            "graph_replay": True},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": kernel, "avg_launch_us": round(step_s * 1e6, 3),
+                     "algorithmic_bytes_per_launch": nbytes},
+        "kernels_us": {kernel: round(step_s * 1e6, 3)},
+        "step_bytes": nbytes, "wall_s_timed_region": round(wall_s, 6),
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_producer(name, d, M, width, nbytes, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+def cpu_baseline_producer(name, d, M, width, nbytes, budget_s):
+    """The oracle's fused producer on a bounded sample of the rows."""
+    import oracle
+    oracle.build()
+    rows = max(1, min(M, int(2e7 / width)))
+    runs, t_total = 0, 0.0
+    while t_total < budget_s or runs == 0:
+        t0 = time.perf_counter()
+        if name == "add_rms":
+            oracle.add_rms_norm_quant(d["x"][:rows], d["residual"][:rows], d["weight"], d["eps"])
+        else:
+            oracle.silu_mul_quant(d["gate_up"][:rows])
+        t_total += time.perf_counter() - t0
+        runs += 1
+        if t_total > 3 * budget_s:
+            break
+    value = nbytes * rows / M * runs / t_total / 1e9
+    return {"value": round(value, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": "%d of %d rows, %d passes in %.1f s" % (rows, M, runs, t_total),
             "cpu_model": _cpu_model()}
 
 

@@ -7,6 +7,9 @@
  *                       e4m3fn with one E8M0 scale per 32x32 block
  *   3. gemm_mxfp4_w4a8  the same with MXFP4 weights (fp4 e2m1, one E8M0 scale
  *                       per row per 32 along K)
+ *   4. add_rms_norm_quant_fp8, silu_mul_quant_fp8
+ *                       fused producers: RMSNorm (with an optional residual
+ *                       add) or SiLU(gate) * up, then step 1, in one kernel
  *
  * Sources (web pages bundled as the reference):
  *   - formats and scale grids: vLLM DeepSeek-V4 AMD mono runner page,
@@ -81,6 +84,49 @@ enum bs_epilogue {
  */
 int fp8_quant_rows(const void *x_bf16, int64_t ld_x, void *q_e4m3, int64_t ld_q,
                    float *scale, int64_t M, int64_t K, void *stream);
+
+/*
+ * Fused producers: the row that feeds the quantizer is computed in the same
+ * kernel, and the result is the "(q_fp8, scale)" pair of fp8_quant_rows
+ * applied to that bf16 row (sly-radiance README, fused norm/quant rows of
+ * its file table: add_rms_quant and silu_mul_quant hand (q_fp8, scale) to
+ * the W4A8 GEMM; the norm and activation formulas are the cortiq dit.rs
+ * page's rms_norm, silu and SwiGLU loop).
+ *
+ * add_rms_norm_quant_fp8, per row m (bf16 in, fp64 / fp32 as stated):
+ *     r[k]  = bf16(x[m,k] + residual[m,k])     nearest-even; r = x when
+ *             residual is NULL; otherwise r is written back into residual
+ *     ms    = (sum_k r[k]^2) / K                fp64
+ *     inv   = 1 / sqrt(ms + eps)                fp64
+ *     h[k]  = bf16(fl32(fl32(r[k] * inv) * weight[k]))
+ *     q[m,:], scale[m] = fp8_quant_rows of the row h
+ *   x_bf16       [M, K] bf16, row stride ld_x elements
+ *   residual     [M, K] bf16 in/out (updated in place), row stride ld_r
+ *                elements, or NULL; must not overlap x, weight, q or scale
+ *   weight_bf16  [K] bf16 norm weight
+ *   eps          >= 0, finite
+ *   q_e4m3, ld_q, scale: as fp8_quant_rows.
+ *
+ * silu_mul_quant_fp8, per row m:
+ *     g = gate_up[m, k], u = gate_up[m, I + k]  (gate first, then up)
+ *     a[k]  = bf16(fl32(fl32(g / (1 + exp(-g))) * u))   silu in fp64
+ *     q[m,:], scale[m] = fp8_quant_rows of the row a
+ *   gate_up_bf16 [M, 2I] bf16, row stride ld_gu elements (ld_gu >= 2I)
+ *   q_e4m3 [M, I], scale [M] as fp8_quant_rows.
+ *
+ * Both: M >= 1; K (or I) >= 32, a multiple of 32 and at most 32768; the
+ * alignment rules of fp8_quant_rows for every bf16 row stride. The sums of
+ * squares are taken in fp64 in a different order than written above; the
+ * rounding decisions that follow are the written ones unless a value lies
+ * within about 1e-16 (relative) of a rounding boundary. NaN/Inf inputs are
+ * not supported.
+ */
+int add_rms_norm_quant_fp8(const void *x_bf16, int64_t ld_x, void *residual_bf16, int64_t ld_r,
+                           const void *weight_bf16, double eps, void *q_e4m3, int64_t ld_q,
+                           float *scale, int64_t M, int64_t K, void *stream);
+
+int silu_mul_quant_fp8(const void *gate_up_bf16, int64_t ld_gu, void *q_e4m3, int64_t ld_q,
+                       float *scale, int64_t M, int64_t I, void *stream);
 
 /*
  * Block-scaled e4m3 GEMM (y = x W^T form):

@@ -19,7 +19,8 @@ import os
 
 import torch
 
-__all__ = ["fp8_quant_rows", "gemm_bs_fp8", "gemm_mxfp4_w4a8", "bs_workspace_bytes",
+__all__ = ["fp8_quant_rows", "add_rms_norm_quant_fp8", "silu_mul_quant_fp8",
+           "gemm_bs_fp8", "gemm_mxfp4_w4a8", "bs_workspace_bytes",
            "bs_status_string", "BsError", "EPI_NONE", "EPI_BIAS", "EPI_BIAS_GELU_TANH",
            "weight_shape", "w_scale_shape", "library_path", "load_library",
            "EXPORTED_SYMBOLS"]
@@ -27,8 +28,8 @@ __all__ = ["fp8_quant_rows", "gemm_bs_fp8", "gemm_mxfp4_w4a8", "bs_workspace_byt
 EPI_NONE, EPI_BIAS, EPI_BIAS_GELU_TANH = 0, 1, 2
 BS_OK, BS_EINVAL, BS_EALIGN, BS_EARCH, BS_EWORKSPACE, BS_ELAUNCH = 0, -1, -2, -3, -4, -5
 
-EXPORTED_SYMBOLS = ("fp8_quant_rows", "gemm_bs_fp8", "gemm_mxfp4_w4a8", "bs_workspace_bytes",
-                    "bs_status_string")
+EXPORTED_SYMBOLS = ("fp8_quant_rows", "add_rms_norm_quant_fp8", "silu_mul_quant_fp8",
+                    "gemm_bs_fp8", "gemm_mxfp4_w4a8", "bs_workspace_bytes", "bs_status_string")
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsgemm.so")
 _lib = None
@@ -55,6 +56,11 @@ def load_library():
         i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         lib.fp8_quant_rows.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp]
         lib.fp8_quant_rows.restype = i32
+        lib.add_rms_norm_quant_fp8.argtypes = [vp, i64, vp, i64, vp, ctypes.c_double, vp, i64, vp,
+                                               i64, i64, vp]
+        lib.add_rms_norm_quant_fp8.restype = i32
+        lib.silu_mul_quant_fp8.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp]
+        lib.silu_mul_quant_fp8.restype = i32
         gemm = [vp, i64, vp, vp, i64, vp, vp, i32, vp, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
         lib.gemm_bs_fp8.argtypes = gemm
         lib.gemm_bs_fp8.restype = i32
@@ -124,6 +130,63 @@ def fp8_quant_rows(x: torch.Tensor, q: torch.Tensor | None = None,
                                        ctypes.c_void_p(_stream(stream)))
     if st != BS_OK:
         raise BsError(st, "fp8_quant_rows")
+    return q, scale
+
+
+def _quant_outputs(q, scale, M, K, device):
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=device)
+    q = _u8(q, "q")
+    ldq = _matrix(q, "q", M, K)
+    if scale is None:
+        scale = torch.empty((M,), dtype=torch.float32, device=device)
+    if scale.dtype != torch.float32 or scale.shape != (M,) or not scale.is_contiguous():
+        raise ValueError("scale must be a contiguous fp32 [M] tensor")
+    return q, ldq, scale
+
+
+def add_rms_norm_quant_fp8(x: torch.Tensor, residual: torch.Tensor | None, weight: torch.Tensor,
+                           eps: float, q: torch.Tensor | None = None,
+                           scale: torch.Tensor | None = None, stream=None):
+    """RMSNorm of x (+ residual, which is updated in place to the bf16 sum)
+    with the bf16 weight [K], then per-token e4m3 quantization. Returns
+    (q uint8 [M, K], scale fp32 [M])."""
+    if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("x and weight must be bfloat16")
+    M, K = x.shape
+    ldx = _matrix(x, "x", M, K)
+    ldr = 0
+    if residual is not None:
+        if residual.dtype != torch.bfloat16:
+            raise TypeError("residual must be bfloat16")
+        ldr = _matrix(residual, "residual", M, K)
+    if weight.shape != (K,) or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous bf16 [K] tensor")
+    q, ldq, scale = _quant_outputs(q, scale, M, K, x.device)
+    st = load_library().add_rms_norm_quant_fp8(_ptr(x), ldx, _ptr(residual), ldr, _ptr(weight),
+                                               float(eps), _ptr(q), ldq, _ptr(scale), M, K,
+                                               ctypes.c_void_p(_stream(stream)))
+    if st != BS_OK:
+        raise BsError(st, "add_rms_norm_quant_fp8")
+    return q, scale
+
+
+def silu_mul_quant_fp8(gate_up: torch.Tensor, q: torch.Tensor | None = None,
+                       scale: torch.Tensor | None = None, stream=None):
+    """SiLU(gate) * up of gate_up [M, 2I] (gate first), then per-token e4m3
+    quantization. Returns (q uint8 [M, I], scale fp32 [M])."""
+    if gate_up.dtype != torch.bfloat16:
+        raise TypeError("gate_up must be bfloat16")
+    M, I2 = gate_up.shape
+    if I2 % 2:
+        raise ValueError("gate_up must have an even number of columns")
+    I = I2 // 2
+    ldgu = _matrix(gate_up, "gate_up", M, I2)
+    q, ldq, scale = _quant_outputs(q, scale, M, I, gate_up.device)
+    st = load_library().silu_mul_quant_fp8(_ptr(gate_up), ldgu, _ptr(q), ldq, _ptr(scale), M, I,
+                                           ctypes.c_void_p(_stream(stream)))
+    if st != BS_OK:
+        raise BsError(st, "silu_mul_quant_fp8")
     return q, scale
 
 

@@ -11,11 +11,20 @@ namespace bsg {
 hipError_t launch_quant_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_t ld_q,
                              float *scale, int64_t M, int64_t K, hipStream_t stream);
 
+// Fused producers (row width at most PRODUCER_MAX_K): RMSNorm with an
+// optional in-place residual add, or SiLU(gate) * up, then the quantizer.
+constexpr int64_t PRODUCER_MAX_K = 32768;
+hipError_t launch_add_rms_quant(const uint16_t *x, int64_t ld_x, uint16_t *residual, int64_t ld_r,
+                                const uint16_t *weight, double eps, uint8_t *q, int64_t ld_q,
+                                float *scale, int64_t M, int64_t K, hipStream_t stream);
+hipError_t launch_silu_mul_quant(const uint16_t *gate_up, int64_t ld_gu, uint8_t *q, int64_t ld_q,
+                                 float *scale, int64_t M, int64_t I, hipStream_t stream);
+
 // M <= DECODE_MAX_M: the bandwidth-bound small-M GEMM.
 constexpr int64_t DECODE_MAX_M = 64;
 
 // `workspace` holds decode_workspace_bytes(M, N, K) bytes (fp32 partial sums
-// of the split-K path, 8 < M <= 64), 4-byte aligned; unused otherwise.
+// of the split-K path, 8 < M <= 64), 16-byte aligned; unused otherwise.
 hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
                               const uint8_t *w, int64_t ldw, const uint8_t *ws,
                               const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,

@@ -110,6 +110,45 @@ int fp8_quant_rows(const void *x_bf16, int64_t ld_x, void *q_e4m3, int64_t ld_q,
     return e == hipSuccess ? BS_OK : BS_ELAUNCH;
 }
 
+int add_rms_norm_quant_fp8(const void *x_bf16, int64_t ld_x, void *residual_bf16, int64_t ld_r,
+                           const void *weight_bf16, double eps, void *q_e4m3, int64_t ld_q,
+                           float *scale, int64_t M, int64_t K, void *stream) {
+    if (!x_bf16 || !weight_bf16 || !q_e4m3 || !scale) return BS_EINVAL;
+    if (M < 1 || K < 32 || K % 32 || M > INT32_MAX || K > bsg::PRODUCER_MAX_K) return BS_EINVAL;
+    if (ld_x < K || ld_q < K || (residual_bf16 && ld_r < K)) return BS_EINVAL;
+    if (!(eps >= 0.0) || eps > 1e300) return BS_EINVAL;
+    if (!aligned16(x_bf16) || !aligned16(q_e4m3) || !aligned16(weight_bf16) || (2 * ld_x) % 16 ||
+        ld_q % 16)
+        return BS_EALIGN;
+    if (residual_bf16 && (!aligned16(residual_bf16) || (2 * ld_r) % 16)) return BS_EALIGN;
+    if ((reinterpret_cast<uintptr_t>(scale) & 3u) != 0) return BS_EALIGN;
+    int num_cus = 0;
+    int st = device_check(&num_cus);
+    if (st != BS_OK) return st;
+    hipError_t e = bsg::launch_add_rms_quant(
+        static_cast<const uint16_t *>(x_bf16), ld_x, static_cast<uint16_t *>(residual_bf16), ld_r,
+        static_cast<const uint16_t *>(weight_bf16), eps, static_cast<uint8_t *>(q_e4m3), ld_q,
+        scale, M, K, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BS_OK : BS_ELAUNCH;
+}
+
+int silu_mul_quant_fp8(const void *gate_up_bf16, int64_t ld_gu, void *q_e4m3, int64_t ld_q,
+                       float *scale, int64_t M, int64_t I, void *stream) {
+    if (!gate_up_bf16 || !q_e4m3 || !scale) return BS_EINVAL;
+    if (M < 1 || I < 32 || I % 32 || M > INT32_MAX || I > bsg::PRODUCER_MAX_K) return BS_EINVAL;
+    if (ld_gu < 2 * I || ld_q < I) return BS_EINVAL;
+    if (!aligned16(gate_up_bf16) || !aligned16(q_e4m3) || (2 * ld_gu) % 16 || ld_q % 16)
+        return BS_EALIGN;
+    if ((reinterpret_cast<uintptr_t>(scale) & 3u) != 0) return BS_EALIGN;
+    int num_cus = 0;
+    int st = device_check(&num_cus);
+    if (st != BS_OK) return st;
+    hipError_t e = bsg::launch_silu_mul_quant(static_cast<const uint16_t *>(gate_up_bf16), ld_gu,
+                                              static_cast<uint8_t *>(q_e4m3), ld_q, scale, M, I,
+                                              static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BS_OK : BS_ELAUNCH;
+}
+
 int gemm_bs_fp8(const void *a_e4m3, int64_t ld_a, const float *a_scale, const void *w_e4m3,
                 int64_t ld_w, const uint8_t *w_scale, const void *bias_bf16, int epilogue,
                 void *y_bf16, int64_t ld_y, int64_t M, int64_t N, int64_t K, void *workspace,

@@ -578,11 +578,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
         bq = make_float4(bf16_to_f32(bias[c0]), bf16_to_f32(bias[c0 + 1]),
                          bf16_to_f32(bias[c0 + 2]), bf16_to_f32(bias[c0 + 3]));
     const float as = a_scale[t];
-    const uint32_t o0 = f32_to_bf16(epilogue(sum.x, as, bq.x, epi));
-    const uint32_t o1 = f32_to_bf16(epilogue(sum.y, as, bq.y, epi));
-    const uint32_t o2 = f32_to_bf16(epilogue(sum.z, as, bq.z, epi));
-    const uint32_t o3 = f32_to_bf16(epilogue(sum.w, as, bq.w, epi));
-    *reinterpret_cast<uint2 *>(Y + (int64_t)t * ldy + c0) = make_uint2(o0 | (o1 << 16), o2 | (o3 << 16));
+    const uint32_t o01 = pack_bf16x2(epilogue(sum.x, as, bq.x, epi), epilogue(sum.y, as, bq.y, epi));
+    const uint32_t o23 = pack_bf16x2(epilogue(sum.z, as, bq.z, epi), epilogue(sum.w, as, bq.w, epi));
+    *reinterpret_cast<uint2 *>(Y + (int64_t)t * ldy + c0) = make_uint2(o01, o23);
 }
 
 template <bool FP4, int MT>

@@ -623,14 +623,11 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
             const int rr = ch / CPR, cc = 4 * (ch % CPR);
             const float4 v = *reinterpret_cast<const float4 *>(slab + rr * C::EP_ROW + 4 * cc);
             const float4 bv = *reinterpret_cast<const float4 *>(bias_w + cc);
-            const uint32_t h0 = f32_to_bf16(epilogue_rest(v.x, bv.x, epi));
-            const uint32_t h1 = f32_to_bf16(epilogue_rest(v.y, bv.y, epi));
-            const uint32_t h2 = f32_to_bf16(epilogue_rest(v.z, bv.z, epi));
-            const uint32_t h3 = f32_to_bf16(epilogue_rest(v.w, bv.w, epi));
+            const uint32_t h01 = pack_bf16x2(epilogue_rest(v.x, bv.x, epi), epilogue_rest(v.y, bv.y, epi));
+            const uint32_t h23 = pack_bf16x2(epilogue_rest(v.z, bv.z, epi), epilogue_rest(v.w, bv.w, epi));
             const int m = mrow + rr, n = ncol0 + cc;
             if (m < M && n < N)
-                *reinterpret_cast<uint2 *>(Y + (int64_t)m * ldy + n) =
-                    make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                *reinterpret_cast<uint2 *>(Y + (int64_t)m * ldy + n) = make_uint2(h01, h23);
         }
         __syncthreads();
     }

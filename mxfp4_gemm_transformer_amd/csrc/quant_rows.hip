@@ -2,6 +2,11 @@
 // (amax / 448) and the row's codes, in one HBM pass over the bf16 input.
 // The "(q_fp8, scale)" pair is what the sly-radiance README's fused
 // producers hand to its W4A8 GEMM (fused norm/quant rows of its file table).
+//
+// The same kernel, instantiated with a producer stage, is those fused
+// producers: RMSNorm (with an optional residual add, the new residual
+// written back) or SiLU(gate) * up computes each bf16 row in registers,
+// and the quantizer runs on it without a trip through HBM.
 #include "bs_device.hpp"
 #include "bs_kernels.hpp"
 
@@ -94,16 +99,139 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v, int width) {
     return v;
 }
 
+// ------------------------------------------------------------ producers
+enum { PROD_NONE = 0, PROD_RMS = 1, PROD_ADD_RMS = 2, PROD_SILU_MUL = 3 };
+
+struct ProdParams {
+    const uint16_t *res;    // PROD_ADD_RMS: residual rows, read
+    uint16_t *res_out;      // PROD_ADD_RMS: new residual rows, written (may equal res)
+    int64_t ldr;
+    const uint16_t *w;      // PROD_RMS / PROD_ADD_RMS: norm weight [K]
+    double eps;
+};
+
+// Nearest bf16 to an fp64 value (bits), ties to even, overflow to infinity.
+// Normal bf16 range: round the 52-bit fraction to 7 bits by adding
+// 2^44 - 1 plus the kept LSB (a carry moves into the exponent), then rebias
+// the exponent from 1023 to 127. Below 2^-126 the bf16 grid is uniform with
+// step 2^-133, so the code is rint(|v| 2^133) (exact scaling; rint rounds
+// to nearest even). `v` must be finite.
+__device__ __forceinline__ uint32_t f64_to_bf16(double v) {
+    const uint64_t bits = (uint64_t)__double_as_longlong(v);
+    const uint32_t sign = (uint32_t)(bits >> 48) & 0x8000u;
+    const uint64_t mag = bits & 0x7FFFFFFFFFFFFFFFull;
+    uint32_t code;
+    if (mag >= ((uint64_t)(1023 + 128) << 52)) {               // |v| >= 2^128
+        code = 0x7F80u;
+    } else if (mag < ((uint64_t)(1023 - 126) << 52)) {         // |v| < 2^-126
+        code = (uint32_t)__builtin_rint(__longlong_as_double((long long)mag) * 0x1p133);
+    } else {
+        const uint64_t r = mag + ((1ull << 44) - 1) + ((mag >> 45) & 1ull);
+        code = (uint32_t)(r >> 45) - ((1023u - 127u) << 7);    // may carry to 0x7F80
+    }
+    return sign | code;
+}
+
+__device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xFFFFu; }
+__device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
+
+// bf16(x + r) for the 8 pairs of two chunks (the fp64 sum of two bf16
+// values rounds to the same bf16 as the exact sum), and the sum of the
+// results' squares in fp64, in element order.
+__device__ __forceinline__ uint4 add8(const uint4 &x, const uint4 &r, double &ss) {
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, rw[4] = {r.x, r.y, r.z, r.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t a = f64_to_bf16((double)bf16_to_f32(lo16(xw[i])) + (double)bf16_to_f32(lo16(rw[i])));
+        const uint32_t b = f64_to_bf16((double)bf16_to_f32(hi16(xw[i])) + (double)bf16_to_f32(hi16(rw[i])));
+        const double da = bf16_to_f32(a), db = bf16_to_f32(b);
+        ss += da * da;
+        ss += db * db;
+        o[i] = a | (b << 16);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ void sumsq8(const uint4 &x, double &ss) {
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const double a = bf16_to_f32(lo16(xw[i])), b = bf16_to_f32(hi16(xw[i]));
+        ss += a * a;
+        ss += b * b;
+    }
+}
+
+// h = bf16(fl32(fl32(r * inv) * w)) for a chunk: the normalized value is
+// rounded to fp32 from fp64, then multiplied by the weight in fp32.
+__device__ __forceinline__ uint4 norm8(const uint4 &r, const uint4 &w, double inv) {
+    const uint32_t rw[4] = {r.x, r.y, r.z, r.w}, ww[4] = {w.x, w.y, w.z, w.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float na = (float)((double)bf16_to_f32(lo16(rw[i])) * inv);
+        const float nb = (float)((double)bf16_to_f32(hi16(rw[i])) * inv);
+        o[i] = pack_bf16x2(na * bf16_to_f32(lo16(ww[i])), nb * bf16_to_f32(hi16(ww[i])));
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// fl32(fl32(silu(g)) * u) (the caller rounds it to bf16), silu(g) =
+// g / (1 + exp(-g)) taken in fp64 and rounded once to fp32. Fast path in fp32 for g >= -8: e = 2^(-g log2 e)
+// from the hardware exp2 (the rounded argument, |arg| < 11.6, costs at most
+// 6 ulps of relative error, the exp2 itself 1), then 1 + e, the hardware
+// reciprocal (1 ulp), g * 1/(1 + e) and * u: the product is within about
+// 10 fp32 ulps of the exact chain's product. Its bf16 rounding can only
+// differ from the exact chain's when it lies within 16 fp32 ulps of a bf16
+// rounding midpoint (low 16 bits near 0x8000) or is tiny; those elements,
+// and gates below -8, are recomputed in fp64 (about 1 in 2000 for
+// unit-scale data).
+__device__ __forceinline__ float silu_mul1(uint32_t gb, uint32_t ub) {
+    const float g = bf16_to_f32(gb), u = bf16_to_f32(ub);
+    const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+    float a = (g * __builtin_amdgcn_rcpf(1.0f + e)) * u;
+    const uint32_t ab = __float_as_uint(a);
+    const bool risky = (g < -8.0f) | ((ab & 0x7FFFFFFFu) < 0x0F800000u) |     // |a| < 2^-96
+                       (((ab & 0xFFFFu) - 0x8000u + 16u) <= 32u);
+    if (risky) {
+        const double gd = g;
+        const float sg64 = (float)(gd / (1.0 + exp(-gd)));
+        a = sg64 * u;
+    }
+    return a;
+}
+
+__device__ __forceinline__ uint4 silu_mul8(const uint4 &g, const uint4 &u) {
+    const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, uw[4] = {u.x, u.y, u.z, u.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = pack_bf16x2(silu_mul1(lo16(gw[i]), lo16(uw[i])), silu_mul1(hi16(gw[i]), hi16(uw[i])));
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ double group_sum(double v, int width) {
+    for (int off = width / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
 // TPR threads per row (16, 64, 256 or 1024); each holds NCH chunks of 8
 // values (16 bytes) in registers between the max reduction and the encode.
 // Chunk c of a row is handled by thread c % TPR, so each load instruction
 // of a wave reads 64 consecutive chunks (1 KiB) and each store writes 512
 // consecutive code bytes.
-template <int QB, int TPR, int NCH>
+//
+// With a producer stage (PROD != PROD_NONE) the row to quantize is made
+// first: x + residual (written back) and RMSNorm, or SiLU(gate) * up with
+// the gate in columns [0, K) of x and up in [K, 2K). RMSNorm's sum of
+// squares meets across the row's threads (shuffles, then LDS) before the
+// normalization pass over the chunks still in registers.
+template <int PROD, int QB, int TPR, int NCH>
 __global__ __launch_bounds__(QB, (QB <= 256 && NCH <= 8) ? 4 : 1) void quant_rows_kernel(const uint16_t *__restrict__ x,
                                                             int64_t ldx, uint8_t *__restrict__ q,
                                                             int64_t ldq, float *__restrict__ scale,
-                                                            int64_t M, int K) {
+                                                            int64_t M, int K, ProdParams pp) {
     constexpr int RPB = QB / TPR;
     const int tid = threadIdx.x;
     const int t = tid % TPR;
@@ -113,17 +241,51 @@ __global__ __launch_bounds__(QB, (QB <= 256 && NCH <= 8) ? 4 : 1) void quant_row
     const uint16_t *xr = x + (active ? m : 0) * ldx;
 
     uint4 v[NCH];
-    uint32_t amax = 0;
+    double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         const int c = t + i * TPR;
         if (active && c < nch) {
-            v[i] = ldg16(xr + 8 * c);
-            amax = max(amax, absmax8(v[i]));
+            if constexpr (PROD == PROD_NONE) {
+                v[i] = ldg16(xr + 8 * c);
+            } else if constexpr (PROD == PROD_RMS) {
+                v[i] = ldg16(xr + 8 * c);
+                sumsq8(v[i], ss);
+            } else if constexpr (PROD == PROD_ADD_RMS) {
+                const uint4 xv = ldg16(xr + 8 * c);
+                const uint4 rv = ldg16(pp.res + m * pp.ldr + 8 * c);
+                v[i] = add8(xv, rv, ss);
+                *reinterpret_cast<uint4 *>(pp.res_out + m * pp.ldr + 8 * c) = v[i];
+            } else {
+                v[i] = silu_mul8(ldg16(xr + 8 * c), ldg16(xr + K + 8 * c));
+            }
         } else {
             v[i] = make_uint4(0u, 0u, 0u, 0u);
         }
     }
+    if constexpr (PROD == PROD_RMS || PROD == PROD_ADD_RMS) {
+        if (TPR <= 64) {
+            ss = group_sum(ss, TPR);
+        } else {
+            __shared__ double sred[QB / 64];
+            ss = group_sum(ss, 64);
+            if ((tid & 63) == 0) sred[tid >> 6] = ss;
+            __syncthreads();
+            const int w0 = (tid / TPR) * (TPR / 64);
+            ss = sred[w0];
+#pragma unroll
+            for (int i = 1; i < TPR / 64; ++i) ss += sred[w0 + i];
+        }
+        const double inv = 1.0 / __builtin_sqrt(ss / (double)K + pp.eps);
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = t + i * TPR;
+            if (active && c < nch) v[i] = norm8(v[i], ldg16(pp.w + 8 * c), inv);
+        }
+    }
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) amax = max(amax, absmax8(v[i]));
     if (TPR <= 64) {
         amax = group_max(amax, TPR);
     } else {   // the TPR / 64 waves of this row meet in LDS
@@ -178,26 +340,26 @@ __global__ __launch_bounds__(QBLOCK) void quant_rows_long_kernel(const uint16_t 
         *reinterpret_cast<uint2 *>(qr + 8 * c) = encode8(ldg16(xr + 8 * c), s, r, r_ok);
 }
 
-template <int QB, int TPR, int NCH>
+template <int PROD, int QB, int TPR, int NCH>
 void launch(const uint16_t *x, int64_t ldx, uint8_t *q, int64_t ldq, float *s, int64_t M, int K,
-            hipStream_t st) {
+            const ProdParams &pp, hipStream_t st) {
     constexpr int RPB = QB / TPR;
     const dim3 grid((unsigned)((M + RPB - 1) / RPB));
-    hipLaunchKernelGGL((quant_rows_kernel<QB, TPR, NCH>), grid, dim3(QB), 0, st, x, ldx, q, ldq, s,
-                       M, K);
+    hipLaunchKernelGGL((quant_rows_kernel<PROD, QB, TPR, NCH>), grid, dim3(QB), 0, st, x, ldx, q,
+                       ldq, s, M, K, pp);
 }
 
 // Register budget: 1024-thread blocks get 128 VGPRs per lane, enough for 4
 // chunks; 256-thread blocks hold up to 16.
-template <int QB, int TPR>
+template <int PROD, int QB, int TPR>
 bool launch_tpr(int nch_per_thread, const uint16_t *x, int64_t ldx, uint8_t *q, int64_t ldq,
-                float *s, int64_t M, int K, hipStream_t st) {
+                float *s, int64_t M, int K, const ProdParams &pp, hipStream_t st) {
     constexpr int CAP = QB > 256 ? 4 : 16;
-    if (nch_per_thread <= 1) launch<QB, TPR, 1>(x, ldx, q, ldq, s, M, K, st);
-    else if (nch_per_thread <= 2) launch<QB, TPR, 2>(x, ldx, q, ldq, s, M, K, st);
-    else if (nch_per_thread <= 4) launch<QB, TPR, 4>(x, ldx, q, ldq, s, M, K, st);
-    else if (nch_per_thread <= 8 && CAP >= 8) launch<QB, TPR, (CAP >= 8 ? 8 : 1)>(x, ldx, q, ldq, s, M, K, st);
-    else if (nch_per_thread <= 16 && CAP >= 16) launch<QB, TPR, (CAP >= 16 ? 16 : 1)>(x, ldx, q, ldq, s, M, K, st);
+    if (nch_per_thread <= 1) launch<PROD, QB, TPR, 1>(x, ldx, q, ldq, s, M, K, pp, st);
+    else if (nch_per_thread <= 2) launch<PROD, QB, TPR, 2>(x, ldx, q, ldq, s, M, K, pp, st);
+    else if (nch_per_thread <= 4) launch<PROD, QB, TPR, 4>(x, ldx, q, ldq, s, M, K, pp, st);
+    else if (nch_per_thread <= 8 && CAP >= 8) launch<PROD, QB, TPR, (CAP >= 8 ? 8 : 1)>(x, ldx, q, ldq, s, M, K, pp, st);
+    else if (nch_per_thread <= 16 && CAP >= 16) launch<PROD, QB, TPR, (CAP >= 16 ? 16 : 1)>(x, ldx, q, ldq, s, M, K, pp, st);
     else return false;
     return true;
 }
@@ -219,20 +381,70 @@ hipError_t launch_quant_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_
     else if (nch <= 64) tpr = 64;
     else if (nch <= 256 && tpr > 256) tpr = 256;
     const int per = (nch + tpr - 1) / tpr;
+    const ProdParams pp{};
     bool ok;
-    if (tpr == 16) ok = launch_tpr<QBLOCK, 16>(per, x, ld_x, q, ld_q, scale, M, k, stream);
-    else if (tpr == 64) ok = launch_tpr<QBLOCK, 64>(per, x, ld_x, q, ld_q, scale, M, k, stream);
-    else if (tpr == 128) ok = launch_tpr<QBLOCK, 128>(per, x, ld_x, q, ld_q, scale, M, k, stream);
-    else if (tpr == 256) ok = launch_tpr<QBLOCK, 256>(per, x, ld_x, q, ld_q, scale, M, k, stream);
+    if (tpr == 16) ok = launch_tpr<PROD_NONE, QBLOCK, 16>(per, x, ld_x, q, ld_q, scale, M, k, pp, stream);
+    else if (tpr == 64) ok = launch_tpr<PROD_NONE, QBLOCK, 64>(per, x, ld_x, q, ld_q, scale, M, k, pp, stream);
+    else if (tpr == 128) ok = launch_tpr<PROD_NONE, QBLOCK, 128>(per, x, ld_x, q, ld_q, scale, M, k, pp, stream);
+    else if (tpr == 256) ok = launch_tpr<PROD_NONE, QBLOCK, 256>(per, x, ld_x, q, ld_q, scale, M, k, pp, stream);
     else {
-        ok = launch_tpr<1024, 1024>(per, x, ld_x, q, ld_q, scale, M, k, stream);
+        ok = launch_tpr<PROD_NONE, 1024, 1024>(per, x, ld_x, q, ld_q, scale, M, k, pp, stream);
         if (!ok)   // long rows: 256 threads each hold more chunks
-            ok = launch_tpr<QBLOCK, 256>((nch + 255) / 256, x, ld_x, q, ld_q, scale, M, k, stream);
+            ok = launch_tpr<PROD_NONE, QBLOCK, 256>((nch + 255) / 256, x, ld_x, q, ld_q, scale, M, k, pp, stream);
     }
     if (!ok)
         hipLaunchKernelGGL(quant_rows_long_kernel, dim3((unsigned)M), dim3(QBLOCK), 0, stream, x,
                            ld_x, q, ld_q, scale, M, k);
     return hipGetLastError();
+}
+
+namespace {
+
+// Thread count per row for a producer: the quantizer's choice, widened
+// until each thread holds at most 16 chunks (8 for 128 threads per row).
+template <int PROD>
+bool launch_producer(const uint16_t *x, int64_t ldx, uint8_t *q, int64_t ldq, float *s, int64_t M,
+                     int K, const ProdParams &pp, hipStream_t st) {
+    const int nch = K / 8;
+    int tpr = M >= 512 ? (nch > 512 ? 128 : 64) : (M <= 64 ? 1024 : 256);
+    if (nch <= 16) tpr = 16;
+    else if (nch <= 64) tpr = 64;
+    else if (nch <= 256 && tpr > 256) tpr = 256;
+    if (tpr == 64 && nch > 64 * 16) tpr = 128;
+    if (tpr == 128 && nch > 128 * 8) tpr = 256;
+    if (tpr == 256 && nch > 256 * 16) tpr = 1024;
+    const int per = (nch + tpr - 1) / tpr;
+    switch (tpr) {
+    case 16: return launch_tpr<PROD, QBLOCK, 16>(per, x, ldx, q, ldq, s, M, K, pp, st);
+    case 64: return launch_tpr<PROD, QBLOCK, 64>(per, x, ldx, q, ldq, s, M, K, pp, st);
+    case 128: return launch_tpr<PROD, QBLOCK, 128>(per, x, ldx, q, ldq, s, M, K, pp, st);
+    case 256: return launch_tpr<PROD, QBLOCK, 256>(per, x, ldx, q, ldq, s, M, K, pp, st);
+    default: return launch_tpr<PROD, 1024, 1024>(per, x, ldx, q, ldq, s, M, K, pp, st);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_add_rms_quant(const uint16_t *x, int64_t ld_x, uint16_t *residual, int64_t ld_r,
+                                const uint16_t *weight, double eps, uint8_t *q, int64_t ld_q,
+                                float *scale, int64_t M, int64_t K, hipStream_t stream) {
+    ProdParams pp{};
+    pp.res = residual;
+    pp.res_out = residual;
+    pp.ldr = ld_r;
+    pp.w = weight;
+    pp.eps = eps;
+    const bool ok = residual
+        ? launch_producer<PROD_ADD_RMS>(x, ld_x, q, ld_q, scale, M, (int)K, pp, stream)
+        : launch_producer<PROD_RMS>(x, ld_x, q, ld_q, scale, M, (int)K, pp, stream);
+    return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+hipError_t launch_silu_mul_quant(const uint16_t *gate_up, int64_t ld_gu, uint8_t *q, int64_t ld_q,
+                                 float *scale, int64_t M, int64_t I, hipStream_t stream) {
+    const ProdParams pp{};
+    const bool ok = launch_producer<PROD_SILU_MUL>(gate_up, ld_gu, q, ld_q, scale, M, (int)I, pp, stream);
+    return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
 }  // namespace bsg

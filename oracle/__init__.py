@@ -21,6 +21,14 @@ Parity status of each function (the pins are the ``-m "not gpu"`` tests in
   torch's tanh GELU).
 * MXFP4 weight preparation: pinned (OCP rule properties, exact round trip
   of representable groups, the input generator's independent numpy path).
+* bf16 rounding of fp64 values: pinned (torch's fp32 -> bf16 cast on values
+  exact in fp32, exact rational nearest-neighbour search on values that are
+  not, overflow and signed zeros).
+* fused producers (RMSNorm with residual add, SiLU * up, each followed by
+  the quantizer): pinned (closed forms on constant rows and eps, power-of-two
+  scaling invariance, torch's float64 rms_norm and silu within one bf16
+  step, torch's bf16 residual add, gate/up half order, the quantizer applied
+  to the returned intermediate).
 """
 from __future__ import annotations
 
@@ -87,6 +95,13 @@ def _load():
         lib.or_encode_e4m3.restype = None
         lib.or_quant_mxfp4_weights.argtypes = [vp, i64, i64, vp, vp]
         lib.or_quant_mxfp4_weights.restype = None
+        lib.or_bf16_round.argtypes = [f64]
+        lib.or_bf16_round.restype = ctypes.c_uint16
+        lib.or_add_rms_norm_quant.argtypes = [vp, i64, vp, i64, vp, f64, i64, i64, vp, i64, vp, i64,
+                                              vp, i64, vp]
+        lib.or_add_rms_norm_quant.restype = None
+        lib.or_silu_mul_quant.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp]
+        lib.or_silu_mul_quant.restype = None
         lib.or_num_threads.argtypes = []
         lib.or_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -159,6 +174,48 @@ def quant_rows(x_bf16: np.ndarray):
     s = np.empty((M,), dtype=np.float32)
     _load().or_quant_rows(_ptr(x), K, M, K, _ptr(q), K, _ptr(s))
     return q, s
+
+
+# ---------------------------------------------------------- fused producers
+def bf16_round(v: float) -> int:
+    """Bits of the nearest bfloat16 to v (ties even, overflow to infinity)."""
+    return int(_load().or_bf16_round(float(v)))
+
+
+def add_rms_norm_quant(x_bf16, residual_bf16, weight_bf16, eps):
+    """RMSNorm (with the residual added first when given) then the per-token
+    quantizer. bf16 bits in (uint16 [M, K], [M, K] or None, [K]); returns
+    (codes uint8 [M, K], scales float32 [M], new residual uint16 [M, K] or
+    None, normalized row h uint16 [M, K])."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    w = _c(weight_bf16, np.uint16)
+    assert w.shape == (K,)
+    r = None if residual_bf16 is None else _c(residual_bf16, np.uint16)
+    if r is not None:
+        assert r.shape == (M, K)
+    r_out = None if r is None else np.empty((M, K), dtype=np.uint16)
+    h = np.empty((M, K), dtype=np.uint16)
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M,), dtype=np.float32)
+    _load().or_add_rms_norm_quant(_ptr(x), K, _ptr(r), K, _ptr(w), float(eps), M, K,
+                                  _ptr(r_out), K, _ptr(h), K, _ptr(q), K, _ptr(s))
+    return q, s, r_out, h
+
+
+def silu_mul_quant(gate_up_bf16):
+    """SiLU(gate) * up then the per-token quantizer; gate_up bf16 bits
+    [M, 2I] (gate in the first I columns). Returns (codes uint8 [M, I],
+    scales float32 [M], the bf16 product row a uint16 [M, I])."""
+    gu = _c(gate_up_bf16, np.uint16)
+    M, I2 = gu.shape
+    assert I2 % 2 == 0
+    I = I2 // 2
+    a = np.empty((M, I), dtype=np.uint16)
+    q = np.empty((M, I), dtype=np.uint8)
+    s = np.empty((M,), dtype=np.float32)
+    _load().or_silu_mul_quant(_ptr(gu), I2, M, I, _ptr(a), I, _ptr(q), I, _ptr(s))
+    return q, s, a
 
 
 # ------------------------------------------------------------------- GEMMs

@@ -178,6 +178,113 @@ void or_quant_rows(const uint16_t *x, int64_t ldx, int64_t M, int64_t K,
     }
 }
 
+/* ------------------------------------------------------ fused producers */
+
+/* Nearest bfloat16 to a real number held exactly in a double, as bits:
+ * ties to the even significand, magnitudes that round past the largest
+ * finite value become infinity, the sign is kept (also for zero results).
+ * bfloat16 has binary32's exponent range and 8 significand bits, so its
+ * spacing is 2^(e-7) in the binade [2^e, 2^(e+1)) for e >= -126 and 2^-133
+ * below 2^-126. |v| / spacing is exact in fp64 (a power-of-two scaling),
+ * rint() rounds it to the nearest integer with ties to even, and the
+ * rounded value times the spacing is a bfloat16 value (or 2^128), which
+ * the binary32 cast holds exactly. `v` must be finite. */
+static uint16_t bf16_round(double v)
+{
+    union { float f; uint32_t u; } c;
+    double a = fabs(v), ulp, r;
+    if (a == 0.0) {
+        ulp = 1.0;
+    } else if (a < ldexp(1.0, -126)) {
+        ulp = ldexp(1.0, -133);
+    } else {
+        int e2;
+        frexp(a, &e2);                 /* a = f * 2^e2, f in [0.5, 1) */
+        ulp = ldexp(1.0, (e2 - 1) - 7);
+    }
+    r = rint(a / ulp) * ulp;
+    c.f = r >= ldexp(1.0, 128) ? INFINITY : (float)r;
+    return (uint16_t)((c.u >> 16) | (signbit(v) ? 0x8000u : 0u));
+}
+
+uint16_t or_bf16_round(double v) { return bf16_round(v); }
+
+/* RMSNorm with an optional residual add in front, the input side of the
+ * sly-radiance README's fused add_rms_quant producer (fused norm/quant rows
+ * of its file table: the new residual and the "(q_fp8, scale)" pair come
+ * out of one kernel). Per row m, with bf16 inputs x, res and weight w:
+ *     r[k]  = bf16(x[k] + res[k])          (r = x when res is NULL)
+ *     ms    = (sum_k r[k]^2) / K            fp64, summed in k order
+ *     inv   = 1 / sqrt(ms + eps)            fp64
+ *     h[k]  = bf16(fl32(fl32(r[k] * inv) * w[k]))
+ *     (q, s) = the per-token quantizer applied to the row h.
+ * The norm is the cortiq dit.rs page's rms_norm (mean of squares and the
+ * reciprocal root in fp64, the normalized value rounded to fp32, then the
+ * fp32 weight multiply); h is rounded to bf16 as the unfused chain's norm
+ * output would be before the quantizer reads it. The sum x + res of two
+ * bf16 values is exact in fp64. Outputs: r into res_out (when res is
+ * given), h into h_out, codes and scales as or_quant_rows. */
+void or_add_rms_norm_quant(const uint16_t *x, int64_t ldx, const uint16_t *res, int64_t ldr,
+                           const uint16_t *w, double eps, int64_t M, int64_t K,
+                           uint16_t *res_out, int64_t ldro, uint16_t *h_out, int64_t ldh,
+                           uint8_t *q, int64_t ldq, float *s)
+{
+    int64_t m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        const uint16_t *xr = x + m * ldx;
+        uint16_t *hr = h_out + m * ldh;
+        double ss = 0.0, inv;
+        int64_t k;
+        for (k = 0; k < K; ++k) {
+            double r = or_bf16_value(xr[k]);
+            if (res) {
+                uint16_t rb = bf16_round(r + or_bf16_value(res[m * ldr + k]));
+                res_out[m * ldro + k] = rb;
+                r = or_bf16_value(rb);
+            }
+            ss += r * r;
+        }
+        inv = 1.0 / sqrt(ss / (double)K + eps);
+        for (k = 0; k < K; ++k) {
+            double r = or_bf16_value(res ? res_out[m * ldro + k] : xr[k]);
+            float n32 = to_f32(r * inv);
+            float h32 = n32 * (float)or_bf16_value(w[k]);     /* binary32 multiply */
+            hr[k] = bf16_round((double)h32);
+        }
+    }
+    or_quant_rows(h_out, ldh, M, K, q, ldq, s);
+}
+
+/* SiLU(gate) * up, the input side of the sly-radiance README's fused
+ * silu_mul_quant producer (same rows of its table; the gated MLP's act_fn).
+ * gu is [M, 2I] bf16 with the gate in columns [0, I) and up in [I, 2I).
+ *     sg[k] = fl32(g / (1 + exp(-g)))      fp64 inside, g = gu[m, k]
+ *     a[k]  = bf16(fl32(sg[k] * u))          u = gu[m, I + k], binary32 multiply
+ *     (q, s) = the per-token quantizer applied to the row a.
+ * silu and the gate-times-up product follow the cortiq dit.rs page's
+ * silu() and SwiGLU loop (binary32 values); silu is evaluated in fp64 and
+ * rounded once to binary32 (exp in fp64 is within an ulp on any platform,
+ * where binary32 expf implementations differ). Outputs a into a_out and the
+ * codes and scales as or_quant_rows. */
+void or_silu_mul_quant(const uint16_t *gu, int64_t ldgu, int64_t M, int64_t I,
+                       uint16_t *a_out, int64_t lda, uint8_t *q, int64_t ldq, float *s)
+{
+    int64_t m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        int64_t k;
+        for (k = 0; k < I; ++k) {
+            double g = or_bf16_value(gu[m * ldgu + k]);
+            double u = or_bf16_value(gu[m * ldgu + I + k]);
+            float sg = to_f32(g / (1.0 + exp(-g)));
+            float a32 = sg * (float)u;                      /* binary32 multiply */
+            a_out[m * lda + k] = bf16_round((double)a32);
+        }
+    }
+    or_quant_rows(a_out, lda, M, I, q, ldq, s);
+}
+
 /* ------------------------------------------------------------- epilogue */
 
 /* tanh-approximated GELU: 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))),

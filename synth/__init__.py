@@ -25,6 +25,15 @@ fused gate_up):
 Value laws: A ~ N(0,1) rounded to bf16; e4m3 W = nearest e4m3 code of an
 N(0, 0.05) sample; 32x32 scale bytes uniform on [120, 130]; bias ~ N(0, 0.1)
 rounded to bf16; MXFP4 W from N(0, 0.02) samples by the OCP MX conversion.
+
+Fused-producer inputs (the sly-radiance README's add_rms_quant and
+silu_mul_quant feed the 5120-wide gate_up and the 17408-wide down
+projection of the same model):
+
+  add_rms   x [M, 5120] ~ N(0,1), residual ~ N(0, 2^2), norm weight
+            ~ U(0.5, 1.5), all rounded to bf16; eps = 1e-6
+  silu_mul  gate_up [M, 2*17408] ~ N(0, 1.5^2) rounded to bf16 (gate in
+            the first half)
 """
 from __future__ import annotations
 
@@ -37,6 +46,7 @@ EPI_NONE, EPI_BIAS, EPI_BIAS_GELU_TANH = 0, 1, 2
 
 # tensor ids of the per-tensor streams
 _T_A, _T_OUTLIER, _T_W, _T_WS, _T_BIAS = 0, 1, 2, 3, 4
+_T_RES, _T_GAMMA, _T_GU = 5, 6, 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -164,3 +174,27 @@ def make(name: str, M: int | None = None, seed: int = 0) -> dict:
     w, ws = weights(wl, seed)
     return {"wl": wl, "M": wl.M if M is None else M, "a_bf16": activations(wl, M, seed),
             "w": w, "w_scale": ws, "bias": bias(wl, seed), "epilogue": wl.epilogue}
+
+
+# fused producers: name -> (row width at full size, M sweep)
+PRODUCERS = {
+    "add_rms": (5120, (1, 16, 512, 4096)),
+    "silu_mul": (17408, (1, 16, 512, 4096)),
+}
+RMS_EPS = 1e-6
+
+
+def producer_inputs(name: str, M: int, width: int | None = None, seed: int = 0) -> dict:
+    """Inputs of a fused producer as bf16 bits. add_rms: x [M, width],
+    residual [M, width], weight [width], eps. silu_mul: gate_up [M, 2 width]."""
+    width = PRODUCERS[name][0] if width is None else width
+    if name == "add_rms":
+        x = _rng(seed, _T_A).standard_normal((M, width), dtype=np.float32)
+        r = _rng(seed, _T_RES).standard_normal((M, width), dtype=np.float32) * np.float32(2.0)
+        g = _rng(seed, _T_GAMMA).uniform(0.5, 1.5, width).astype(np.float32)
+        return {"x": to_bf16_bits(x), "residual": to_bf16_bits(r), "weight": to_bf16_bits(g),
+                "eps": RMS_EPS, "M": M, "K": width}
+    if name == "silu_mul":
+        gu = _rng(seed, _T_GU).standard_normal((M, 2 * width), dtype=np.float32) * np.float32(1.5)
+        return {"gate_up": to_bf16_bits(gu), "M": M, "I": width}
+    raise KeyError(name)

@@ -111,6 +111,52 @@ def test_quant_argument_checks():
     assert q(s=ctypes.c_void_p(0x10002)) == bs.BS_EALIGN
 
 
+def test_producer_argument_checks():
+    lib = bs.load_library()
+    E, A = bs.BS_EINVAL, bs.BS_EALIGN
+
+    def rms(x=FAKE, ldx=64, r=FAKE, ldr=64, w=FAKE, eps=1e-6, q=FAKE, ldq=64, s=FAKE, M=4, K=64):
+        return lib.add_rms_norm_quant_fp8(x, ldx, r, ldr, w, eps, q, ldq, s, M, K, None)
+
+    assert rms(x=None) == E
+    assert rms(w=None) == E
+    assert rms(q=None) == E
+    assert rms(s=None) == E
+    assert rms(M=0) == E
+    assert rms(K=48) == E
+    assert rms(K=32768 + 32, ldx=40000, ldr=40000, ldq=40000) == E    # longer than 32768
+    assert rms(ldx=32) == E
+    assert rms(ldr=32) == E
+    assert rms(ldq=32) == E
+    assert rms(eps=-1.0) == E
+    assert rms(eps=float("nan")) == E
+    assert rms(x=ctypes.c_void_p(0x10008)) == A
+    assert rms(r=ctypes.c_void_p(0x10008)) == A
+    assert rms(w=ctypes.c_void_p(0x10002)) == A
+    assert rms(q=ctypes.c_void_p(0x10001)) == A
+    assert rms(ldx=68) == A
+    assert rms(ldr=68) == A
+    assert rms(ldq=72) == A
+    assert rms(s=ctypes.c_void_p(0x10002)) == A
+    assert rms(r=None, ldr=0, x=ctypes.c_void_p(0x10008)) == A     # no residual: its stride is unused
+
+    def silu(gu=FAKE, ld=128, q=FAKE, ldq=64, s=FAKE, M=4, I=64):
+        return lib.silu_mul_quant_fp8(gu, ld, q, ldq, s, M, I, None)
+
+    assert silu(gu=None) == E
+    assert silu(q=None) == E
+    assert silu(s=None) == E
+    assert silu(M=0) == E
+    assert silu(I=48) == E
+    assert silu(I=32768 + 32, ld=70000, ldq=40000) == E
+    assert silu(ld=127) == E                                          # < 2I
+    assert silu(ldq=32) == E
+    assert silu(gu=ctypes.c_void_p(0x10008)) == A
+    assert silu(ld=132) == A
+    assert silu(ldq=72) == A
+    assert silu(s=ctypes.c_void_p(0x10002)) == A
+
+
 def test_valid_call_without_a_gpu_is_refused_by_the_arch_gate():
     import subprocess
     import sys
