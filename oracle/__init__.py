@@ -24,6 +24,12 @@ Parity status of each function (the pins are the ``-m "not gpu"`` tests in
 * bf16 rounding of fp64 values: pinned (torch's fp32 -> bf16 cast on values
   exact in fp32, exact rational nearest-neighbour search on values that are
   not, overflow and signed zeros).
+* static-scale quantizer: pinned (equals the dynamic quantizer when given
+  the row's own scale; saturation beyond 448 s; torch's float8 cast).
+* row-wise scaled GEMM (per-token x per-channel fp32 scales): pinned
+  (dequantize-then-matmul in numpy, exact rational brute force, equality
+  with the block-scaled GEMM when the channel scales are uniform powers of
+  two, sampled = whole).
 * fused producers (RMSNorm with residual add, SiLU * up, each followed by
   the quantizer): pinned (closed forms on constant rows and eps, power-of-two
   scaling invariance, torch's float64 rms_norm and silu within one bf16
@@ -95,6 +101,14 @@ def _load():
         lib.or_encode_e4m3.restype = None
         lib.or_quant_mxfp4_weights.argtypes = [vp, i64, i64, vp, vp]
         lib.or_quant_mxfp4_weights.restype = None
+        lib.or_quant_rows_static.argtypes = [vp, i64, i64, i64, ctypes.c_float, vp, i64]
+        lib.or_quant_rows_static.restype = None
+        rw = [vp, i64, vp, vp, i64, vp, vp, ctypes.c_int, i64, i64, i64, vp, vp]
+        lib.or_gemm_fp8_rowwise.argtypes = rw
+        lib.or_gemm_fp8_rowwise.restype = None
+        lib.or_gemm_fp8_rowwise_sampled.argtypes = [vp, i64, vp, vp, i64, vp, vp, ctypes.c_int,
+                                                    i64, i64, vp, vp, vp, vp]
+        lib.or_gemm_fp8_rowwise_sampled.restype = None
         lib.or_bf16_round.argtypes = [f64]
         lib.or_bf16_round.restype = ctypes.c_uint16
         lib.or_add_rms_norm_quant.argtypes = [vp, i64, vp, i64, vp, f64, i64, i64, vp, i64, vp, i64,
@@ -174,6 +188,15 @@ def quant_rows(x_bf16: np.ndarray):
     s = np.empty((M,), dtype=np.float32)
     _load().or_quant_rows(_ptr(x), K, M, K, _ptr(q), K, _ptr(s))
     return q, s
+
+
+def quant_rows_static(x_bf16: np.ndarray, scale: float) -> np.ndarray:
+    """e4m3 codes of bf16 bits [M, K] divided by one given fp32 scale."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    q = np.empty((M, K), dtype=np.uint8)
+    _load().or_quant_rows_static(_ptr(x), K, M, K, float(np.float32(scale)), _ptr(q), K)
+    return q
 
 
 # ---------------------------------------------------------- fused producers
@@ -277,6 +300,42 @@ def gemm_sampled(fmt, a_codes, a_scale, w, w_scale, bias_bf16, epilogue, ms, ns)
         fn, ldw = _load().or_gemm_mxfp4_w4a8_sampled, K // 2
     fn(_ptr(a), K, _ptr(s), _ptr(w), ldw, _ptr(ws), _ptr(b), int(epilogue), K,
        ms.size, _ptr(ms), _ptr(ns), _ptr(out), _ptr(absum))
+    return out, absum
+
+
+def gemm_fp8_rowwise(a_codes, a_scale, w_codes, w_scale_f32, bias_bf16=None,
+                     epilogue=EPI_NONE):
+    """fp64 output and absum [M, N] of the row-wise scaled e4m3 GEMM
+    (per-token a_scale [M] x per-channel w_scale [N], both fp32)."""
+    a = _c(a_codes, np.uint8)
+    s = _c(a_scale, np.float32)
+    w = _c(w_codes, np.uint8)
+    ws = _c(w_scale_f32, np.float32)
+    M, K = a.shape
+    N = w.shape[0]
+    assert w.shape == (N, K) and ws.shape == (N,) and s.shape == (M,)
+    b = None if bias_bf16 is None else _c(bias_bf16, np.uint16)
+    out = np.empty((M, N), dtype=np.float64)
+    absum = np.empty((M, N), dtype=np.float64)
+    _load().or_gemm_fp8_rowwise(_ptr(a), K, _ptr(s), _ptr(w), K, _ptr(ws), _ptr(b),
+                                int(epilogue), M, N, K, _ptr(out), _ptr(absum))
+    return out, absum
+
+
+def gemm_fp8_rowwise_sampled(a_codes, a_scale, w_codes, w_scale_f32, bias_bf16, epilogue, ms, ns):
+    a = _c(a_codes, np.uint8)
+    s = _c(a_scale, np.float32)
+    w = _c(w_codes, np.uint8)
+    ws = _c(w_scale_f32, np.float32)
+    K = a.shape[1]
+    b = None if bias_bf16 is None else _c(bias_bf16, np.uint16)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    out = np.empty(ms.shape, dtype=np.float64)
+    absum = np.empty(ms.shape, dtype=np.float64)
+    _load().or_gemm_fp8_rowwise_sampled(_ptr(a), K, _ptr(s), _ptr(w), K, _ptr(ws), _ptr(b),
+                                        int(epilogue), K, ms.size, _ptr(ms), _ptr(ns),
+                                        _ptr(out), _ptr(absum))
     return out, absum
 
 

@@ -178,6 +178,22 @@ void or_quant_rows(const uint16_t *x, int64_t ldx, int64_t M, int64_t K,
     }
 }
 
+/* Quantization with a given (static, per-tensor) scale, the flash-rt
+ * groot_n17 frontend's calibrated activation scales (its host "alphas" are
+ * act_scale x w_scale): q = enc(fl32(x / s)) for every element, s > 0
+ * finite. Values beyond 448 s saturate. */
+void or_quant_rows_static(const uint16_t *x, int64_t ldx, int64_t M, int64_t K, float sc,
+                          uint8_t *q, int64_t ldq)
+{
+    int64_t m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        int64_t k;
+        for (k = 0; k < K; ++k)
+            q[m * ldq + k] = or_e4m3_encode((double)to_f32(or_bf16_value(x[m * ldx + k]) / (double)sc));
+    }
+}
+
 /* ------------------------------------------------------ fused producers */
 
 /* Nearest bfloat16 to a real number held exactly in a double, as bits:
@@ -398,6 +414,59 @@ void or_gemm_mxfp4_w4a8(const uint8_t *a, int64_t lda, const float *a_scale,
         int64_t m = idx / N, n = idx % N;
         one_mxfp4(a + m * lda, a_scale[m], w + n * ldw, ws + n * (K / 32),
                   bias ? bias + n : NULL, epi, K, out + idx, absum + idx);
+    }
+}
+
+/* One output of the row-wise scaled e4m3 GEMM: per-token activation scale
+ * times per-output-channel weight scale (sly-radiance README, lm_head row of
+ * its file table: the head's weight quantized to fp8 per output channel and
+ * run as a row-wise scaled GEMM with per-token fp8 activations). In fp64:
+ *   acc   = sum_k a[k] w[k]
+ *   pre   = a_scale * w_scale * acc (+ bias)
+ *   out   = pre, or GELU_tanh(pre)
+ *   absum = |a_scale * w_scale| * sum_k |a[k] w[k]|                        */
+static void one_rowwise(const uint8_t *a, float a_scale, const uint8_t *w, float w_scale,
+                        const uint16_t *bias_n, int epi, int64_t K, double *out, double *absum)
+{
+    double acc = 0.0, abs_acc = 0.0, pre;
+    int64_t k;
+    for (k = 0; k < K; ++k) {
+        double p = or_e4m3_value(a[k]) * or_e4m3_value(w[k]);
+        acc += p;
+        abs_acc += fabs(p);
+    }
+    pre = (double)a_scale * (double)w_scale * acc;
+    if (epi >= OR_EPI_BIAS)
+        pre += or_bf16_value(*bias_n);
+    *out = epilogue(pre, epi);
+    *absum = fabs((double)a_scale * (double)w_scale) * abs_acc;
+}
+
+void or_gemm_fp8_rowwise(const uint8_t *a, int64_t lda, const float *a_scale,
+                         const uint8_t *w, int64_t ldw, const float *w_scale,
+                         const uint16_t *bias, int epi, int64_t M, int64_t N, int64_t K,
+                         double *out, double *absum)
+{
+    int64_t idx;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (idx = 0; idx < M * N; ++idx) {
+        int64_t m = idx / N, n = idx % N;
+        one_rowwise(a + m * lda, a_scale[m], w + n * ldw, w_scale[n], bias ? bias + n : NULL,
+                    epi, K, out + idx, absum + idx);
+    }
+}
+
+void or_gemm_fp8_rowwise_sampled(const uint8_t *a, int64_t lda, const float *a_scale,
+                                 const uint8_t *w, int64_t ldw, const float *w_scale,
+                                 const uint16_t *bias, int epi, int64_t K, int64_t count,
+                                 const int64_t *ms, const int64_t *ns, double *out, double *absum)
+{
+    int64_t i;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (i = 0; i < count; ++i) {
+        int64_t m = ms[i], n = ns[i];
+        one_rowwise(a + m * lda, a_scale[m], w + n * ldw, w_scale[n], bias ? bias + n : NULL,
+                    epi, K, out + i, absum + i);
     }
 }
 

@@ -21,10 +21,15 @@ fused gate_up):
   ffn_up   M=2048, N=4096, K=1024, e4m3 W, bias + tanh-GELU (second variant
            bias only)
   gate_up  M in {1,16,512,4096}, N=34816, K=5120, MXFP4 W (e2m1 + 1x32 E8M0)
+  lm_head  M in {1,8,16}, N=248320, K=5120, e4m3 W with one fp32 scale per
+           output channel (the sly-radiance README's fp8 lm_head: weight
+           quantized per output channel, per-token fp8 activations)
 
 Value laws: A ~ N(0,1) rounded to bf16; e4m3 W = nearest e4m3 code of an
 N(0, 0.05) sample; 32x32 scale bytes uniform on [120, 130]; bias ~ N(0, 0.1)
-rounded to bf16; MXFP4 W from N(0, 0.02) samples by the OCP MX conversion.
+rounded to bf16; MXFP4 W from N(0, 0.02) samples by the OCP MX conversion;
+per-channel e4m3 W from N(0, 0.02) samples rounded to bf16, each row
+quantized with scale amax/448 (the per-token rule applied to weight rows).
 
 Fused-producer inputs (the sly-radiance README's add_rms_quant and
 silu_mul_quant feed the 5120-wide gate_up and the 17408-wide down
@@ -55,7 +60,7 @@ class Workload:
     M: int
     N: int
     K: int
-    fmt: str               # "fp8" (e4m3 W, 32x32 scales) or "mxfp4"
+    fmt: str               # "fp8" (e4m3 W, 32x32 scales), "mxfp4" or "fp8_rowwise"
     epilogue: int
     outlier_frac: float = 0.0
     m_sweep: tuple = ()
@@ -68,6 +73,7 @@ WORKLOADS = {
     "ffn_up": Workload("ffn_up", 2048, 4096, 1024, "fp8", EPI_BIAS_GELU_TANH),
     "ffn_up_bias": Workload("ffn_up_bias", 2048, 4096, 1024, "fp8", EPI_BIAS),
     "gate_up": Workload("gate_up", 16, 34816, 5120, "mxfp4", EPI_NONE, m_sweep=(1, 16, 512, 4096)),
+    "lm_head": Workload("lm_head", 8, 248320, 5120, "fp8_rowwise", EPI_NONE, m_sweep=(1, 8, 16)),
 }
 
 
@@ -141,9 +147,43 @@ def _mx_quantize_rows(v: np.ndarray):
     return packed, byte.astype(np.uint8)
 
 
+def _rowwise_quantize_rows(v_bf16: np.ndarray):
+    # Offline per-output-channel weight quantization: per row, the scale
+    # fl32(amax / 448) and each element's e4m3 code of fl32(w / scale) by
+    # torch's float8_e4m3fn cast (nearest, ties even; |w / scale| <= 448 up
+    # to the fp32 rounding of the division, which the cast rounds to 448).
+    # A CPU test checks the result bit for bit against the oracle's
+    # per-token quantizer applied to the weight rows.
+    t = torch.from_numpy(np.ascontiguousarray(v_bf16).view(np.int16)).view(torch.bfloat16).float()
+    amax = t.abs().amax(dim=1)
+    scale = (amax.double() / 448.0).float()
+    safe = torch.where(scale > 0, scale, torch.ones_like(scale))
+    q = (t / safe[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return q, scale.numpy()
+
+
+def weight_bf16_rows(wl: Workload, r0: int, r1: int, seed: int = 0) -> np.ndarray:
+    """bf16 bits of weight rows [r0, r1) for the per-channel workloads."""
+    rng = _rng(seed, _T_W)
+    if r0:
+        rng.standard_normal((r0, wl.K), dtype=np.float32)   # advance the stream
+    return to_bf16_bits(rng.standard_normal((r1 - r0, wl.K), dtype=np.float32) * np.float32(0.02))
+
+
 def weights(wl: Workload, seed: int = 0):
     """(W, W scales): e4m3 codes [N, K] with E8M0 [N/32, K/32] uniform on
-    [120, 130], or MXFP4 packed [N, K/2] with E8M0 [N, K/32]."""
+    [120, 130]; MXFP4 packed [N, K/2] with E8M0 [N, K/32]; or e4m3 codes
+    [N, K] with one fp32 scale per row [N] (fmt "fp8_rowwise")."""
+    if wl.fmt == "fp8_rowwise":
+        codes = np.empty((wl.N, wl.K), dtype=np.uint8)
+        scales = np.empty((wl.N,), dtype=np.float32)
+        rng = _rng(seed, _T_W)
+        chunk = 8192
+        for r0 in range(0, wl.N, chunk):
+            r1 = min(wl.N, r0 + chunk)
+            v = to_bf16_bits(rng.standard_normal((r1 - r0, wl.K), dtype=np.float32) * np.float32(0.02))
+            codes[r0:r1], scales[r0:r1] = _rowwise_quantize_rows(v)
+        return codes, scales
     if wl.fmt == "fp8":
         w = _encode_e4m3_weights(weight_values(wl, seed))
         ws = _rng(seed, _T_WS).integers(120, 131, size=(wl.N // 32, wl.K // 32),
