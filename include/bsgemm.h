@@ -7,7 +7,9 @@
  *                       e4m3fn with one E8M0 scale per 32x32 block
  *   3. gemm_mxfp4_w4a8  the same with MXFP4 weights (fp4 e2m1, one E8M0 scale
  *                       per row per 32 along K)
- *   4. add_rms_norm_quant_fp8, silu_mul_quant_fp8
+ *   4. gemm_fp8_rowwise  e4m3 weights with one fp32 scale per output channel;
+ *      fp8_quant_rows_static  quantization with a given per-tensor scale
+ *   5. add_rms_norm_quant_fp8, silu_mul_quant_fp8
  *                       fused producers: RMSNorm (with an optional residual
  *                       add) or SiLU(gate) * up, then step 1, in one kernel
  *
@@ -84,6 +86,20 @@ enum bs_epilogue {
  */
 int fp8_quant_rows(const void *x_bf16, int64_t ld_x, void *q_e4m3, int64_t ld_q,
                    float *scale, int64_t M, int64_t K, void *stream);
+
+/*
+ * Quantization with one given (static, per-tensor) scale, for calibrated
+ * activation scales (flash-rt groot_n17 frontend, fused-epilogue tier: its
+ * host alphas are act_scale x w_scale per site):
+ *     q[m,k] = e4m3fn(x[m,k] / scale_in[0])    (same rounding as above)
+ *   scale_in   device pointer to one fp32 > 0 (finite); read by the kernel
+ *   scale_out  [M] fp32 out, or NULL: every entry set to scale_in[0], so the
+ *              pair (q, scale_out) feeds the GEMMs like fp8_quant_rows' does
+ *   Other arguments as fp8_quant_rows. Values beyond 448 * scale saturate.
+ */
+int fp8_quant_rows_static(const void *x_bf16, int64_t ld_x, const float *scale_in,
+                          void *q_e4m3, int64_t ld_q, float *scale_out, int64_t M, int64_t K,
+                          void *stream);
 
 /*
  * Fused producers: the row that feeds the quantizer is computed in the same
@@ -167,8 +183,27 @@ int gemm_mxfp4_w4a8(const void *a_e4m3, int64_t ld_a, const float *a_scale,
                     int64_t M, int64_t N, int64_t K,
                     void *workspace, size_t workspace_bytes, void *stream);
 
-/* Scratch bytes gemm_bs_fp8 (op 0) or gemm_mxfp4_w4a8 (op 1) needs for this
- * shape; 0 means none. Nonzero for 8 < M <= 64, where K is split across
+/*
+ * Row-wise scaled e4m3 GEMM: one fp32 scale per token and one per output
+ * channel (sly-radiance README, lm_head row of its file table: the head's
+ * weight quantized to fp8 per output channel, computed as a row-wise scaled
+ * GEMM with per-token fp8 activations):
+ *     acc[m,n] = sum_k e4m3(a[m,k]) * e4m3(w[n,k])             (fp32 accumulation)
+ *     y[m,n]   = epilogue(a_scale[m] * w_scale[n] * acc (+ bias[n]))  -> bf16
+ *   w_scale  [N] fp32, 16-byte aligned
+ *   Everything else as gemm_bs_fp8 (a per-tensor pair of scales is the case
+ *   of constant a_scale and w_scale vectors); workspace:
+ *   bs_workspace_bytes(2, M, N, K).
+ */
+int gemm_fp8_rowwise(const void *a_e4m3, int64_t ld_a, const float *a_scale,
+                     const void *w_e4m3, int64_t ld_w, const float *w_scale,
+                     const void *bias_bf16, int epilogue,
+                     void *y_bf16, int64_t ld_y,
+                     int64_t M, int64_t N, int64_t K,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Scratch bytes gemm_bs_fp8 (op 0), gemm_mxfp4_w4a8 (op 1) or
+ * gemm_fp8_rowwise (op 2) needs for this shape; 0 means none. Nonzero for 8 < M <= 64, where K is split across
  * workgroups and fp32 partial sums [S][M][N] go through the workspace
  * (S depends only on N and K). The workspace must then be 16-byte aligned;
  * its contents on entry do not matter (every byte read is written first by

@@ -19,8 +19,9 @@ import os
 
 import torch
 
-__all__ = ["fp8_quant_rows", "add_rms_norm_quant_fp8", "silu_mul_quant_fp8",
-           "gemm_bs_fp8", "gemm_mxfp4_w4a8", "bs_workspace_bytes",
+__all__ = ["fp8_quant_rows", "fp8_quant_rows_static", "add_rms_norm_quant_fp8",
+           "silu_mul_quant_fp8", "gemm_bs_fp8", "gemm_mxfp4_w4a8", "gemm_fp8_rowwise",
+           "bs_workspace_bytes",
            "bs_status_string", "BsError", "EPI_NONE", "EPI_BIAS", "EPI_BIAS_GELU_TANH",
            "weight_shape", "w_scale_shape", "library_path", "load_library",
            "EXPORTED_SYMBOLS"]
@@ -28,8 +29,9 @@ __all__ = ["fp8_quant_rows", "add_rms_norm_quant_fp8", "silu_mul_quant_fp8",
 EPI_NONE, EPI_BIAS, EPI_BIAS_GELU_TANH = 0, 1, 2
 BS_OK, BS_EINVAL, BS_EALIGN, BS_EARCH, BS_EWORKSPACE, BS_ELAUNCH = 0, -1, -2, -3, -4, -5
 
-EXPORTED_SYMBOLS = ("fp8_quant_rows", "add_rms_norm_quant_fp8", "silu_mul_quant_fp8",
-                    "gemm_bs_fp8", "gemm_mxfp4_w4a8", "bs_workspace_bytes", "bs_status_string")
+EXPORTED_SYMBOLS = ("fp8_quant_rows", "fp8_quant_rows_static", "add_rms_norm_quant_fp8",
+                    "silu_mul_quant_fp8", "gemm_bs_fp8", "gemm_mxfp4_w4a8", "gemm_fp8_rowwise",
+                    "bs_workspace_bytes", "bs_status_string")
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsgemm.so")
 _lib = None
@@ -66,6 +68,10 @@ def load_library():
         lib.gemm_bs_fp8.restype = i32
         lib.gemm_mxfp4_w4a8.argtypes = gemm
         lib.gemm_mxfp4_w4a8.restype = i32
+        lib.gemm_fp8_rowwise.argtypes = gemm
+        lib.gemm_fp8_rowwise.restype = i32
+        lib.fp8_quant_rows_static.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, vp]
+        lib.fp8_quant_rows_static.restype = i32
         lib.bs_workspace_bytes.argtypes = [i32, i64, i64, i64]
         lib.bs_workspace_bytes.restype = ctypes.c_size_t
         lib.bs_status_string.argtypes = [i32]
@@ -191,9 +197,9 @@ def silu_mul_quant_fp8(gate_up: torch.Tensor, q: torch.Tensor | None = None,
 
 
 def weight_shape(op: int, N: int, K: int) -> tuple:
-    """Byte shape of the weight operand: e4m3 [N, K] (op 0) or fp4 e2m1
-    packed two per byte [N, K/2] (op 1)."""
-    return (N, K) if op == 0 else (N, K // 2)
+    """Byte shape of the weight operand: e4m3 [N, K] (op 0, and op 2 with
+    per-channel scales) or fp4 e2m1 packed two per byte [N, K/2] (op 1)."""
+    return (N, K // 2) if op == 1 else (N, K)
 
 
 def w_scale_shape(op: int, N: int, K: int) -> tuple:
@@ -212,7 +218,11 @@ def _gemm(fn_name, op, a, a_scale, w, w_scale, bias, epilogue, y, workspace, str
     ldw = _matrix(w, "w", N, weight_shape(op, N, K)[1])
     if a_scale.dtype != torch.float32 or a_scale.shape != (M,) or not a_scale.is_contiguous():
         raise ValueError("a_scale must be a contiguous fp32 [M] tensor")
-    if w_scale.dtype != torch.uint8 or tuple(w_scale.shape) != w_scale_shape(op, N, K) \
+    if op == 2:
+        if w_scale.dtype != torch.float32 or tuple(w_scale.shape) != (N,) \
+                or not w_scale.is_contiguous():
+            raise ValueError("w_scale must be a contiguous fp32 [N] tensor")
+    elif w_scale.dtype != torch.uint8 or tuple(w_scale.shape) != w_scale_shape(op, N, K) \
             or not w_scale.is_contiguous():
         raise ValueError("w_scale must be a contiguous uint8 %s tensor"
                          % (w_scale_shape(op, N, K),))
@@ -243,6 +253,34 @@ def gemm_bs_fp8(a, a_scale, w, w_scale, bias=None, epilogue=EPI_NONE, y=None, wo
     """y [M, N] bf16 = epilogue(a_scale[m] * sum_k a[m,k] w[n,k] 2^(S[n/32,k/32]-127) (+ bias)).
     a: e4m3 [M, K]; w: e4m3 [N, K]; w_scale: uint8 E8M0 [N/32, K/32]."""
     return _gemm("gemm_bs_fp8", 0, a, a_scale, w, w_scale, bias, epilogue, y, workspace, stream)
+
+
+def gemm_fp8_rowwise(a, a_scale, w, w_scale, bias=None, epilogue=EPI_NONE, y=None,
+                     workspace=None, stream=None):
+    """y [M, N] bf16 = epilogue(a_scale[m] * w_scale[n] * sum_k a[m,k] w[n,k] (+ bias)).
+    a: e4m3 [M, K]; w: e4m3 [N, K]; w_scale: fp32 [N], one per output channel."""
+    return _gemm("gemm_fp8_rowwise", 2, a, a_scale, w, w_scale, bias, epilogue, y, workspace,
+                 stream)
+
+
+def fp8_quant_rows_static(x: torch.Tensor, scale: torch.Tensor, q: torch.Tensor | None = None,
+                          scale_out: torch.Tensor | None = None, stream=None):
+    """e4m3 codes of bf16 x [M, K] divided by one given scale (a device fp32
+    tensor of one element). Returns (q uint8 [M, K], scale_out fp32 [M] filled
+    with that scale)."""
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if scale.dtype != torch.float32 or scale.numel() != 1 or not scale.is_cuda:
+        raise ValueError("scale must be a one-element fp32 device tensor")
+    M, K = x.shape
+    ldx = _matrix(x, "x", M, K)
+    q, ldq, scale_out = _quant_outputs(q, scale_out, M, K, x.device)
+    st = load_library().fp8_quant_rows_static(_ptr(x), ldx, _ptr(scale), _ptr(q), ldq,
+                                              _ptr(scale_out), M, K,
+                                              ctypes.c_void_p(_stream(stream)))
+    if st != BS_OK:
+        raise BsError(st, "fp8_quant_rows_static")
+    return q, scale_out
 
 
 def gemm_mxfp4_w4a8(a, a_scale, w, w_scale, bias=None, epilogue=EPI_NONE, y=None,

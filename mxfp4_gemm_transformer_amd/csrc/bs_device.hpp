@@ -89,6 +89,12 @@ __device__ __forceinline__ float epilogue(float acc, float a_scale, float bias, 
     return epilogue_rest(a_scale * acc, bias, epi);
 }
 
+// With a per-output-channel weight scale cs (1 when the weights carry E8M0
+// block scales instead: the product is then exact).
+__device__ __forceinline__ float epilogue(float acc, float a_scale, float cs, float bias, int epi) {
+    return epilogue_rest(a_scale * acc * cs, bias, epi);
+}
+
 // ------------------------------------------------------ MFMA operand layout
 // V_MFMA_SCALE_F32_16X16X128_F8F6F4 (measured on gfx950):
 //   lane l = i + 16 g (i = row of A / column of B, g = 0..3).

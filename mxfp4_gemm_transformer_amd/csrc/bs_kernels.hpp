@@ -11,6 +11,11 @@ namespace bsg {
 hipError_t launch_quant_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_t ld_q,
                              float *scale, int64_t M, int64_t K, hipStream_t stream);
 
+// Quantization with one given scale (device scalar); scale_out [M] may be NULL.
+hipError_t launch_quant_rows_static(const uint16_t *x, int64_t ld_x, const float *scale_in,
+                                    uint8_t *q, int64_t ld_q, float *scale_out, int64_t M,
+                                    int64_t K, hipStream_t stream);
+
 // Fused producers (row width at most PRODUCER_MAX_K): RMSNorm with an
 // optional in-place residual add, or SiLU(gate) * up, then the quantizer.
 constexpr int64_t PRODUCER_MAX_K = 32768;
@@ -23,17 +28,19 @@ hipError_t launch_silu_mul_quant(const uint16_t *gate_up, int64_t ld_gu, uint8_t
 // M <= DECODE_MAX_M: the bandwidth-bound small-M GEMM.
 constexpr int64_t DECODE_MAX_M = 64;
 
+// `ws` is the E8M0 grid, or NULL for e4m3 weights with one fp32 scale per
+// output channel in `cs` (NULL otherwise): Y = s[m] cs[n] sum_k a w.
 // `workspace` holds decode_workspace_bytes(M, N, K) bytes (fp32 partial sums
 // of the split-K path, 8 < M <= 64), 16-byte aligned; unused otherwise.
 hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
-                              const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                              const uint8_t *w, int64_t ldw, const uint8_t *ws, const float *cs,
                               const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
                               int64_t N, int64_t K, void *workspace, int num_cus,
                               hipStream_t stream);
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_gemm_prefill(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
-                               const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                               const uint8_t *w, int64_t ldw, const uint8_t *ws, const float *cs,
                                const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
                                int64_t N, int64_t K, int num_cus, hipStream_t stream);
 

@@ -61,15 +61,20 @@ int check_gemm(const void *a, int64_t ld_a, const float *a_scale, const void *w,
     return BS_OK;
 }
 
+// `w_scale` is the E8M0 grid; `chan_scale` (e4m3 weights only) replaces it
+// with one fp32 scale per output channel when not NULL.
 int gemm_common(bool fp4, const void *a_e4m3, int64_t ld_a, const float *a_scale, const void *w,
-                int64_t ld_w, const uint8_t *w_scale, const void *bias_bf16, int epilogue,
-                void *y_bf16, int64_t ld_y, int64_t M, int64_t N, int64_t K, void *workspace,
-                size_t workspace_bytes, void *stream) {
+                int64_t ld_w, const uint8_t *w_scale, const float *chan_scale,
+                const void *bias_bf16, int epilogue, void *y_bf16, int64_t ld_y, int64_t M,
+                int64_t N, int64_t K, void *workspace, size_t workspace_bytes, void *stream) {
     const int64_t w_row = fp4 ? K / 2 : K;
     const size_t ws_need = bs_workspace_bytes(fp4 ? 1 : 0, M, N, K);
-    int st = check_gemm(a_e4m3, ld_a, a_scale, w, ld_w, w_row, w_scale, bias_bf16, epilogue,
-                        y_bf16, ld_y, M, N, K, workspace_bytes, ws_need);
+    int st = check_gemm(a_e4m3, ld_a, a_scale, w, ld_w, w_row,
+                        chan_scale ? reinterpret_cast<const uint8_t *>(chan_scale) : w_scale,
+                        bias_bf16, epilogue, y_bf16, ld_y, M, N, K, workspace_bytes, ws_need);
     if (st != BS_OK) return st;
+    if (chan_scale && !aligned16(chan_scale)) return BS_EALIGN;
+    if (chan_scale) w_scale = nullptr;
     if (ws_need && (!workspace || !aligned16(workspace)))
         return workspace ? BS_EALIGN : BS_EWORKSPACE;
     int num_cus = 0;
@@ -81,11 +86,11 @@ int gemm_common(bool fp4, const void *a_e4m3, int64_t ld_a, const float *a_scale
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (M <= bsg::DECODE_MAX_M)
-        e = bsg::launch_gemm_decode(fp4, a, ld_a, a_scale, wb, ld_w, w_scale, bias, epilogue, y,
-                                    ld_y, M, N, K, workspace, num_cus, s);
+        e = bsg::launch_gemm_decode(fp4, a, ld_a, a_scale, wb, ld_w, w_scale, chan_scale, bias,
+                                    epilogue, y, ld_y, M, N, K, workspace, num_cus, s);
     else
-        e = bsg::launch_gemm_prefill(fp4, a, ld_a, a_scale, wb, ld_w, w_scale, bias, epilogue, y,
-                                     ld_y, M, N, K, num_cus, s);
+        e = bsg::launch_gemm_prefill(fp4, a, ld_a, a_scale, wb, ld_w, w_scale, chan_scale, bias,
+                                     epilogue, y, ld_y, M, N, K, num_cus, s);
     return e == hipSuccess ? BS_OK : BS_ELAUNCH;
 }
 
@@ -153,16 +158,43 @@ int gemm_bs_fp8(const void *a_e4m3, int64_t ld_a, const float *a_scale, const vo
                 int64_t ld_w, const uint8_t *w_scale, const void *bias_bf16, int epilogue,
                 void *y_bf16, int64_t ld_y, int64_t M, int64_t N, int64_t K, void *workspace,
                 size_t workspace_bytes, void *stream) {
-    return gemm_common(false, a_e4m3, ld_a, a_scale, w_e4m3, ld_w, w_scale, bias_bf16, epilogue,
-                       y_bf16, ld_y, M, N, K, workspace, workspace_bytes, stream);
+    return gemm_common(false, a_e4m3, ld_a, a_scale, w_e4m3, ld_w, w_scale, nullptr, bias_bf16,
+                       epilogue, y_bf16, ld_y, M, N, K, workspace, workspace_bytes, stream);
 }
 
 int gemm_mxfp4_w4a8(const void *a_e4m3, int64_t ld_a, const float *a_scale, const void *w_fp4x2,
                     int64_t ld_w, const uint8_t *w_scale, const void *bias_bf16, int epilogue,
                     void *y_bf16, int64_t ld_y, int64_t M, int64_t N, int64_t K, void *workspace,
                     size_t workspace_bytes, void *stream) {
-    return gemm_common(true, a_e4m3, ld_a, a_scale, w_fp4x2, ld_w, w_scale, bias_bf16, epilogue,
-                       y_bf16, ld_y, M, N, K, workspace, workspace_bytes, stream);
+    return gemm_common(true, a_e4m3, ld_a, a_scale, w_fp4x2, ld_w, w_scale, nullptr, bias_bf16,
+                       epilogue, y_bf16, ld_y, M, N, K, workspace, workspace_bytes, stream);
+}
+
+int gemm_fp8_rowwise(const void *a_e4m3, int64_t ld_a, const float *a_scale, const void *w_e4m3,
+                     int64_t ld_w, const float *w_scale, const void *bias_bf16, int epilogue,
+                     void *y_bf16, int64_t ld_y, int64_t M, int64_t N, int64_t K, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    if (!w_scale) return BS_EINVAL;
+    return gemm_common(false, a_e4m3, ld_a, a_scale, w_e4m3, ld_w, nullptr, w_scale, bias_bf16,
+                       epilogue, y_bf16, ld_y, M, N, K, workspace, workspace_bytes, stream);
+}
+
+int fp8_quant_rows_static(const void *x_bf16, int64_t ld_x, const float *scale_in, void *q_e4m3,
+                          int64_t ld_q, float *scale_out, int64_t M, int64_t K, void *stream) {
+    if (!x_bf16 || !q_e4m3 || !scale_in) return BS_EINVAL;
+    if (M < 1 || K < 32 || K % 32 || M > INT32_MAX || K > INT32_MAX) return BS_EINVAL;
+    if (ld_x < K || ld_q < K) return BS_EINVAL;
+    if (!aligned16(x_bf16) || !aligned16(q_e4m3) || (2 * ld_x) % 16 || ld_q % 16)
+        return BS_EALIGN;
+    if ((reinterpret_cast<uintptr_t>(scale_in) & 3u) != 0) return BS_EALIGN;
+    if (scale_out && (reinterpret_cast<uintptr_t>(scale_out) & 3u) != 0) return BS_EALIGN;
+    int num_cus = 0;
+    int st = device_check(&num_cus);
+    if (st != BS_OK) return st;
+    hipError_t e = bsg::launch_quant_rows_static(static_cast<const uint16_t *>(x_bf16), ld_x,
+                                                 scale_in, static_cast<uint8_t *>(q_e4m3), ld_q,
+                                                 scale_out, M, K, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BS_OK : BS_ELAUNCH;
 }
 
 size_t bs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {

@@ -48,8 +48,8 @@ template <bool FP4, bool FOLD, int MT, int NW, int SPW>
 __global__ __launch_bounds__(NW * 64) void gemm_decode_kernel(
     const uint8_t *__restrict__ A, int64_t lda, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ W, int64_t ldw, const uint8_t *__restrict__ WS,
-    const uint16_t *__restrict__ bias, int epi, uint16_t *__restrict__ Y, int64_t ldy, int M,
-    int K) {
+    const float *__restrict__ colscale, const uint16_t *__restrict__ bias, int epi,
+    uint16_t *__restrict__ Y, int64_t ldy, int M, int K) {
     constexpr int COLS = FOLD ? 8 : 16;
     constexpr int ROWS = FOLD ? 8 : 16 * MT;
     constexpr int KSTEP = FOLD ? 256 : 128;
@@ -68,12 +68,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_decode_kernel(
     // the epilogue's per-token scales and bias, fetched first so that the
     // epilogue waits for no global load (entries idx = tid, tid + NW*64)
     constexpr int EPI_IT = (ROWS * COLS + NW * 64 - 1) / (NW * 64);
-    float ep_as[EPI_IT], ep_b[EPI_IT];
+    float ep_as[EPI_IT], ep_b[EPI_IT], ep_cs[EPI_IT];
     {
         const __amdgpu_buffer_rsrc_t rsT = make_rsrc(a_scale, (int64_t)M * 4);
         const __amdgpu_buffer_rsrc_t rsB =
             epi != EPI_NONE ? make_rsrc(bias + (int64_t)blockIdx.x * COLS, COLS * 2)
                             : make_rsrc(bias, 0);
+        const __amdgpu_buffer_rsrc_t rsC =
+            colscale ? make_rsrc(colscale + (int64_t)blockIdx.x * COLS, COLS * 4)
+                     : make_rsrc(colscale, 0);
 #pragma unroll
         for (int it = 0; it < EPI_IT; ++it) {
             const int idx = threadIdx.x + it * NW * 64;
@@ -83,6 +86,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_decode_kernel(
                 rsT, (ok & (r < M)) ? (uint32_t)(4 * r) : OOB_OFF, 0, 0));
             ep_b[it] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
                 rsB, ok ? (uint32_t)(2 * c) : OOB_OFF, 0, 0));
+            const float cs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rsC, ok ? (uint32_t)(4 * c) : OOB_OFF, 0, 0));
+            ep_cs[it] = colscale ? cs : 1.0f;
         }
     }
 
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_decode_kernel(
             } else {
                 if (on && klo < K) lo = ldg16(wrow + klo);
                 if (on && khi < K) hi = ldg16(wrow + khi);
-                if (on && kblk < K) sc = wsrow[kblk >> 5];
+                if (on && kblk < K && WS) sc = wsrow[kblk >> 5];   // no WS: per-channel scales
             }
             wv[u] = pack8(lo, hi);
             wsc[u] = sc;
@@ -158,18 +164,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_decode_kernel(
 #pragma unroll
             for (int w = 0; w < NW; ++w) sum += red[w][r][c];
             const int64_t nn = (int64_t)blockIdx.x * COLS + c;
-            Y[(int64_t)r * ldy + nn] = (uint16_t)f32_to_bf16(epilogue(sum, ep_as[it], ep_b[it], epi));
+            Y[(int64_t)r * ldy + nn] =
+                (uint16_t)f32_to_bf16(epilogue(sum, ep_as[it], ep_cs[it], ep_b[it], epi));
         }
     }
 }
 
 template <bool FP4, bool FOLD, int MT, int NW, int SPW>
 void launch_one(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w, int64_t ldw,
-                const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y, int64_t ldy,
-                int64_t M, int64_t N, int64_t K, hipStream_t st) {
+                const uint8_t *ws, const float *cs, const uint16_t *bias, int epi, uint16_t *y,
+                int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t st) {
     constexpr int COLS = FOLD ? 8 : 16;
     hipLaunchKernelGGL((gemm_decode_kernel<FP4, FOLD, MT, NW, SPW>), dim3((unsigned)(N / COLS)),
-                       dim3(NW * 64), 0, st, a, lda, as, w, ldw, ws, bias, epi, y, ldy, (int)M,
+                       dim3(NW * 64), 0, st, a, lda, as, w, ldw, ws, cs, bias, epi, y, ldy, (int)M,
                        (int)K);
 }
 
@@ -177,19 +184,19 @@ void launch_one(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w
 // fits (at most 8 weight fragments, and at most 8 fragments x M-tiles).
 template <bool FP4, bool FOLD, int MT>
 void launch_spw(int per_wave, const uint8_t *a, int64_t lda, const float *as, const uint8_t *w,
-                int64_t ldw, const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y,
-                int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+                int64_t ldw, const uint8_t *ws, const float *cs, const uint16_t *bias, int epi,
+                uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t st) {
     constexpr int NW = 8;
     constexpr int CAP = 8 / MT;
     if (per_wave <= 1 || CAP == 1)
-        launch_one<FP4, FOLD, MT, NW, 1>(a, lda, as, w, ldw, ws, bias, epi, y, ldy, M, N, K, st);
+        launch_one<FP4, FOLD, MT, NW, 1>(a, lda, as, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
     else if (per_wave <= 2 || CAP == 2)
-        launch_one<FP4, FOLD, MT, NW, 2>(a, lda, as, w, ldw, ws, bias, epi, y, ldy, M, N, K, st);
+        launch_one<FP4, FOLD, MT, NW, 2>(a, lda, as, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
     else if (per_wave <= 4 || CAP == 4)
-        launch_one<FP4, FOLD, MT, NW, (CAP >= 4 ? 4 : 1)>(a, lda, as, w, ldw, ws, bias, epi, y,
+        launch_one<FP4, FOLD, MT, NW, (CAP >= 4 ? 4 : 1)>(a, lda, as, w, ldw, ws, cs, bias, epi, y,
                                                           ldy, M, N, K, st);
     else
-        launch_one<FP4, FOLD, MT, NW, (CAP >= 8 ? 8 : 1)>(a, lda, as, w, ldw, ws, bias, epi, y,
+        launch_one<FP4, FOLD, MT, NW, (CAP >= 8 ? 8 : 1)>(a, lda, as, w, ldw, ws, cs, bias, epi, y,
                                                           ldy, M, N, K, st);
 }
 
@@ -217,11 +224,12 @@ struct UnitsLds {
     __host__ __device__ static int scale_rows(int gpw) { return FP4 ? 8 * gpw : (8 * gpw + 31) / 32 + 1; }
     // then the sums: one slot per group (groups a wave covers whole) and
     // two per wave (its first and last group, when cut between waves)
-    // and the per-token scales and the bias of the workgroup's rows
+    // and the per-token scales, the bias and the per-channel scales of the
+    // workgroup's rows
     static size_t bytes(int K, int gpw) {
         return a_bytes(K) + (size_t)scale_rows(gpw) * (K / 32) +
                (size_t)(gpw + UNIT_WAVES * 2) * 64 * MT * sizeof(float) +
-               (size_t)(TOK + 8 * gpw) * sizeof(float);
+               (size_t)(TOK + 16 * gpw) * sizeof(float);
     }
 };
 
@@ -229,8 +237,8 @@ template <bool FP4, int MT, int P>
 __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
     const uint8_t *__restrict__ A, int64_t lda, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ W, int64_t ldw, const uint8_t *__restrict__ WS,
-    const uint16_t *__restrict__ bias, int epi, uint16_t *__restrict__ Y, int64_t ldy, int M,
-    int N, int K, int gpw) {
+    const float *__restrict__ colscale, const uint16_t *__restrict__ bias, int epi,
+    uint16_t *__restrict__ Y, int64_t ldy, int M, int N, int K, int gpw) {
     using L = UnitsLds<FP4, MT>;
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int KSTEP = 256;
@@ -257,6 +265,7 @@ __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
     float *part = gsum + gpw * PE;
     float *tok_scale = part + UNIT_WAVES * 2 * PE;   // [TOK]
     float *row_bias = tok_scale + TOK;               // [8 gpw]
+    float *row_cs = row_bias + 8 * gpw;              // [8 gpw] per-channel scales (1 if none)
 
     // ---- activations and scales into registers first, then the weights,
     // then the LDS writes (which wait only for the first two groups of
@@ -264,8 +273,9 @@ __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
     // buffer's range return zeros), issued unconditionally, so the compiler
     // counts them exactly and waits for no more than it needs.
     const __amdgpu_buffer_rsrc_t rsA = make_rsrc(A, (int64_t)M * lda);
+    // no WS (per-channel scales): an empty range, every scale reads as 0
     const __amdgpu_buffer_rsrc_t rsS =
-        make_rsrc(WS + (int64_t)srow0 * KB, (int64_t)nsrows * KB);
+        WS ? make_rsrc(WS + (int64_t)srow0 * KB, (int64_t)nsrows * KB) : make_rsrc(WS, 0);
     const __amdgpu_buffer_rsrc_t rsW = make_rsrc(W + (int64_t)row0 * ldw, (int64_t)ng * 8 * ldw);
     constexpr int ACH = 8 * MT * 8192 / 16 / 1024;   // 16-byte chunks per thread for K <= 8192
     const int kc = K >> 4, chunks = TOK * kc;
@@ -279,9 +289,11 @@ __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
     // the epilogue's per-token scales and bias, fetched now so that the
     // epilogue waits for no global load (one value per thread at most)
     // (range-checked buffer loads: branch-free, so the compiler counts them)
-    float ep_val;
+    float ep_val, ep_cs;
     {
         const __amdgpu_buffer_rsrc_t rsT = make_rsrc(a_scale, (int64_t)M * 4);
+        const __amdgpu_buffer_rsrc_t rsC =
+            colscale ? make_rsrc(colscale + row0, (int64_t)(N - row0) * 4) : make_rsrc(colscale, 0);
         // bias of this workgroup's rows (no bias: an empty range, nothing read)
         const __amdgpu_buffer_rsrc_t rsB =
             epi != EPI_NONE ? make_rsrc(bias + row0, (int64_t)(N - row0) * 2) : make_rsrc(bias, 0);
@@ -291,6 +303,9 @@ __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
         const uint32_t bb = __builtin_amdgcn_raw_buffer_load_b16(
             rsB, ((t >= TOK) & (t < TOK + 8 * ng)) ? (uint32_t)(2 * (t - TOK)) : OOB_OFF, 0, 0);
         ep_val = t < TOK ? __uint_as_float(ts) : bf16_to_f32(bb);
+        const uint32_t cw = __builtin_amdgcn_raw_buffer_load_b32(
+            rsC, t < 8 * ng ? (uint32_t)(4 * t) : OOB_OFF, 0, 0);
+        ep_cs = colscale ? __uint_as_float(cw) : 1.0f;
     }
     const int words = nsrows * (KB >> 2);
     constexpr int SCW = 8;                           // scale words per thread (the launcher checks the bound)
@@ -341,6 +356,7 @@ __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
         if (c < words) *reinterpret_cast<uint32_t *>(s_lds + 4 * c) = sv[j];
     }
     if (threadIdx.x < TOK + 8 * ng) tok_scale[threadIdx.x] = ep_val;   // row_bias follows tok_scale
+    if (threadIdx.x < 8 * ng) row_cs[threadIdx.x] = ep_cs;
     __syncthreads();
 
     // ---- this wave's units; a group's sum is flushed when the next group
@@ -379,7 +395,7 @@ __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
             const int k0 = cst * KSTEP + half * 128;
             const int kblk = k0 + 32 * g, klo = k0 + 16 * g, khi = k0 + 64 + 16 * g;
             const int srl = FP4 ? cgl * 8 + col : ((row0 + cgl * 8 + col) >> 5) - srow0;
-            const int sc = kblk < K ? s_lds[srl * KB + (kblk >> 5)] : E8M0_ONE;
+            const int sc = (kblk < K) & (WS != nullptr) ? s_lds[srl * KB + (kblk >> 5)] : E8M0_ONE;
             const v8i wv = pack8(wlo[q % WIN], FP4 ? make_uint4(0u, 0u, 0u, 0u) : whi[FP4 ? 0 : q % WIN]);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -415,20 +431,20 @@ __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
         const int m = e / 8, r = e % 8;
         if (m >= M) continue;
         const int64_t nn = (int64_t)row0 + gl * 8 + r;
-        Y[(int64_t)m * ldy + nn] =
-            (uint16_t)f32_to_bf16(epilogue(sum, tok_scale[m], row_bias[gl * 8 + r], epi));
+        Y[(int64_t)m * ldy + nn] = (uint16_t)f32_to_bf16(
+            epilogue(sum, tok_scale[m], row_cs[gl * 8 + r], row_bias[gl * 8 + r], epi));
     }
 }
 
 template <bool FP4, int MT, int P>
 void launch_units(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w, int64_t ldw,
-                  const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y, int64_t ldy,
-                  int64_t M, int64_t N, int64_t K, int gpw, hipStream_t st) {
+                  const uint8_t *ws, const float *cs, const uint16_t *bias, int epi, uint16_t *y,
+                  int64_t ldy, int64_t M, int64_t N, int64_t K, int gpw, hipStream_t st) {
     const size_t lds = UnitsLds<FP4, MT>::bytes((int)K, gpw);
     const int64_t groups = N / 8;
     hipLaunchKernelGGL((gemm_decode_units_kernel<FP4, MT, P>),
                        dim3((unsigned)((groups + gpw - 1) / gpw)), dim3(1024), lds, st, a, lda, as,
-                       w, ldw, ws, bias, epi, y, ldy, (int)M, (int)N, (int)K, gpw);
+                       w, ldw, ws, cs, bias, epi, y, ldy, (int)M, (int)N, (int)K, gpw);
 }
 
 
@@ -488,8 +504,9 @@ __global__ __launch_bounds__(256) void gemm_decode_splitk_kernel(
     // ---- this wave's weights: SPLIT_MAX_STEPS steps (16x16x128 B operand)
     const __amdgpu_buffer_rsrc_t rsW = make_rsrc(W + (int64_t)row0 * ldw, (int64_t)(N - row0) * ldw);
     const __amdgpu_buffer_rsrc_t rsS =
-        FP4 ? make_rsrc(WS + (int64_t)row0 * KB, (int64_t)(N - row0) * KB)
-            : make_rsrc(WS + (int64_t)(row0 >> 5) * KB, (int64_t)((N >> 5) - (row0 >> 5)) * KB);
+        !WS ? make_rsrc(WS, 0)   // per-channel scales: no E8M0 bytes
+        : FP4 ? make_rsrc(WS + (int64_t)row0 * KB, (int64_t)(N - row0) * KB)
+              : make_rsrc(WS + (int64_t)(row0 >> 5) * KB, (int64_t)((N >> 5) - (row0 >> 5)) * KB);
     const uint32_t wrow = (uint32_t)((16 * wave + i) * ldw);
     const uint32_t srow = (uint32_t)((FP4 ? (16 * wave + i) : ((n >> 5) - (row0 >> 5))) * KB);
     uint4 wlo[SPLIT_MAX_STEPS], whi[FP4 ? 1 : SPLIT_MAX_STEPS];
@@ -531,7 +548,7 @@ __global__ __launch_bounds__(256) void gemm_decode_splitk_kernel(
                 const uint8_t *arow = lds + (mt * 16 + i) * lds_row + kl;
                 const v8i a8 = pack8(*reinterpret_cast<const uint4 *>(arow + 16 * g),
                                      *reinterpret_cast<const uint4 *>(arow + 64 + 16 * g));
-                acc[mt] = mfma16<FP4>(a8, wv, acc[mt], E8M0_ONE, (int)wsc[u]);
+                acc[mt] = mfma16<FP4>(a8, wv, acc[mt], E8M0_ONE, WS ? (int)wsc[u] : E8M0_ONE);
             }
         }
     }
@@ -551,6 +568,7 @@ __global__ __launch_bounds__(256) void gemm_decode_splitk_kernel(
 // four columns per thread, eight slices' loads in flight before their adds.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part,
                                                             const float *__restrict__ a_scale,
+                                                            const float *__restrict__ colscale,
                                                             const uint16_t *__restrict__ bias,
                                                             int epi, uint16_t *__restrict__ Y,
                                                             int64_t ldy, int M, int N, int S) {
@@ -578,16 +596,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
         bq = make_float4(bf16_to_f32(bias[c0]), bf16_to_f32(bias[c0 + 1]),
                          bf16_to_f32(bias[c0 + 2]), bf16_to_f32(bias[c0 + 3]));
     const float as = a_scale[t];
-    const uint32_t o01 = pack_bf16x2(epilogue(sum.x, as, bq.x, epi), epilogue(sum.y, as, bq.y, epi));
-    const uint32_t o23 = pack_bf16x2(epilogue(sum.z, as, bq.z, epi), epilogue(sum.w, as, bq.w, epi));
+    const float4 cq = colscale ? *reinterpret_cast<const float4 *>(colscale + c0)
+                               : make_float4(1.f, 1.f, 1.f, 1.f);
+    const uint32_t o01 = pack_bf16x2(epilogue(sum.x, as, cq.x, bq.x, epi),
+                                     epilogue(sum.y, as, cq.y, bq.y, epi));
+    const uint32_t o23 = pack_bf16x2(epilogue(sum.z, as, cq.z, bq.z, epi),
+                                     epilogue(sum.w, as, cq.w, bq.w, epi));
     *reinterpret_cast<uint2 *>(Y + (int64_t)t * ldy + c0) = make_uint2(o01, o23);
 }
 
 template <bool FP4, int MT>
 hipError_t launch_splitk(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w,
-                         int64_t ldw, const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y,
-                         int64_t ldy, int64_t M, int64_t N, int64_t K, float *part,
-                         hipStream_t st) {
+                         int64_t ldw, const uint8_t *ws, const float *cs, const uint16_t *bias,
+                         int epi, uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                         float *part, hipStream_t st) {
     const int64_t S = decode_splits(N, K);
     const int64_t steps = (K + 127) / 128, per = (steps + S - 1) / S;
     const size_t lds = (size_t)16 * MT * (per * 128 + 16);
@@ -595,14 +617,14 @@ hipError_t launch_splitk(const uint8_t *a, int64_t lda, const float *as, const u
                        dim3(256), lds, st, a, lda, w, ldw, ws, part, (int)M, (int)N, (int)K, (int)S);
     const int64_t quads = M * N / 4;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st,
-                       part, as, bias, epi, y, ldy, (int)M, (int)N, (int)S);
+                       part, as, cs, bias, epi, y, ldy, (int)M, (int)N, (int)S);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
-                              const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                              const uint8_t *w, int64_t ldw, const uint8_t *ws, const float *cs,
                               const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
                               int64_t N, int64_t K, void *workspace, int num_cus, hipStream_t st) {
     constexpr int NW = 8;
@@ -625,11 +647,11 @@ hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const flo
         const int64_t scale_words = (fp4 ? 8 * gpw : (8 * gpw + 31) / 32 + 1) * (K / 128);
         if (upw <= (fp4 ? 32 : 16) && (fp4 ? lds : lds8) <= 160 * 1024 && scale_words <= 8 * 1024) {
 #define BSG_UNITS(FP4_, MT_)                                                                       \
-    if (upw <= 4) launch_units<FP4_, MT_, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, gpw, st); \
-    else if (upw <= 8) launch_units<FP4_, MT_, 8>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, gpw, st); \
-    else if (upw <= 16) launch_units<FP4_, MT_, 16>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, gpw, st); \
-    else if (upw <= 24) launch_units<true, MT_, 24>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, gpw, st); \
-    else launch_units<true, MT_, 32>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, gpw, st);
+    if (upw <= 4) launch_units<FP4_, MT_, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st); \
+    else if (upw <= 8) launch_units<FP4_, MT_, 8>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st); \
+    else if (upw <= 16) launch_units<FP4_, MT_, 16>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st); \
+    else if (upw <= 24) launch_units<true, MT_, 24>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st); \
+    else launch_units<true, MT_, 32>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st);
             if (fp4) { if (mt == 1) { BSG_UNITS(true, 1) } else { BSG_UNITS(true, 2) } }
             else { if (mt == 1) { BSG_UNITS(false, 1) } else { BSG_UNITS(false, 2) } }
 #undef BSG_UNITS
@@ -639,22 +661,22 @@ hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const flo
     if (M <= 8) {
         const int per = (int)(((K + 255) / 256 + NW - 1) / NW);
         if (fp4)
-            launch_spw<true, true, 1>(per, a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, st);
+            launch_spw<true, true, 1>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
         else
-            launch_spw<false, true, 1>(per, a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, st);
+            launch_spw<false, true, 1>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
         return hipGetLastError();
     }
     // 8 < M <= 64: split K over workgroups, partial sums in the workspace
     float *part = static_cast<float *>(workspace);
     switch ((M + 15) / 16) {
-    case 1: return fp4 ? launch_splitk<true, 1>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st)
-                       : launch_splitk<false, 1>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st);
-    case 2: return fp4 ? launch_splitk<true, 2>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st)
-                       : launch_splitk<false, 2>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st);
-    case 3: return fp4 ? launch_splitk<true, 3>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st)
-                       : launch_splitk<false, 3>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st);
-    default: return fp4 ? launch_splitk<true, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st)
-                        : launch_splitk<false, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, part, st);
+    case 1: return fp4 ? launch_splitk<true, 1>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, part, st)
+                       : launch_splitk<false, 1>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, part, st);
+    case 2: return fp4 ? launch_splitk<true, 2>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, part, st)
+                       : launch_splitk<false, 2>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, part, st);
+    case 3: return fp4 ? launch_splitk<true, 3>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, part, st)
+                       : launch_splitk<false, 3>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, part, st);
+    default: return fp4 ? launch_splitk<true, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, part, st)
+                        : launch_splitk<false, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, part, st);
     }
 }
 

@@ -81,8 +81,8 @@ template <bool FP4, int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
     const uint8_t *__restrict__ A, int64_t lda, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ W, int64_t ldw, const uint8_t *__restrict__ WS,
-    const uint16_t *__restrict__ bias, int epi, uint16_t *__restrict__ Y, int64_t ldy, int M, int N,
-    int K, int group_m) {
+    const float *__restrict__ colscale, const uint16_t *__restrict__ bias, int epi,
+    uint16_t *__restrict__ Y, int64_t ldy, int M, int N, int K, int group_m) {
     using C = Cfg<FP4, BM, BN, WGM, WGN>;
     static_assert(C::NT == 256, "launch bounds assume four waves");
     __shared__ __align__(16) uint8_t lds[C::NBUF * C::STAGE_ALL];
@@ -116,10 +116,11 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
     // the scale rows of this tile: [N/32, KB] for e4m3 weights, [N, KB] for
     // MXFP4; rows past the end and K blocks past KB read as zero (a zero
     // E8M0 byte scales zero data there)
+    // (no WS: per-channel fp32 scales instead, an empty range here)
     const int srow0 = FP4 ? n0 : (n0 >> 5);
-    const int64_t s_bytes = (int64_t)((FP4 ? N : (N >> 5)) - srow0) * KB;
+    const int64_t s_bytes = WS ? (int64_t)((FP4 ? N : (N >> 5)) - srow0) * KB : 0;
     const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(WS + (int64_t)srow0 * KB), (short)0,
+        (void *)(WS ? WS + (int64_t)srow0 * KB : WS), (short)0,
         (int)(s_bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : s_bytes), 0x00020000);
     const uint32_t s_off = (uint32_t)(tid * KB);   // this thread's scale row
 
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
                 const int fz = swz4(row);
                 const uint8_t *base = sw + row * C::WROW;
                 f.b[b] = pack8(lds16(base + 16 * (lg ^ fz)), lds16(base + 16 * ((2 + lg) ^ fz)));
-                f.sc[b] = ss[2 * (row >> 5) + lg];
+                f.sc[b] = WS ? ss[2 * (row >> 5) + lg] : E8M0_ONE;
             }
         }
     };
@@ -294,16 +295,20 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
             for (int q = 0; q < 4; ++q) {
                 const int n = n0 + wn * (BN / WGN) + b * 32 + 8 * q + 4 * lg;
                 if (n >= N) continue;
-                float bv[4] = {0.f, 0.f, 0.f, 0.f};
+                float bv[4] = {0.f, 0.f, 0.f, 0.f}, cv[4] = {1.f, 1.f, 1.f, 1.f};
                 if (epi != EPI_NONE) {  // bias is only 2-byte aligned
 #pragma unroll
                     for (int j = 0; j < 4; ++j) bv[j] = bf16_to_f32(bias[n + j]);
                 }
-                uint32_t h[4];
+                if (colscale) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    h[j] = f32_to_bf16(epilogue(acc[a][b][4 * q + j], as, bv[j], epi));
-                *reinterpret_cast<uint2 *>(yrow + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                    for (int j = 0; j < 4; ++j) cv[j] = colscale[n + j];
+                }
+                float o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = epilogue(acc[a][b][4 * q + j], as, cv[j], bv[j], epi);
+                *reinterpret_cast<uint2 *>(yrow + n) =
+                    make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
             }
         }
     }
@@ -311,13 +316,14 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
 
 template <bool FP4, int BM, int BN, int WGM, int WGN>
 hipError_t launch_tile(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w,
-                       int64_t ldw, const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y,
-                       int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+                       int64_t ldw, const uint8_t *ws, const float *cs, const uint16_t *bias,
+                       int epi, uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                       hipStream_t st) {
     using C = Cfg<FP4, BM, BN, WGM, WGN>;
     auto kern = gemm_prefill_kernel<FP4, BM, BN, WGM, WGN>;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(C::NT), 0, st, a, lda, as, w, ldw, ws,
-                       bias, epi, y, ldy, (int)M, (int)N, (int)K, 8);
+                       cs, bias, epi, y, ldy, (int)M, (int)N, (int)K, 8);
     return hipGetLastError();
 }
 
@@ -388,7 +394,8 @@ struct DCfg {
     static constexpr int EP_ROW = TN * 32 * 4 + 16;
     static constexpr int EP_WAVE = 32 * EP_ROW;
     static constexpr int EP_BIAS = NW * EP_WAVE;      // then each wave's TN*32 bias values
-    static constexpr int EP_ALL = EP_BIAS + NW * TN * 32 * 4;
+    static constexpr int EP_CS = EP_BIAS + NW * TN * 32 * 4;   // and per-channel scales
+    static constexpr int EP_ALL = EP_CS + NW * TN * 32 * 4;
     static constexpr int LDS = NBUF * STAGE > EP_ALL ? NBUF * STAGE : EP_ALL;
     static_assert(A_STAGE % (16 * NT) == 0 && W_STAGE % (16 * NT) == 0, "stage split");
     static_assert(SC_ROWS <= NT, "one scale row per thread");
@@ -401,8 +408,8 @@ template <bool FP4, int BM, int BN, int NBUF, int WGM, int WGN>
 __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     const uint8_t *__restrict__ A, int64_t lda, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ W, int64_t ldw, const uint8_t *__restrict__ WS,
-    const uint16_t *__restrict__ bias, int epi, uint16_t *__restrict__ Y, int64_t ldy, int M, int N,
-    int K, int group_m) {
+    const float *__restrict__ colscale, const uint16_t *__restrict__ bias, int epi,
+    uint16_t *__restrict__ Y, int64_t ldy, int M, int N, int K, int group_m) {
     using C = DCfg<FP4, BM, BN, NBUF, WGM, WGN>;
     __shared__ __align__(16) uint8_t lds[C::LDS];
 
@@ -431,9 +438,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         (void *)(W + (int64_t)n0 * ldw), (short)0, (int)(w_bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : w_bytes),
         0x00020000);
     const int srow0 = FP4 ? n0 : (n0 >> 5);
-    const int64_t s_bytes = (int64_t)((FP4 ? N : (N >> 5)) - srow0) * KB;
+    const int64_t s_bytes = WS ? (int64_t)((FP4 ? N : (N >> 5)) - srow0) * KB : 0;   // no WS: empty
     const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(WS + (int64_t)srow0 * KB), (short)0,
+        (void *)(WS ? WS + (int64_t)srow0 * KB : WS), (short)0,
         (int)(s_bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : s_bytes), 0x00020000);
 
     // This thread's 16-byte chunk of each load: physical chunk j*NT + tid of
@@ -509,7 +516,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
             const int fz = swz4(row);
             const uint8_t *p = sw + row * C::WROW;
             f.b[b] = pack8(lds16(p + 16 * (lg ^ fz)), lds16(p + 16 * ((2 + lg) ^ fz)));
-            f.sc[b] = ss[4 * (row >> 5) + lg];
+            f.sc[b] = WS ? ss[4 * (row >> 5) + lg] : E8M0_ONE;   // no WS: per-channel scales
         }
     };
     // The loads of a step go one before each fragment read, so that with the
@@ -585,15 +592,18 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     wait_loads_and_barrier<0>();
     uint8_t *slab = lds + wave * C::EP_WAVE;
     float *bias_w = reinterpret_cast<float *>(lds + C::EP_BIAS) + wave * C::TN * 32;
+    float *cs_w = reinterpret_cast<float *>(lds + C::EP_CS) + wave * C::TN * 32;
     constexpr int WCOLS = C::TN * 32;               // the wave's columns
     constexpr int CPR = WCOLS / 4;                  // 4-column chunks per slab row
     const int ncol0 = n0 + wn * (BN / WGN);         // the wave's first column
 #pragma unroll
-    for (int c = lane; c < WCOLS; c += 64) {        // bias of the wave's columns (0 past N)
+    for (int c = lane; c < WCOLS; c += 64) {        // bias and channel scale of the wave's columns
         const int n = ncol0 + c;
-        float bv = 0.f;
+        float bv = 0.f, cv = 1.f;
         if ((epi != EPI_NONE) & (n < N)) bv = bf16_to_f32(bias[n]);
+        if (colscale && (n < N)) cv = colscale[n];
         bias_w[c] = bv;
+        cs_w[c] = cv;
     }
     float asv[C::TM];
 #pragma unroll
@@ -623,8 +633,11 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
             const int rr = ch / CPR, cc = 4 * (ch % CPR);
             const float4 v = *reinterpret_cast<const float4 *>(slab + rr * C::EP_ROW + 4 * cc);
             const float4 bv = *reinterpret_cast<const float4 *>(bias_w + cc);
-            const uint32_t h01 = pack_bf16x2(epilogue_rest(v.x, bv.x, epi), epilogue_rest(v.y, bv.y, epi));
-            const uint32_t h23 = pack_bf16x2(epilogue_rest(v.z, bv.z, epi), epilogue_rest(v.w, bv.w, epi));
+            const float4 cv = *reinterpret_cast<const float4 *>(cs_w + cc);
+            const uint32_t h01 = pack_bf16x2(epilogue_rest(v.x * cv.x, bv.x, epi),
+                                             epilogue_rest(v.y * cv.y, bv.y, epi));
+            const uint32_t h23 = pack_bf16x2(epilogue_rest(v.z * cv.z, bv.z, epi),
+                                             epilogue_rest(v.w * cv.w, bv.w, epi));
             const int m = mrow + rr, n = ncol0 + cc;
             if (m < M && n < N)
                 *reinterpret_cast<uint2 *>(Y + (int64_t)m * ldy + n) = make_uint2(h01, h23);
@@ -635,13 +648,13 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
 
 template <bool FP4, int BM, int BN, int NBUF, int WGM = 2, int WGN = 2>
 hipError_t launch_tile_dma(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w,
-                           int64_t ldw, const uint8_t *ws, const uint16_t *bias, int epi,
-                           uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                           int64_t ldw, const uint8_t *ws, const float *cs, const uint16_t *bias,
+                           int epi, uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                            hipStream_t st) {
     auto kern = gemm_prefill_dma_kernel<FP4, BM, BN, NBUF, WGM, WGN>;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(WGM * WGN * 64), 0, st, a, lda, as, w,
-                       ldw, ws, bias, epi, y, ldy, (int)M, (int)N, (int)K, 8);
+                       ldw, ws, cs, bias, epi, y, ldy, (int)M, (int)N, (int)K, 8);
     return hipGetLastError();
 }
 
@@ -676,27 +689,27 @@ int best_shape(bool fp4, int64_t M, int64_t N, int64_t K, int num_cus, double *c
 }
 
 hipError_t launch_shape(int shape, bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
-                        const uint8_t *w, int64_t ldw, const uint8_t *ws, const uint16_t *bias,
-                        int epi, uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
-                        hipStream_t st) {
+                        const uint8_t *w, int64_t ldw, const uint8_t *ws, const float *cs,
+                        const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
+                        int64_t N, int64_t K, hipStream_t st) {
     switch (shape) {
     case 0:
         // MXFP4 weights: eight waves (4 x 2, each 64 x 128) measured faster
         // than four for 256x256 tiles; e4m3 weights: four
         if (fp4)
-            return launch_tile_dma<true, 256, 256, 4, 4, 2>(a, lda, a_scale, w, ldw, ws, bias, epi,
+            return launch_tile_dma<true, 256, 256, 4, 4, 2>(a, lda, a_scale, w, ldw, ws, cs, bias, epi,
                                                             y, ldy, M, N, K, st);
-        return launch_tile_dma<false, 256, 256, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy,
+        return launch_tile_dma<false, 256, 256, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy,
                                                    M, N, K, st);
     case 1:
-        return fp4 ? launch_tile_dma<true, 256, 128, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y,
+        return fp4 ? launch_tile_dma<true, 256, 128, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y,
                                                         ldy, M, N, K, st)
-                   : launch_tile_dma<false, 256, 128, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y,
+                   : launch_tile_dma<false, 256, 128, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y,
                                                          ldy, M, N, K, st);
     default:
-        return fp4 ? launch_tile_dma<true, 128, 128, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y,
+        return fp4 ? launch_tile_dma<true, 128, 128, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y,
                                                         ldy, M, N, K, st)
-                   : launch_tile_dma<false, 128, 128, 4>(a, lda, a_scale, w, ldw, ws, bias, epi, y,
+                   : launch_tile_dma<false, 128, 128, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y,
                                                          ldy, M, N, K, st);
     }
 }
@@ -706,7 +719,7 @@ hipError_t launch_shape(int shape, bool fp4, const uint8_t *a, int64_t lda, cons
 // cheapest shape over the rest (a last round that 256x256 tiles would leave
 // part idle can be filled by smaller tiles). The two write disjoint columns.
 hipError_t launch_prefill_dma(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
-                              const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                              const uint8_t *w, int64_t ldw, const uint8_t *ws, const float *cs,
                               const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
                               int64_t N, int64_t K, int num_cus, hipStream_t st) {
     double one_cost = 0.0;
@@ -720,37 +733,38 @@ hipError_t launch_prefill_dma(bool fp4, const uint8_t *a, int64_t lda, const flo
         double c2 = 0.0;
         const int two = best_shape(fp4, M, N - n1, K, num_cus, &c2);
         if (c1 + c2 + LAUNCH_COST < one_cost) {
-            hipError_t e = launch_shape(0, fp4, a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M,
-                                        n1, K, st);
+            hipError_t e = launch_shape(0, fp4, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy,
+                                        M, n1, K, st);
             if (e != hipSuccess) return e;
             const int64_t kb = K / 32;
             const uint8_t *w2 = w + n1 * ldw;
-            const uint8_t *ws2 = ws + (fp4 ? n1 * kb : (n1 / 32) * kb);
+            const uint8_t *ws2 = ws ? ws + (fp4 ? n1 * kb : (n1 / 32) * kb) : nullptr;
+            const float *cs2 = cs ? cs + n1 : nullptr;
             const uint16_t *bias2 = bias ? bias + n1 : nullptr;
-            return launch_shape(two, fp4, a, lda, a_scale, w2, ldw, ws2, bias2, epi, y + n1, ldy, M,
-                                N - n1, K, st);
+            return launch_shape(two, fp4, a, lda, a_scale, w2, ldw, ws2, cs2, bias2, epi, y + n1,
+                                ldy, M, N - n1, K, st);
         }
     }
-    return launch_shape(one, fp4, a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K, st);
+    return launch_shape(one, fp4, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_prefill(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
-                               const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                               const uint8_t *w, int64_t ldw, const uint8_t *ws, const float *cs,
                                const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
                                int64_t N, int64_t K, int num_cus, hipStream_t st) {
     if (K % 64 == 0)   // whole steps: LDS-mode staging
-        return launch_prefill_dma(fp4, a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, M, N, K,
+        return launch_prefill_dma(fp4, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K,
                                   num_cus, st);
     // K % 64 == 32: register-staged kernel; the largest tile that still
     // gives every CU a tile
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
     const int64_t t128 = ((M + 255) / 256) * ((N + 127) / 128);
 #define BSG_PREFILL(BM_, BN_)                                                                      \
-    return fp4 ? launch_tile<true, BM_, BN_, 2, 2>(a, lda, a_scale, w, ldw, ws, bias, epi, y, ldy, \
-                                                   M, N, K, st)                                    \
-               : launch_tile<false, BM_, BN_, 2, 2>(a, lda, a_scale, w, ldw, ws, bias, epi, y,     \
+    return fp4 ? launch_tile<true, BM_, BN_, 2, 2>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y,  \
+                                                   ldy, M, N, K, st)                               \
+               : launch_tile<false, BM_, BN_, 2, 2>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, \
                                                     ldy, M, N, K, st)
     if (t256 >= num_cus) BSG_PREFILL(256, 256);
     if (t128 >= num_cus) BSG_PREFILL(256, 128);

@@ -400,6 +400,28 @@ hipError_t launch_quant_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_
 
 namespace {
 
+// Static-scale quantization: one given scale for every row, so no reduction;
+// each thread encodes 16-byte chunks of the flattened rows.
+__global__ __launch_bounds__(256) void quant_static_kernel(const uint16_t *__restrict__ x,
+                                                           int64_t ldx, uint8_t *__restrict__ q,
+                                                           int64_t ldq,
+                                                           const float *__restrict__ s_in,
+                                                           float *__restrict__ s_out, int64_t M,
+                                                           int K) {
+    const float s = *s_in;
+    bool r_ok;
+    const float r = recip_of(s, r_ok);
+    const int nch = K >> 3;
+    const int64_t total = M * nch;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * 256) {
+        const int64_t m = idx / nch;
+        const int c = (int)(idx - m * nch);
+        *reinterpret_cast<uint2 *>(q + m * ldq + 8 * c) = encode8(ldg16(x + m * ldx + 8 * c), s, r, r_ok);
+        if (s_out && c == 0) s_out[m] = s;
+    }
+}
+
 // Thread count per row for a producer: the quantizer's choice, widened
 // until each thread holds at most 16 chunks (8 for 128 threads per row).
 template <int PROD>
@@ -438,6 +460,16 @@ hipError_t launch_add_rms_quant(const uint16_t *x, int64_t ld_x, uint16_t *resid
         ? launch_producer<PROD_ADD_RMS>(x, ld_x, q, ld_q, scale, M, (int)K, pp, stream)
         : launch_producer<PROD_RMS>(x, ld_x, q, ld_q, scale, M, (int)K, pp, stream);
     return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+hipError_t launch_quant_rows_static(const uint16_t *x, int64_t ld_x, const float *scale_in,
+                                    uint8_t *q, int64_t ld_q, float *scale_out, int64_t M,
+                                    int64_t K, hipStream_t stream) {
+    const int64_t chunks = M * (K / 8);
+    const int64_t blocks = (chunks + 255) / 256;
+    hipLaunchKernelGGL(quant_static_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
+                       dim3(256), 0, stream, x, ld_x, q, ld_q, scale_in, scale_out, M, (int)K);
+    return hipGetLastError();
 }
 
 hipError_t launch_silu_mul_quant(const uint16_t *gate_up, int64_t ld_gu, uint8_t *q, int64_t ld_q,

@@ -1,0 +1,128 @@
+"""Row-wise scaled e4m3 GEMM (per-token x per-output-channel fp32 scales)
+and the static-scale quantizer on the GPU, against the oracle.
+
+The GEMM runs through every kernel the dispatcher can pick (folded decode,
+wide-layer decode, split-K decode, both prefill kernels), each epilogue, and
+the lm_head workload at full size on sampled outputs; the quantizer must
+match bit for bit, saturation included."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_gemm_transformer_amd as bs
+import oracle
+import synth
+from gpu_util import DEV, assert_within, bf16_dev, f32_dev, u8_dev, y_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _problem(M, N, K, seed):
+    rng = np.random.default_rng(seed)
+    a, s = oracle.quant_rows(synth.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32)))
+    w, ws = oracle.quant_rows(synth.to_bf16_bits((rng.standard_normal((N, K)) * 0.02)
+                                                 .astype(np.float32)))
+    ws = ws * np.exp2(rng.integers(-3, 4, N)).astype(np.float32)   # channel scales of several binades
+    b = synth.to_bf16_bits((rng.standard_normal(N) * 0.1).astype(np.float32))
+    return a, s, w, ws, b
+
+
+def _run(a, s, w, ws, b, epi, ld_pad=0):
+    M, K = a.shape
+    N = w.shape[0]
+    if ld_pad:
+        af = np.zeros((M, K + ld_pad), np.uint8); af[:, :K] = a
+        wf = np.zeros((N, K + ld_pad), np.uint8); wf[:, :K] = w
+        a_t, w_t = u8_dev(af)[:, :K], u8_dev(wf)[:, :K]
+        y = torch.full((M, N + ld_pad), float("nan"), dtype=torch.bfloat16, device=DEV)[:, :N]
+    else:
+        a_t, w_t, y = u8_dev(a), u8_dev(w), None
+    out = bs.gemm_fp8_rowwise(a_t, f32_dev(s), w_t, f32_dev(ws), bf16_dev(b) if epi else None,
+                              epi, y=y)
+    return y_host(out)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 96, 1056), (8, 2048, 512), (5, 32768 + 32, 640), (16, 32768 + 32, 1024),   # decode
+    (24, 2048, 1152), (64, 512, 4096), (12, 2080, 1184),                            # split-K
+    (200, 320, 512), (300, 4192, 256), (513, 1024, 2048),                           # prefill DMA
+    (130, 416, 96), (257, 160, 1056)])                                              # K % 64 = 32
+@pytest.mark.parametrize("epi", [synth.EPI_NONE, synth.EPI_BIAS_GELU_TANH])
+def test_rowwise_shapes(M, N, K, epi):
+    a, s, w, ws, b = _problem(M, N, K, seed=M + N + K)
+    got = _run(a, s, w, ws, b, epi)
+    ref, absum = oracle.gemm_fp8_rowwise(a, s, w, ws, b if epi else None, epi)
+    assert_within(got, ref, absum, "rowwise M=%d N=%d K=%d epi=%d" % (M, N, K, epi))
+
+
+@pytest.mark.parametrize("M", [4, 40, 300])
+def test_rowwise_padded_and_bias(M):
+    a, s, w, ws, b = _problem(M, 256, 512, seed=7 + M)
+    got = _run(a, s, w, ws, b, synth.EPI_BIAS, ld_pad=48)
+    ref, absum = oracle.gemm_fp8_rowwise(a, s, w, ws, b, synth.EPI_BIAS)
+    assert_within(got, ref, absum, "rowwise padded M=%d" % M)
+
+
+def test_rowwise_uniform_power_of_two_scales_equal_block_scaled():
+    """Channel scales that are one power of two per 32-row block give the
+    block-scaled GEMM's exact bits on the same kernels."""
+    rng = np.random.default_rng(61)
+    M, N, K = 8, 512, 1024
+    a, s = oracle.quant_rows(synth.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32)))
+    w = oracle.encode_e4m3((rng.standard_normal((N, K)) * 0.05).astype(np.float32))
+    byte = rng.integers(120, 131, size=N // 32).astype(np.uint8)
+    grid = np.repeat(byte[:, None], K // 32, axis=1)
+    chan = np.repeat(np.exp2(byte.astype(np.float64) - 127), 32).astype(np.float32)
+    y_rw = bs.gemm_fp8_rowwise(u8_dev(a), f32_dev(s), u8_dev(w), f32_dev(chan))
+    y_bs = bs.gemm_bs_fp8(u8_dev(a), f32_dev(s), u8_dev(w), u8_dev(grid))
+    torch.cuda.synchronize()
+    assert torch.equal(y_rw.view(torch.int16), y_bs.view(torch.int16))
+
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_lm_head_full_size_sampled(M):
+    d = synth.make("lm_head", M)
+    wl = d["wl"]
+    x = bf16_dev(d["a_bf16"])
+    q, s = bs.fp8_quant_rows(x)
+    q_ref, s_ref = oracle.quant_rows(d["a_bf16"])
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    y = bs.gemm_fp8_rowwise(q, s, u8_dev(d["w"]), f32_dev(d["w_scale"]))
+    got = y_host(y)
+    rng = np.random.default_rng(62)
+    ms = np.concatenate([rng.integers(0, M, 4000), [0, M - 1]])
+    ns = np.concatenate([rng.integers(0, wl.N, 4000), [wl.N - 1, 0]])
+    ref, absum = oracle.gemm_fp8_rowwise_sampled(q_ref, s_ref, d["w"], d["w_scale"], None, 0, ms, ns)
+    assert_within(got[ms, ns], ref, absum, "lm_head M=%d" % M)
+    assert np.isfinite(got).all()
+
+
+# ------------------------------------------------------------ static quant
+@pytest.mark.parametrize("M,K,scale", [(1, 32, 0.01), (7, 1056, 0.003), (300, 5120, 0.02),
+                                       (65, 2048, 1e-4), (4, 256, 3.0)])
+def test_static_quant(M, K, scale):
+    rng = np.random.default_rng(M + K)
+    x = synth.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    sc = np.float32(scale)
+    q, s_out = bs.fp8_quant_rows_static(bf16_dev(x), torch.tensor([sc], device=DEV))
+    torch.cuda.synchronize()
+    want = oracle.quant_rows_static(x, sc)
+    assert np.array_equal(q.cpu().numpy(), want)
+    assert np.all(s_out.cpu().numpy() == sc)
+
+
+def test_static_quant_then_rowwise_gemm():
+    """Per-tensor scales end to end: static activation scale and a constant
+    channel scale, i.e. y = alpha * sum a w with alpha = act_scale * w_scale."""
+    rng = np.random.default_rng(63)
+    M, N, K = 16, 256, 512
+    x = synth.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    act = np.float32(0.01)
+    q, s = bs.fp8_quant_rows_static(bf16_dev(x), torch.tensor([act], device=DEV))
+    w = oracle.encode_e4m3((rng.standard_normal((N, K)) * 0.05).astype(np.float32))
+    wsc = np.full(N, 0.125, np.float32)
+    y = bs.gemm_fp8_rowwise(q, s, u8_dev(w), f32_dev(wsc))
+    q_ref = oracle.quant_rows_static(x, act)
+    ref, absum = oracle.gemm_fp8_rowwise(q_ref, np.full(M, act, np.float32), w, wsc)
+    assert_within(y_host(y), ref, absum, "per-tensor")

@@ -111,6 +111,32 @@ def test_quant_argument_checks():
     assert q(s=ctypes.c_void_p(0x10002)) == bs.BS_EALIGN
 
 
+def test_rowwise_and_static_argument_checks():
+    lib = bs.load_library()
+    E, A = bs.BS_EINVAL, bs.BS_EALIGN
+    fn = lib.gemm_fp8_rowwise
+    assert _gemm(fn, ws=None) == E
+    assert _gemm(fn, ws=ctypes.c_void_p(0x10008)) == A            # fp32 scales need 16 bytes
+    assert _gemm(fn, a=None) == E
+    assert _gemm(fn, N=48) == E
+    assert bs.bs_workspace_bytes(2, 16, 2048, 7168) == bs.bs_workspace_bytes(0, 16, 2048, 7168)
+
+    def st(x=FAKE, ldx=64, s=FAKE, q=FAKE, ldq=64, so=FAKE, M=4, K=64):
+        return lib.fp8_quant_rows_static(x, ldx, s, q, ldq, so, M, K, None)
+
+    assert st(x=None) == E
+    assert st(s=None) == E
+    assert st(q=None) == E
+    assert st(M=0) == E
+    assert st(K=48) == E
+    assert st(ldx=32) == E
+    assert st(ldq=32) == E
+    assert st(x=ctypes.c_void_p(0x10008)) == A
+    assert st(s=ctypes.c_void_p(0x10002)) == A
+    assert st(so=ctypes.c_void_p(0x10002)) == A
+    assert st(ldq=72) == A
+
+
 def test_producer_argument_checks():
     lib = bs.load_library()
     E, A = bs.BS_EINVAL, bs.BS_EALIGN
