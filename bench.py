@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", default="decode",
                    choices=["tiny", "decode", "prefill", "ffn_up", "ffn_up_bias", "gate_up",
-                            "add_rms", "silu_mul"],
+                            "lm_head", "add_rms", "silu_mul"],
                    help="a GEMM workload (quantize + GEMM per step), or a fused producer "
                         "(add_rms: residual add + RMSNorm + quantize on [M, 5120]; silu_mul: "
                         "SiLU(gate) * up + quantize on [M, 2 x 17408])")
@@ -95,8 +95,8 @@ def algorithmic(wl, M):
     """Bytes each kernel must move and the GEMM's FLOPs, by definition."""
     N, K = wl.N, wl.K
     quant = 2 * M * K + M * K + 4 * M                      # bf16 in, codes + scales out
-    w_bytes = N * K if wl.fmt == "fp8" else N * K // 2
-    ws_bytes = (N // 32) * (K // 32) if wl.fmt == "fp8" else N * (K // 32)
+    w_bytes = N * K // 2 if wl.fmt == "mxfp4" else N * K
+    ws_bytes = {"fp8": (N // 32) * (K // 32), "mxfp4": N * (K // 32), "fp8_rowwise": 4 * N}[wl.fmt]
     gemm = w_bytes + ws_bytes + M * K + 4 * M + 2 * M * N
     if wl.epilogue:
         gemm += 2 * N
@@ -147,9 +147,10 @@ def main():
     q = torch.empty((M, wl.K), dtype=torch.uint8, device=dev)
     s = torch.empty((M,), dtype=torch.float32, device=dev)
     y = torch.empty((M, wl.N), dtype=torch.bfloat16, device=dev)
-    gemm = bs.gemm_bs_fp8 if wl.fmt == "fp8" else bs.gemm_mxfp4_w4a8
+    gemm = {"fp8": bs.gemm_bs_fp8, "mxfp4": bs.gemm_mxfp4_w4a8,
+            "fp8_rowwise": bs.gemm_fp8_rowwise}[wl.fmt]
     work = None
-    need = bs.bs_workspace_bytes(0 if wl.fmt == "fp8" else 1, M, wl.N, wl.K)
+    need = bs.bs_workspace_bytes({"fp8": 0, "mxfp4": 1, "fp8_rowwise": 2}[wl.fmt], M, wl.N, wl.K)
     if need:
         work = torch.zeros((need,), dtype=torch.uint8, device=dev)
 
@@ -221,7 +222,8 @@ def main():
         achieved = alg["gemm_bytes"] / gemm_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["kernel"] = "gemm_mxfp4_w4a8" if wl.fmt == "mxfp4" else "gemm_bs_fp8"
+    roof["kernel"] = {"fp8": "gemm_bs_fp8", "mxfp4": "gemm_mxfp4_w4a8",
+                      "fp8_rowwise": "gemm_fp8_rowwise"}[wl.fmt]
     roof["traffic"] = measured_traffic(roof["kernel"], wl.name, M)
     roof["avg_launch_us"] = round(gemm_s * 1e6, 3)
     roof["algorithmic_bytes_per_launch"] = alg["gemm_bytes"]
@@ -231,11 +233,11 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8_e4m3" if wl.fmt == "fp8" else "fp8_e4m3 x fp4_e2m1",
+        "dtype": "fp8_e4m3 x fp4_e2m1" if wl.fmt == "mxfp4" else "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": "%s M=%d N=%d K=%d (%s weights, %s scales, epilogue %s)" % (
-            wl.name, M, wl.N, wl.K, "e4m3" if wl.fmt == "fp8" else "MXFP4 e2m1",
-            "32x32 E8M0" if wl.fmt == "fp8" else "1x32 E8M0",
+            wl.name, M, wl.N, wl.K, "MXFP4 e2m1" if wl.fmt == "mxfp4" else "e4m3",
+            {"fp8": "32x32 E8M0", "mxfp4": "1x32 E8M0", "fp8_rowwise": "fp32 per-channel"}[wl.fmt],
             ["none", "bias", "bias+tanh-GELU"][epi]),
             "M": M, "N": wl.N, "K": wl.K, "weight_copies_rotated": copies,
             "step": "fp8_quant_rows + %s" % roof["kernel"], "graph_replay": True},
@@ -265,6 +267,8 @@ def cpu_baseline(d, wl, M, alg, compute_bound, budget_s):
         q, s = oracle.quant_rows(sample)
         if wl.fmt == "fp8":
             oracle.gemm_bs_fp8(q, s, d["w"], d["w_scale"], d["bias"], d["epilogue"])
+        elif wl.fmt == "fp8_rowwise":
+            oracle.gemm_fp8_rowwise(q, s, d["w"], d["w_scale"], d["bias"], d["epilogue"])
         else:
             oracle.gemm_mxfp4_w4a8(q, s, d["w"], d["w_scale"], d["bias"], d["epilogue"])
         t_total += time.perf_counter() - t0

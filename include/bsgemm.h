@@ -203,7 +203,8 @@ int gemm_fp8_rowwise(const void *a_e4m3, int64_t ld_a, const float *a_scale,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Scratch bytes gemm_bs_fp8 (op 0), gemm_mxfp4_w4a8 (op 1) or
- * gemm_fp8_rowwise (op 2) needs for this shape; 0 means none. Nonzero for 8 < M <= 64, where K is split across
+ * gemm_fp8_rowwise (op 2) needs for this shape; 0 means none. Nonzero for
+ * 8 < M <= 64, and for 2 <= M <= 8 when N * K >= 2^26: K is split across
  * workgroups and fp32 partial sums [S][M][N] go through the workspace
  * (S depends only on N and K). The workspace must then be 16-byte aligned;
  * its contents on entry do not matter (every byte read is written first by

@@ -469,6 +469,14 @@ __host__ __device__ inline int64_t decode_splits(int64_t N, int64_t K) {
     return s;
 }
 
+// 2 <= M <= 8 on a layer of at least 2^26 weights (when the wide-layer
+// kernel does not take it): the folded kernel's workgroups would each read
+// M x K activation bytes for 8 x K weight bytes; split-K reads M/8 of that
+// per 64 rows and its second launch is small against a long first one.
+__host__ __device__ inline bool large_splitk(int64_t M, int64_t N, int64_t K) {
+    return M >= 2 && M <= 8 && N * K >= ((int64_t)1 << 26);
+}
+
 template <bool FP4, int MT>
 __global__ __launch_bounds__(256) void gemm_decode_splitk_kernel(
     const uint8_t *__restrict__ A, int64_t lda, const uint8_t *__restrict__ W, int64_t ldw,
@@ -658,7 +666,7 @@ hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const flo
             return hipGetLastError();
         }
     }
-    if (M <= 8) {
+    if (M <= 8 && !large_splitk(M, N, K)) {
         const int per = (int)(((K + 255) / 256 + NW - 1) / NW);
         if (fp4)
             launch_spw<true, true, 1>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
@@ -666,7 +674,8 @@ hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const flo
             launch_spw<false, true, 1>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
         return hipGetLastError();
     }
-    // 8 < M <= 64: split K over workgroups, partial sums in the workspace
+    // 8 < M <= 64, or 2 <= M <= 8 on a large layer: split K over
+    // workgroups, partial sums in the workspace
     float *part = static_cast<float *>(workspace);
     switch ((M + 15) / 16) {
     case 1: return fp4 ? launch_splitk<true, 1>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, part, st)
@@ -681,7 +690,7 @@ hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const flo
 }
 
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    if (M <= 8 || M > DECODE_MAX_M) return 0;
+    if ((M <= 8 && !large_splitk(M, N, K)) || M > DECODE_MAX_M) return 0;
     return (size_t)decode_splits(N, K) * (size_t)M * (size_t)N * sizeof(float);
 }
 

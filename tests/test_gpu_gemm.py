@@ -60,7 +60,10 @@ def test_decode_wide_rows(fmt, M, K):
 # steps; (2048, 1152) leaves the last three slices empty, (2080, 1184) adds
 # a half-full last column block and a 32-wide K tail
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
-@pytest.mark.parametrize("M,N,K", [(40, 2048, 1152), (12, 2080, 1184), (64, 512, 4096)])
+# (3 and 8 x 8192 x 8224: small M on a layer of >= 2^26 weights that the
+# wide-layer kernel does not take, K > 8192)
+@pytest.mark.parametrize("M,N,K", [(40, 2048, 1152), (12, 2080, 1184), (64, 512, 4096),
+                                   (3, 8192, 8224), (8, 8192, 8224)])
 def test_decode_split_k(fmt, M, N, K):
     _full_check(fmt, M, N, K, synth.EPI_BIAS_GELU_TANH if M == 12 else synth.EPI_BIAS, seed=M + K)
 

@@ -44,6 +44,10 @@ def test_status_strings_and_workspace():
     assert bs.bs_workspace_bytes(1, 16, 2048, 7168) == 8 * 16 * 2048 * 4
     assert bs.bs_workspace_bytes(0, 9, 32, 32) == 1 * 9 * 32 * 4
     assert bs.bs_workspace_bytes(0, 65, 2048, 7168) == 0
+    # 2 <= M <= 8 on layers of >= 2^26 weights: split-K too (S = 5 at K = 5120)
+    assert bs.bs_workspace_bytes(2, 8, 248320, 5120) == 5 * 8 * 248320 * 4
+    assert bs.bs_workspace_bytes(2, 1, 248320, 5120) == 0
+    assert bs.bs_workspace_bytes(0, 8, 7168, 8192) == 0            # 2^25.8 weights
 
 
 def _gemm(fn, a=FAKE, lda=64, s=FAKE, w=FAKE, ldw=64, ws=FAKE, bias=None, epi=0, y=FAKE, ldy=64,
