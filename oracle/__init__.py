@@ -24,6 +24,11 @@ Parity status of each function (the pins are the ``-m "not gpu"`` tests in
 * bf16 rounding of fp64 values: pinned (torch's fp32 -> bf16 cast on values
   exact in fp32, exact rational nearest-neighbour search on values that are
   not, overflow and signed zeros).
+* MXFP4 activation quantizer and the W4A4 GEMM: pinned (the quantizer is
+  the weight conversion applied to activation rows, checked against the
+  generator's independent numpy conversion; the GEMM against
+  dequantize-then-matmul, exact rational brute force, and the W4A8 GEMM
+  where the activations are representable in both formats).
 * static-scale quantizer: pinned (equals the dynamic quantizer when given
   the row's own scale; saturation beyond 448 s; torch's float8 cast).
 * row-wise scaled GEMM (per-token x per-channel fp32 scales): pinned
@@ -101,6 +106,14 @@ def _load():
         lib.or_encode_e4m3.restype = None
         lib.or_quant_mxfp4_weights.argtypes = [vp, i64, i64, vp, vp]
         lib.or_quant_mxfp4_weights.restype = None
+        lib.or_quant_mxfp4_rows.argtypes = [vp, i64, i64, i64, vp, vp]
+        lib.or_quant_mxfp4_rows.restype = None
+        w4 = [vp, i64, vp, vp, i64, vp, vp, ctypes.c_int, i64, i64, i64, vp, vp]
+        lib.or_gemm_mxfp4_w4a4.argtypes = w4
+        lib.or_gemm_mxfp4_w4a4.restype = None
+        lib.or_gemm_mxfp4_w4a4_sampled.argtypes = [vp, i64, vp, vp, i64, vp, vp, ctypes.c_int,
+                                                   i64, i64, vp, vp, vp, vp]
+        lib.or_gemm_mxfp4_w4a4_sampled.restype = None
         lib.or_quant_rows_static.argtypes = [vp, i64, i64, i64, ctypes.c_float, vp, i64]
         lib.or_quant_rows_static.restype = None
         rw = [vp, i64, vp, vp, i64, vp, vp, ctypes.c_int, i64, i64, i64, vp, vp]
@@ -300,6 +313,52 @@ def gemm_sampled(fmt, a_codes, a_scale, w, w_scale, bias_bf16, epilogue, ms, ns)
         fn, ldw = _load().or_gemm_mxfp4_w4a8_sampled, K // 2
     fn(_ptr(a), K, _ptr(s), _ptr(w), ldw, _ptr(ws), _ptr(b), int(epilogue), K,
        ms.size, _ptr(ms), _ptr(ns), _ptr(out), _ptr(absum))
+    return out, absum
+
+
+def quant_mxfp4_rows(x_bf16: np.ndarray):
+    """MXFP4 (OCP MX) quantization of bf16 activation rows [M, K]:
+    (packed uint8 [M, K/2], E8M0 scales uint8 [M, K/32])."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    packed = np.empty((M, K // 2), dtype=np.uint8)
+    scales = np.empty((M, K // 32), dtype=np.uint8)
+    _load().or_quant_mxfp4_rows(_ptr(x), K, M, K, _ptr(packed), _ptr(scales))
+    return packed, scales
+
+
+def gemm_mxfp4_w4a4(a_packed, a_scales, w_packed, w_scales, bias_bf16=None, epilogue=EPI_NONE):
+    """fp64 output and absum [M, N] of the MXFP4 x MXFP4 GEMM."""
+    a = _c(a_packed, np.uint8)
+    sa = _c(a_scales, np.uint8)
+    w = _c(w_packed, np.uint8)
+    sw = _c(w_scales, np.uint8)
+    M, K2 = a.shape
+    K = 2 * K2
+    N = w.shape[0]
+    assert w.shape == (N, K2) and sa.shape == (M, K // 32) and sw.shape == (N, K // 32)
+    b = None if bias_bf16 is None else _c(bias_bf16, np.uint16)
+    out = np.empty((M, N), dtype=np.float64)
+    absum = np.empty((M, N), dtype=np.float64)
+    _load().or_gemm_mxfp4_w4a4(_ptr(a), K2, _ptr(sa), _ptr(w), K2, _ptr(sw), _ptr(b),
+                               int(epilogue), M, N, K, _ptr(out), _ptr(absum))
+    return out, absum
+
+
+def gemm_mxfp4_w4a4_sampled(a_packed, a_scales, w_packed, w_scales, bias_bf16, epilogue, ms, ns):
+    a = _c(a_packed, np.uint8)
+    sa = _c(a_scales, np.uint8)
+    w = _c(w_packed, np.uint8)
+    sw = _c(w_scales, np.uint8)
+    K2 = a.shape[1]
+    b = None if bias_bf16 is None else _c(bias_bf16, np.uint16)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    out = np.empty(ms.shape, dtype=np.float64)
+    absum = np.empty(ms.shape, dtype=np.float64)
+    _load().or_gemm_mxfp4_w4a4_sampled(_ptr(a), K2, _ptr(sa), _ptr(w), K2, _ptr(sw), _ptr(b),
+                                       int(epilogue), 2 * K2, ms.size, _ptr(ms), _ptr(ns),
+                                       _ptr(out), _ptr(absum))
     return out, absum
 
 

@@ -33,6 +33,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <stdlib.h>
 
 #define OR_EPI_NONE 0
 #define OR_EPI_BIAS 1
@@ -417,6 +418,70 @@ void or_gemm_mxfp4_w4a8(const uint8_t *a, int64_t lda, const float *a_scale,
     }
 }
 
+/* One output of the MXFP4 x MXFP4 GEMM (W4A4): activations and weights both
+ * fp4 e2m1 packed two per byte with one E8M0 scale per row per 32 along K
+ * (sly-radiance README: MXFP4 W4A4 is the base path its W4A8 kernel takes
+ * over from; the per-32 scale rule is OCP MX's, as for the weights). In fp64:
+ *   acc   = sum_kb 2^(sa[kb]-127) 2^(sw[kb]-127) sum_{k in block kb} a[k] w[k]
+ *   pre   = acc (+ bias); out = pre or GELU_tanh(pre)
+ *   absum = sum_kb 2^(sa[kb]-127) 2^(sw[kb]-127) sum_k |a[k] w[k]|         */
+static double e2m1_at(const uint8_t *packed, int64_t k)
+{
+    uint8_t byte = packed[k / 2];
+    return or_e2m1_value((k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15));
+}
+
+static void one_w4a4(const uint8_t *a, const uint8_t *as, const uint8_t *w, const uint8_t *ws,
+                     const uint16_t *bias_n, int epi, int64_t K, double *out, double *absum)
+{
+    double acc = 0.0, abs_acc = 0.0, pre;
+    int64_t kb, k;
+    for (kb = 0; kb < K / 32; ++kb) {
+        double blk = 0.0, blk_abs = 0.0;
+        double sc = or_e8m0_value(as[kb]) * or_e8m0_value(ws[kb]);
+        for (k = kb * 32; k < kb * 32 + 32; ++k) {
+            double p = e2m1_at(a, k) * e2m1_at(w, k);
+            blk += p;
+            blk_abs += fabs(p);
+        }
+        acc += sc * blk;
+        abs_acc += sc * blk_abs;
+    }
+    pre = acc;
+    if (epi >= OR_EPI_BIAS)
+        pre += or_bf16_value(*bias_n);
+    *out = epilogue(pre, epi);
+    *absum = abs_acc;
+}
+
+void or_gemm_mxfp4_w4a4(const uint8_t *a, int64_t lda, const uint8_t *a_scale,
+                        const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                        const uint16_t *bias, int epi, int64_t M, int64_t N, int64_t K,
+                        double *out, double *absum)
+{
+    int64_t idx;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (idx = 0; idx < M * N; ++idx) {
+        int64_t m = idx / N, n = idx % N;
+        one_w4a4(a + m * lda, a_scale + m * (K / 32), w + n * ldw, ws + n * (K / 32),
+                 bias ? bias + n : NULL, epi, K, out + idx, absum + idx);
+    }
+}
+
+void or_gemm_mxfp4_w4a4_sampled(const uint8_t *a, int64_t lda, const uint8_t *a_scale,
+                                const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                                const uint16_t *bias, int epi, int64_t K, int64_t count,
+                                const int64_t *ms, const int64_t *ns, double *out, double *absum)
+{
+    int64_t i;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (i = 0; i < count; ++i) {
+        int64_t m = ms[i], n = ns[i];
+        one_w4a4(a + m * lda, a_scale + m * (K / 32), w + n * ldw, ws + n * (K / 32),
+                 bias ? bias + n : NULL, epi, K, out + i, absum + i);
+    }
+}
+
 /* One output of the row-wise scaled e4m3 GEMM: per-token activation scale
  * times per-output-channel weight scale (sly-radiance README, lm_head row of
  * its file table: the head's weight quantized to fp8 per output channel and
@@ -556,6 +621,24 @@ void or_quant_mxfp4_weights(const float *v, int64_t N, int64_t K,
                 packed[n * (K / 2) + kb * 16 + k / 2] = (uint8_t)(lo | (hi << 4));
             }
         }
+    }
+}
+
+/* MXFP4 quantization of bf16 activation rows [M, K] (row stride ldx
+ * elements): the OCP MX conversion above applied to each row's values
+ * (bf16 values are exact in binary32). Output packed [M, K/2] (low nibble =
+ * even k) and scales [M, K/32]. */
+void or_quant_mxfp4_rows(const uint16_t *x, int64_t ldx, int64_t M, int64_t K,
+                         uint8_t *packed, uint8_t *scales)
+{
+    int64_t m;
+    for (m = 0; m < M; ++m) {
+        float *row = (float *)malloc((size_t)K * sizeof(float));
+        int64_t k;
+        for (k = 0; k < K; ++k)
+            row[k] = (float)or_bf16_value(x[m * ldx + k]);
+        or_quant_mxfp4_weights(row, 1, K, packed + m * (K / 2), scales + m * (K / 32));
+        free(row);
     }
 }
 
