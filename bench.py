@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", default="decode",
                    choices=["tiny", "decode", "prefill", "ffn_up", "ffn_up_bias", "gate_up",
-                            "lm_head", "add_rms", "silu_mul"],
+                            "gate_up_w4a4", "lm_head", "add_rms", "silu_mul"],
                    help="a GEMM workload (quantize + GEMM per step), or a fused producer "
                         "(add_rms: residual add + RMSNorm + quantize on [M, 5120]; silu_mul: "
                         "SiLU(gate) * up + quantize on [M, 2 x 17408])")
@@ -94,10 +94,16 @@ def calibrate_copy(nbytes: int):
 def algorithmic(wl, M):
     """Bytes each kernel must move and the GEMM's FLOPs, by definition."""
     N, K = wl.N, wl.K
-    quant = 2 * M * K + M * K + 4 * M                      # bf16 in, codes + scales out
-    w_bytes = N * K // 2 if wl.fmt == "mxfp4" else N * K
-    ws_bytes = {"fp8": (N // 32) * (K // 32), "mxfp4": N * (K // 32), "fp8_rowwise": 4 * N}[wl.fmt]
-    gemm = w_bytes + ws_bytes + M * K + 4 * M + 2 * M * N
+    if wl.fmt == "mxfp4_w4a4":   # fp4 codes + one E8M0 byte per 32
+        quant = 2 * M * K + M * K // 2 + M * K // 32
+        a_bytes = M * K // 2 + M * K // 32
+    else:
+        quant = 2 * M * K + M * K + 4 * M                  # bf16 in, codes + scales out
+        a_bytes = M * K + 4 * M
+    w_bytes = N * K // 2 if wl.fmt in ("mxfp4", "mxfp4_w4a4") else N * K
+    ws_bytes = {"fp8": (N // 32) * (K // 32), "mxfp4": N * (K // 32), "mxfp4_w4a4": N * (K // 32),
+                "fp8_rowwise": 4 * N}[wl.fmt]
+    gemm = w_bytes + ws_bytes + a_bytes + 2 * M * N
     if wl.epilogue:
         gemm += 2 * N
     return {"quant_bytes": quant, "gemm_bytes": gemm, "gemm_flops": 2 * M * N * K}
@@ -144,25 +150,33 @@ def main():
     if d["bias"] is not None:
         bias = torch.from_numpy(d["bias"].view(np.int16)).view(torch.bfloat16).to(dev)
     epi = d["epilogue"]
-    q = torch.empty((M, wl.K), dtype=torch.uint8, device=dev)
-    s = torch.empty((M,), dtype=torch.float32, device=dev)
+    w4a4 = wl.fmt == "mxfp4_w4a4"
+    if w4a4:
+        q = torch.empty((M, wl.K // 2), dtype=torch.uint8, device=dev)
+        s = torch.empty((M, wl.K // 32), dtype=torch.uint8, device=dev)
+        quant = lambda: bs.fp4_quant_rows(x, q, s)
+    else:
+        q = torch.empty((M, wl.K), dtype=torch.uint8, device=dev)
+        s = torch.empty((M,), dtype=torch.float32, device=dev)
+        quant = lambda: bs.fp8_quant_rows(x, q, s)
     y = torch.empty((M, wl.N), dtype=torch.bfloat16, device=dev)
-    gemm = {"fp8": bs.gemm_bs_fp8, "mxfp4": bs.gemm_mxfp4_w4a8,
+    gemm = {"fp8": bs.gemm_bs_fp8, "mxfp4": bs.gemm_mxfp4_w4a8, "mxfp4_w4a4": bs.gemm_mxfp4_w4a4,
             "fp8_rowwise": bs.gemm_fp8_rowwise}[wl.fmt]
     work = None
-    need = bs.bs_workspace_bytes({"fp8": 0, "mxfp4": 1, "fp8_rowwise": 2}[wl.fmt], M, wl.N, wl.K)
+    need = bs.bs_workspace_bytes({"fp8": 0, "mxfp4": 1, "fp8_rowwise": 2, "mxfp4_w4a4": 3}[wl.fmt],
+                                 M, wl.N, wl.K)
     if need:
         work = torch.zeros((need,), dtype=torch.uint8, device=dev)
 
     def step(i):
-        bs.fp8_quant_rows(x, q, s)
+        quant()
         gemm(q, s, ws_list[i % copies], wss_list[i % copies], bias, epi, y=y, workspace=work)
 
     def gemm_only(i):
         gemm(q, s, ws_list[i % copies], wss_list[i % copies], bias, epi, y=y, workspace=work)
 
     def quant_only(i):
-        bs.fp8_quant_rows(x, q, s)
+        quant()
 
     stream = torch.cuda.Stream()
 
@@ -210,7 +224,7 @@ def main():
     if compute_bound:
         unit = "TFLOP/s"
         value = alg["gemm_flops"] * steps / step_s / 1e12
-        peak = FP4_PEAK_TFLOPS if wl.fmt == "mxfp4" else FP8_PEAK_TFLOPS
+        peak = FP4_PEAK_TFLOPS if wl.fmt in ("mxfp4", "mxfp4_w4a4") else FP8_PEAK_TFLOPS
         achieved = alg["gemm_flops"] / gemm_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
@@ -222,7 +236,7 @@ def main():
         achieved = alg["gemm_bytes"] / gemm_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["kernel"] = {"fp8": "gemm_bs_fp8", "mxfp4": "gemm_mxfp4_w4a8",
+    roof["kernel"] = {"fp8": "gemm_bs_fp8", "mxfp4": "gemm_mxfp4_w4a8", "mxfp4_w4a4": "gemm_mxfp4_w4a4",
                       "fp8_rowwise": "gemm_fp8_rowwise"}[wl.fmt]
     roof["traffic"] = measured_traffic(roof["kernel"], wl.name, M)
     roof["avg_launch_us"] = round(gemm_s * 1e6, 3)
@@ -233,16 +247,19 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8_e4m3 x fp4_e2m1" if wl.fmt == "mxfp4" else "fp8_e4m3",
+        "dtype": {"mxfp4": "fp8_e4m3 x fp4_e2m1", "mxfp4_w4a4": "fp4_e2m1 x fp4_e2m1"}.get(wl.fmt, "fp8_e4m3"),
         "data": "synthetic",
         "config": {"workload": "%s M=%d N=%d K=%d (%s weights, %s scales, epilogue %s)" % (
-            wl.name, M, wl.N, wl.K, "MXFP4 e2m1" if wl.fmt == "mxfp4" else "e4m3",
-            {"fp8": "32x32 E8M0", "mxfp4": "1x32 E8M0", "fp8_rowwise": "fp32 per-channel"}[wl.fmt],
+            wl.name, M, wl.N, wl.K, "MXFP4 e2m1" if wl.fmt in ("mxfp4", "mxfp4_w4a4") else "e4m3",
+            {"fp8": "32x32 E8M0", "mxfp4": "1x32 E8M0", "mxfp4_w4a4": "1x32 E8M0, MXFP4 activations",
+             "fp8_rowwise": "fp32 per-channel"}[wl.fmt],
             ["none", "bias", "bias+tanh-GELU"][epi]),
             "M": M, "N": wl.N, "K": wl.K, "weight_copies_rotated": copies,
-            "step": "fp8_quant_rows + %s" % roof["kernel"], "graph_replay": True},
+            "step": "%s + %s" % ("fp4_quant_rows" if w4a4 else "fp8_quant_rows", roof["kernel"]),
+            "graph_replay": True},
         "roofline": roof,
-        "kernels_us": {"fp8_quant_rows": round(quant_s * 1e6, 3), roof["kernel"]: round(gemm_s * 1e6, 3)},
+        "kernels_us": {("fp4_quant_rows" if w4a4 else "fp8_quant_rows"): round(quant_s * 1e6, 3),
+                       roof["kernel"]: round(gemm_s * 1e6, 3)},
         "step_bytes": step_bytes, "wall_s_timed_region": round(wall_s, 6),
     }
     if args.cpu_seconds > 0:
@@ -264,6 +281,14 @@ def cpu_baseline(d, wl, M, alg, compute_bound, budget_s):
     runs, t_total = 0, 0.0
     while t_total < budget_s or runs == 0:
         t0 = time.perf_counter()
+        if wl.fmt == "mxfp4_w4a4":
+            q, s = oracle.quant_mxfp4_rows(sample)
+            oracle.gemm_mxfp4_w4a4(q, s, d["w"], d["w_scale"], d["bias"], d["epilogue"])
+            t_total += time.perf_counter() - t0
+            runs += 1
+            if t_total > 3 * budget_s:
+                break
+            continue
         q, s = oracle.quant_rows(sample)
         if wl.fmt == "fp8":
             oracle.gemm_bs_fp8(q, s, d["w"], d["w_scale"], d["bias"], d["epilogue"])

@@ -9,7 +9,8 @@
  *                       per row per 32 along K)
  *   4. gemm_fp8_rowwise  e4m3 weights with one fp32 scale per output channel;
  *      fp8_quant_rows_static  quantization with a given per-tensor scale
- *   5. add_rms_norm_quant_fp8, silu_mul_quant_fp8
+ *   5. fp4_quant_rows, gemm_mxfp4_w4a4  MXFP4 activations x MXFP4 weights
+ *   6. add_rms_norm_quant_fp8, silu_mul_quant_fp8
  *                       fused producers: RMSNorm (with an optional residual
  *                       add) or SiLU(gate) * up, then step 1, in one kernel
  *
@@ -184,6 +185,40 @@ int gemm_mxfp4_w4a8(const void *a_e4m3, int64_t ld_a, const float *a_scale,
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * MXFP4 activations (W4A4, the sly-radiance README's base MXFP4 path that its
+ * W4A8 kernel takes prefill shapes over from; the per-32 scale rule is OCP
+ * MX's, the one the MXFP4 weights follow).
+ *
+ * fp4_quant_rows: per row m and 32-element block kb of x:
+ *     scale[m,kb] = E8M0 byte of floor(log2(amax)) - 2, clamped to [0, 254]
+ *                   (0 for an all-zero block)
+ *     q[m,k]      = e2m1(x[m,k] / 2^(scale - 127)): nearest of
+ *                   {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code,
+ *                   saturating at 6, sign kept (also for zeros)
+ *   x_bf16  [M, K] bf16, row stride ld_x elements
+ *   q_fp4x2 [M, K/2] uint8 out (low nibble = even k), row stride ld_q bytes
+ *   scale   [M, K/32] uint8 out, dense row-major
+ *
+ * gemm_mxfp4_w4a4:
+ *     acc[m,n] = sum_kb 2^(sa[m,kb]-127) 2^(sw[n,kb]-127) sum_{k in kb} a[m,k] w[n,k]
+ *     y[m,n]   = epilogue(acc (+ bias[n]))   -> bf16, nearest-even
+ *   a_fp4x2 [M, K/2], row stride ld_a bytes; a_scale [M, K/32] E8M0 dense
+ *   w_fp4x2 [N, K/2], w_scale [N, K/32] as gemm_mxfp4_w4a8
+ *   M > 64 needs K % 64 == 0; workspace: bs_workspace_bytes(3, M, N, K)
+ *   (nonzero for every M <= 64: the small-M path always splits K).
+ *   Other rules as gemm_bs_fp8.
+ */
+int fp4_quant_rows(const void *x_bf16, int64_t ld_x, void *q_fp4x2, int64_t ld_q,
+                   uint8_t *scale, int64_t M, int64_t K, void *stream);
+
+int gemm_mxfp4_w4a4(const void *a_fp4x2, int64_t ld_a, const uint8_t *a_scale,
+                    const void *w_fp4x2, int64_t ld_w, const uint8_t *w_scale,
+                    const void *bias_bf16, int epilogue,
+                    void *y_bf16, int64_t ld_y,
+                    int64_t M, int64_t N, int64_t K,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Row-wise scaled e4m3 GEMM: one fp32 scale per token and one per output
  * channel (sly-radiance README, lm_head row of its file table: the head's
  * weight quantized to fp8 per output channel, computed as a row-wise scaled
@@ -202,8 +237,9 @@ int gemm_fp8_rowwise(const void *a_e4m3, int64_t ld_a, const float *a_scale,
                      int64_t M, int64_t N, int64_t K,
                      void *workspace, size_t workspace_bytes, void *stream);
 
-/* Scratch bytes gemm_bs_fp8 (op 0), gemm_mxfp4_w4a8 (op 1) or
- * gemm_fp8_rowwise (op 2) needs for this shape; 0 means none. Nonzero for
+/* Scratch bytes gemm_bs_fp8 (op 0), gemm_mxfp4_w4a8 (op 1), gemm_fp8_rowwise
+ * (op 2) or gemm_mxfp4_w4a4 (op 3, every M <= 64) needs for this shape; 0
+ * means none. Nonzero for
  * 8 < M <= 64, and for 2 <= M <= 8 when N * K >= 2^26: K is split across
  * workgroups and fp32 partial sums [S][M][N] go through the workspace
  * (S depends only on N and K). The workspace must then be 16-byte aligned;

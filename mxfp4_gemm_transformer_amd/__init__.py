@@ -21,7 +21,7 @@ import torch
 
 __all__ = ["fp8_quant_rows", "fp8_quant_rows_static", "add_rms_norm_quant_fp8",
            "silu_mul_quant_fp8", "gemm_bs_fp8", "gemm_mxfp4_w4a8", "gemm_fp8_rowwise",
-           "bs_workspace_bytes",
+           "fp4_quant_rows", "gemm_mxfp4_w4a4", "bs_workspace_bytes",
            "bs_status_string", "BsError", "EPI_NONE", "EPI_BIAS", "EPI_BIAS_GELU_TANH",
            "weight_shape", "w_scale_shape", "library_path", "load_library",
            "EXPORTED_SYMBOLS"]
@@ -31,7 +31,7 @@ BS_OK, BS_EINVAL, BS_EALIGN, BS_EARCH, BS_EWORKSPACE, BS_ELAUNCH = 0, -1, -2, -3
 
 EXPORTED_SYMBOLS = ("fp8_quant_rows", "fp8_quant_rows_static", "add_rms_norm_quant_fp8",
                     "silu_mul_quant_fp8", "gemm_bs_fp8", "gemm_mxfp4_w4a8", "gemm_fp8_rowwise",
-                    "bs_workspace_bytes", "bs_status_string")
+                    "fp4_quant_rows", "gemm_mxfp4_w4a4", "bs_workspace_bytes", "bs_status_string")
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsgemm.so")
 _lib = None
@@ -70,6 +70,10 @@ def load_library():
         lib.gemm_mxfp4_w4a8.restype = i32
         lib.gemm_fp8_rowwise.argtypes = gemm
         lib.gemm_fp8_rowwise.restype = i32
+        lib.gemm_mxfp4_w4a4.argtypes = gemm
+        lib.gemm_mxfp4_w4a4.restype = i32
+        lib.fp4_quant_rows.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp]
+        lib.fp4_quant_rows.restype = i32
         lib.fp8_quant_rows_static.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, vp]
         lib.fp8_quant_rows_static.restype = i32
         lib.bs_workspace_bytes.argtypes = [i32, i64, i64, i64]
@@ -281,6 +285,63 @@ def fp8_quant_rows_static(x: torch.Tensor, scale: torch.Tensor, q: torch.Tensor 
     if st != BS_OK:
         raise BsError(st, "fp8_quant_rows_static")
     return q, scale_out
+
+
+def fp4_quant_rows(x: torch.Tensor, q: torch.Tensor | None = None,
+                   scale: torch.Tensor | None = None, stream=None):
+    """MXFP4 quantization of bf16 x [M, K]: (q uint8 [M, K/2] two e2m1 codes
+    per byte, low nibble = even k; scale uint8 E8M0 [M, K/32])."""
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    M, K = x.shape
+    ldx = _matrix(x, "x", M, K)
+    if q is None:
+        q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    ldq = _matrix(_u8(q, "q"), "q", M, K // 2)
+    if scale is None:
+        scale = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    if scale.dtype != torch.uint8 or tuple(scale.shape) != (M, K // 32) or not scale.is_contiguous():
+        raise ValueError("scale must be a contiguous uint8 [M, K/32] tensor")
+    st = load_library().fp4_quant_rows(_ptr(x), ldx, _ptr(q), ldq, _ptr(scale), M, K,
+                                       ctypes.c_void_p(_stream(stream)))
+    if st != BS_OK:
+        raise BsError(st, "fp4_quant_rows")
+    return q, scale
+
+
+def gemm_mxfp4_w4a4(a, a_scale, w, w_scale, bias=None, epilogue=EPI_NONE, y=None,
+                    workspace=None, stream=None):
+    """y [M, N] bf16 = epilogue(sum_kb 2^(Sa[m,kb]-127) 2^(Sw[n,kb]-127) sum a w (+ bias)).
+    a: fp4x2 [M, K/2] with E8M0 a_scale [M, K/32]; w: fp4x2 [N, K/2] with
+    w_scale [N, K/32]."""
+    a = _u8(a, "a")
+    w = _u8(w, "w")
+    M, K2 = a.shape
+    K = 2 * K2
+    N = w.shape[0]
+    lda = _matrix(a, "a", M, K2)
+    ldw = _matrix(w, "w", N, K2)
+    for t, name, rows in ((a_scale, "a_scale", M), (w_scale, "w_scale", N)):
+        if t.dtype != torch.uint8 or tuple(t.shape) != (rows, K // 32) or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous uint8 [%d, %d] tensor" % (name, rows, K // 32))
+    if epilogue != EPI_NONE:
+        if bias is None or bias.dtype != torch.bfloat16 or bias.shape != (N,) \
+                or not bias.is_contiguous():
+            raise ValueError("this epilogue needs a contiguous bf16 bias [N]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    ldy = _matrix(y, "y", M, N)
+    need = bs_workspace_bytes(3, M, N, K)
+    if need and workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=a.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().gemm_mxfp4_w4a4(_ptr(a), lda, _ptr(a_scale), _ptr(w), ldw, _ptr(w_scale),
+                                        _ptr(bias if epilogue != EPI_NONE else None),
+                                        int(epilogue), _ptr(y), ldy, M, N, K, _ptr(workspace),
+                                        ws_bytes, ctypes.c_void_p(_stream(stream)))
+    if st != BS_OK:
+        raise BsError(st, "gemm_mxfp4_w4a4")
+    return y
 
 
 def gemm_mxfp4_w4a8(a, a_scale, w, w_scale, bias=None, epilogue=EPI_NONE, y=None,

@@ -140,6 +140,22 @@ __device__ __forceinline__ v16f mfma32_wt(const v8i &w, const v8i &a, const v16f
                                                            sw, 0, E8M0_ONE);
 }
 
+// Both operands' formats chosen (W4A4: fp4 activations with their own
+// per-lane E8M0 scales).
+template <bool FP4W, bool FP4A>
+__device__ __forceinline__ v4f mfma16x(const v8i &a, const v8i &b, const v4f &c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        a, b, c, FP4A ? MFMA_FMT_FP4 : MFMA_FMT_FP8, FP4W ? MFMA_FMT_FP4 : MFMA_FMT_FP8, 0, sa, 0, sb);
+}
+
+// Weights as the instruction's A operand (scale sw), activations as its B
+// operand (scale sa: E8M0_ONE for e4m3 activations).
+template <bool FP4W, bool FP4A>
+__device__ __forceinline__ v16f mfma32_wt2(const v8i &w, const v8i &a, const v16f &c, int sw, int sa) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        w, a, c, FP4W ? MFMA_FMT_FP4 : MFMA_FMT_FP8, FP4A ? MFMA_FMT_FP4 : MFMA_FMT_FP8, 0, sw, 0, sa);
+}
+
 __device__ __forceinline__ v8i pack8(const uint4 &lo, const uint4 &hi) {
     v8i r;
     r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;

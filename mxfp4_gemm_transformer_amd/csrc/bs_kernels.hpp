@@ -12,6 +12,10 @@ hipError_t launch_quant_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_
                              float *scale, int64_t M, int64_t K, hipStream_t stream);
 
 // Quantization with one given scale (device scalar); scale_out [M] may be NULL.
+// MXFP4 (OCP MX) quantization of bf16 rows: packed [M, K/2], E8M0 [M, K/32].
+hipError_t launch_quant_mxfp4_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_t ld_q,
+                                   uint8_t *scale, int64_t M, int64_t K, hipStream_t stream);
+
 hipError_t launch_quant_rows_static(const uint16_t *x, int64_t ld_x, const float *scale_in,
                                     uint8_t *q, int64_t ld_q, float *scale_out, int64_t M,
                                     int64_t K, hipStream_t stream);
@@ -43,5 +47,21 @@ hipError_t launch_gemm_prefill(bool fp4, const uint8_t *a, int64_t lda, const fl
                                const uint8_t *w, int64_t ldw, const uint8_t *ws, const float *cs,
                                const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
                                int64_t N, int64_t K, int num_cus, hipStream_t stream);
+
+// W4A4 (fp4 activations [M, K/2] with E8M0 scales [M, K/32], MXFP4
+// weights). Decode: M <= DECODE_MAX_M, split-K through the workspace
+// (decode_workspace_bytes_w4a4 bytes). Prefill: M > DECODE_MAX_M,
+// K % 64 == 0.
+hipError_t launch_gemm_decode_w4a4(const uint8_t *a, int64_t lda, const uint8_t *a_e8m0,
+                                   const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                                   const uint16_t *bias, int epi, uint16_t *y, int64_t ldy,
+                                   int64_t M, int64_t N, int64_t K, void *workspace,
+                                   hipStream_t stream);
+size_t decode_workspace_bytes_w4a4(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_prefill_w4a4(const uint8_t *a, int64_t lda, const uint8_t *a_e8m0,
+                                    const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                                    const uint16_t *bias, int epi, uint16_t *y, int64_t ldy,
+                                    int64_t M, int64_t N, int64_t K, int num_cus,
+                                    hipStream_t stream);
 
 }  // namespace bsg

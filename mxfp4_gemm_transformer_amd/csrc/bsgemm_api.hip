@@ -197,9 +197,61 @@ int fp8_quant_rows_static(const void *x_bf16, int64_t ld_x, const float *scale_i
     return e == hipSuccess ? BS_OK : BS_ELAUNCH;
 }
 
+int fp4_quant_rows(const void *x_bf16, int64_t ld_x, void *q_fp4x2, int64_t ld_q, uint8_t *scale,
+                   int64_t M, int64_t K, void *stream) {
+    if (!x_bf16 || !q_fp4x2 || !scale) return BS_EINVAL;
+    if (M < 1 || K < 32 || K % 32 || M > INT32_MAX || K > INT32_MAX) return BS_EINVAL;
+    if (ld_x < K || ld_q < K / 2) return BS_EINVAL;
+    if (!aligned16(x_bf16) || !aligned16(q_fp4x2) || (2 * ld_x) % 16 || ld_q % 16)
+        return BS_EALIGN;
+    int num_cus = 0;
+    int st = device_check(&num_cus);
+    if (st != BS_OK) return st;
+    hipError_t e = bsg::launch_quant_mxfp4_rows(static_cast<const uint16_t *>(x_bf16), ld_x,
+                                                static_cast<uint8_t *>(q_fp4x2), ld_q, scale, M, K,
+                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BS_OK : BS_ELAUNCH;
+}
+
+int gemm_mxfp4_w4a4(const void *a_fp4x2, int64_t ld_a, const uint8_t *a_scale, const void *w_fp4x2,
+                    int64_t ld_w, const uint8_t *w_scale, const void *bias_bf16, int epilogue,
+                    void *y_bf16, int64_t ld_y, int64_t M, int64_t N, int64_t K, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    if (!a_fp4x2 || !a_scale || !w_fp4x2 || !w_scale || !y_bf16) return BS_EINVAL;
+    if (M < 1 || N < 32 || K < 32 || N % 32 || K % 32) return BS_EINVAL;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return BS_EINVAL;
+    if (M > bsg::DECODE_MAX_M && K % 64) return BS_EINVAL;   // the prefill kernel takes whole 64-k steps
+    if (epilogue < BS_EPI_NONE || epilogue > BS_EPI_BIAS_GELU_TANH) return BS_EINVAL;
+    if (epilogue != BS_EPI_NONE && !bias_bf16) return BS_EINVAL;
+    if (ld_a < K / 2 || ld_w < K / 2 || ld_y < N) return BS_EINVAL;
+    if (ld_a > BS_MAX_LD_BYTES || ld_w > BS_MAX_LD_BYTES) return BS_EINVAL;
+    if (!aligned16(a_fp4x2) || !aligned16(w_fp4x2) || !aligned16(y_bf16)) return BS_EALIGN;
+    if (ld_a % 16 || ld_w % 16 || (2 * ld_y) % 16) return BS_EALIGN;
+    if (bias_bf16 && (reinterpret_cast<uintptr_t>(bias_bf16) & 1u) != 0) return BS_EALIGN;
+    const size_t ws_need = bs_workspace_bytes(3, M, N, K);
+    if (workspace_bytes < ws_need) return BS_EWORKSPACE;
+    if (ws_need && (!workspace || !aligned16(workspace))) return workspace ? BS_EALIGN : BS_EWORKSPACE;
+    int num_cus = 0;
+    int st = device_check(&num_cus);
+    if (st != BS_OK) return st;
+    const auto *a = static_cast<const uint8_t *>(a_fp4x2);
+    const auto *w = static_cast<const uint8_t *>(w_fp4x2);
+    const auto *bias = static_cast<const uint16_t *>(bias_bf16);
+    auto *y = static_cast<uint16_t *>(y_bf16);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (M <= bsg::DECODE_MAX_M)
+        e = bsg::launch_gemm_decode_w4a4(a, ld_a, a_scale, w, ld_w, w_scale, bias, epilogue, y,
+                                         ld_y, M, N, K, workspace, s);
+    else
+        e = bsg::launch_gemm_prefill_w4a4(a, ld_a, a_scale, w, ld_w, w_scale, bias, epilogue, y,
+                                          ld_y, M, N, K, num_cus, s);
+    return e == hipSuccess ? BS_OK : BS_ELAUNCH;
+}
+
 size_t bs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
-    (void)op;
     if (M < 1 || N < 1 || K < 1) return 0;
+    if (op == 3) return bsg::decode_workspace_bytes_w4a4(M, N, K);   // W4A4: split-K decode
     return bsg::decode_workspace_bytes(M, N, K);   // split-K decode partial sums, else 0
 }
 

@@ -477,11 +477,14 @@ __host__ __device__ inline bool large_splitk(int64_t M, int64_t N, int64_t K) {
     return M >= 2 && M <= 8 && N * K >= ((int64_t)1 << 26);
 }
 
-template <bool FP4, int MT>
+// FP4A (W4A4): the activations are fp4 [M, K/2] with E8M0 scales AS
+// [M, K/32], staged in LDS as packed bytes plus a 32-byte scale row per token.
+template <bool FP4, int MT, bool FP4A = false>
 __global__ __launch_bounds__(256) void gemm_decode_splitk_kernel(
     const uint8_t *__restrict__ A, int64_t lda, const uint8_t *__restrict__ W, int64_t ldw,
-    const uint8_t *__restrict__ WS, float *__restrict__ part, int M, int N, int K, int S) {
-    extern __shared__ __align__(16) uint8_t lds[];   // [16 MT][span + 16] activations
+    const uint8_t *__restrict__ WS, float *__restrict__ part, int M, int N, int K, int S,
+    const uint8_t *__restrict__ AS = nullptr) {
+    extern __shared__ __align__(16) uint8_t lds[];   // [16 MT][span + 16] activations (+ scales)
     constexpr int TOK = 16 * MT;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = lane & 15, g = lane >> 4;
@@ -491,8 +494,10 @@ __global__ __launch_bounds__(256) void gemm_decode_splitk_kernel(
     const int sp = blockIdx.y;
     const int st0 = min(steps, sp * per), st1 = min(steps, st0 + per);
     const int kbeg = st0 * 128;
-    const int span = per * 128;                       // bytes of k per token staged
+    const int span = per * (FP4A ? 64 : 128);         // bytes of k per token staged
     const int lds_row = span + 16;
+    constexpr int SROW = SPLIT_MAX_STEPS * 4;          // FP4A: scale bytes per token
+    uint8_t *s_lds = lds + TOK * lds_row;
     const int row0 = blockIdx.x * 64;
     const int n = row0 + 16 * wave + i;               // this lane's weight row
 
@@ -504,8 +509,24 @@ __global__ __launch_bounds__(256) void gemm_decode_splitk_kernel(
 #pragma unroll
     for (int j = 0; j < ACH; ++j) {
         const int c = threadIdx.x + j * 256;
-        const int t = c / kc, k = kbeg + 16 * (c % kc);
-        av[j] = bload16(rsA, ((c < chunks) & (t < M) & (k < K)) ? (uint32_t)(t * lda + k) : OOB_OFF);
+        const int t = c / kc;
+        // element and byte offset of this chunk (fp4: 32 elements in 16 bytes)
+        const int ke = kbeg + (FP4A ? 32 : 16) * (c % kc);
+        const int kb = FP4A ? (kbeg >> 1) + 16 * (c % kc) : ke;
+        av[j] = bload16(rsA, ((c < chunks) & (t < M) & (ke < K)) ? (uint32_t)(t * lda + kb) : OOB_OFF);
+    }
+    constexpr int SCH = FP4A ? TOK * SROW / 256 : 1;   // activation scale bytes per thread
+    uint32_t asv[SCH];
+    if (FP4A) {
+        const __amdgpu_buffer_rsrc_t rsSA = make_rsrc(AS, (int64_t)M * KB);
+#pragma unroll
+        for (int j = 0; j < SCH; ++j) {
+            const int c = threadIdx.x + j * 256;
+            const int t = c / SROW, b = c % SROW, blk = (kbeg >> 5) + b;
+            asv[j] = __builtin_amdgcn_raw_buffer_load_b8(
+                rsSA, ((t < M) & (b < 4 * (st1 - st0)) & (blk < KB)) ? (uint32_t)(t * KB + blk) : OOB_OFF,
+                0, 0);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -541,6 +562,10 @@ __global__ __launch_bounds__(256) void gemm_decode_splitk_kernel(
         const int t = c / kc, k = 16 * (c % kc);
         if (c < chunks) *reinterpret_cast<uint4 *>(lds + t * lds_row + k) = av[j];
     }
+    if (FP4A) {
+#pragma unroll
+        for (int j = 0; j < SCH; ++j) s_lds[threadIdx.x + j * 256] = (uint8_t)asv[j];
+    }
     __syncthreads();
 
     v4f acc[MT];
@@ -549,14 +574,21 @@ __global__ __launch_bounds__(256) void gemm_decode_splitk_kernel(
 #pragma unroll
     for (int u = 0; u < SPLIT_MAX_STEPS; ++u) {
         if (st0 + u < st1) {   // uniform
-            const int kl = u * 128;                       // offset in the staged slice
+            const int kl = u * (FP4A ? 64 : 128);        // offset in the staged slice
             const v8i wv = pack8(wlo[u], FP4 ? make_uint4(0u, 0u, 0u, 0u) : whi[FP4 ? 0 : u]);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const uint8_t *arow = lds + (mt * 16 + i) * lds_row + kl;
-                const v8i a8 = pack8(*reinterpret_cast<const uint4 *>(arow + 16 * g),
-                                     *reinterpret_cast<const uint4 *>(arow + 64 + 16 * g));
-                acc[mt] = mfma16<FP4>(a8, wv, acc[mt], E8M0_ONE, WS ? (int)wsc[u] : E8M0_ONE);
+                if (FP4A) {
+                    const v8i a8 = pack8(*reinterpret_cast<const uint4 *>(arow + 16 * g),
+                                         make_uint4(0u, 0u, 0u, 0u));
+                    const int sa = s_lds[(mt * 16 + i) * SROW + 4 * u + g];
+                    acc[mt] = mfma16x<FP4, true>(a8, wv, acc[mt], sa, (int)wsc[u]);
+                } else {
+                    const v8i a8 = pack8(*reinterpret_cast<const uint4 *>(arow + 16 * g),
+                                         *reinterpret_cast<const uint4 *>(arow + 64 + 16 * g));
+                    acc[mt] = mfma16<FP4>(a8, wv, acc[mt], E8M0_ONE, WS ? (int)wsc[u] : E8M0_ONE);
+                }
             }
         }
     }
@@ -603,7 +635,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     if (epi != EPI_NONE)   // bias is only 2-byte aligned
         bq = make_float4(bf16_to_f32(bias[c0]), bf16_to_f32(bias[c0 + 1]),
                          bf16_to_f32(bias[c0 + 2]), bf16_to_f32(bias[c0 + 3]));
-    const float as = a_scale[t];
+    const float as = a_scale ? a_scale[t] : 1.0f;   // W4A4: the scales are in the blocks
     const float4 cq = colscale ? *reinterpret_cast<const float4 *>(colscale + c0)
                                : make_float4(1.f, 1.f, 1.f, 1.f);
     const uint32_t o01 = pack_bf16x2(epilogue(sum.x, as, cq.x, bq.x, epi),
@@ -613,16 +645,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     *reinterpret_cast<uint2 *>(Y + (int64_t)t * ldy + c0) = make_uint2(o01, o23);
 }
 
-template <bool FP4, int MT>
+template <bool FP4, int MT, bool FP4A = false>
 hipError_t launch_splitk(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w,
                          int64_t ldw, const uint8_t *ws, const float *cs, const uint16_t *bias,
                          int epi, uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
-                         float *part, hipStream_t st) {
+                         float *part, hipStream_t st, const uint8_t *a_e8m0 = nullptr) {
     const int64_t S = decode_splits(N, K);
     const int64_t steps = (K + 127) / 128, per = (steps + S - 1) / S;
-    const size_t lds = (size_t)16 * MT * (per * 128 + 16);
-    hipLaunchKernelGGL((gemm_decode_splitk_kernel<FP4, MT>), dim3((unsigned)((N + 63) / 64), (unsigned)S),
-                       dim3(256), lds, st, a, lda, w, ldw, ws, part, (int)M, (int)N, (int)K, (int)S);
+    const size_t lds = (size_t)16 * MT * (per * (FP4A ? 64 : 128) + 16) +
+                       (FP4A ? (size_t)16 * MT * SPLIT_MAX_STEPS * 4 : 0);
+    hipLaunchKernelGGL((gemm_decode_splitk_kernel<FP4, MT, FP4A>),
+                       dim3((unsigned)((N + 63) / 64), (unsigned)S), dim3(256), lds, st, a, lda, w,
+                       ldw, ws, part, (int)M, (int)N, (int)K, (int)S, a_e8m0);
     const int64_t quads = M * N / 4;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st,
                        part, as, cs, bias, epi, y, ldy, (int)M, (int)N, (int)S);
@@ -687,6 +721,27 @@ hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const flo
     default: return fp4 ? launch_splitk<true, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, part, st)
                         : launch_splitk<false, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, part, st);
     }
+}
+
+// W4A4 decode: the split-K kernel for every M <= DECODE_MAX_M (fp4
+// activations staged with their scales); no per-token scale.
+hipError_t launch_gemm_decode_w4a4(const uint8_t *a, int64_t lda, const uint8_t *a_e8m0,
+                                   const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                                   const uint16_t *bias, int epi, uint16_t *y, int64_t ldy,
+                                   int64_t M, int64_t N, int64_t K, void *workspace,
+                                   hipStream_t st) {
+    float *part = static_cast<float *>(workspace);
+    switch ((M + 15) / 16) {
+    case 1: return launch_splitk<true, 1, true>(a, lda, nullptr, w, ldw, ws, nullptr, bias, epi, y, ldy, M, N, K, part, st, a_e8m0);
+    case 2: return launch_splitk<true, 2, true>(a, lda, nullptr, w, ldw, ws, nullptr, bias, epi, y, ldy, M, N, K, part, st, a_e8m0);
+    case 3: return launch_splitk<true, 3, true>(a, lda, nullptr, w, ldw, ws, nullptr, bias, epi, y, ldy, M, N, K, part, st, a_e8m0);
+    default: return launch_splitk<true, 4, true>(a, lda, nullptr, w, ldw, ws, nullptr, bias, epi, y, ldy, M, N, K, part, st, a_e8m0);
+    }
+}
+
+size_t decode_workspace_bytes_w4a4(int64_t M, int64_t N, int64_t K) {
+    if (M > DECODE_MAX_M) return 0;
+    return (size_t)decode_splits(N, K) * (size_t)M * (size_t)N * sizeof(float);
 }
 
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {

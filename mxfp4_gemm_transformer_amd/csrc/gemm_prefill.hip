@@ -375,18 +375,20 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-template <bool FP4, int BM, int BN, int NBUF, int WGM, int WGN>
+template <bool FP4, int BM, int BN, int NBUF, int WGM, int WGN, bool FP4A = false>
 struct DCfg {
     static constexpr int NW = WGM * WGN;              // waves, WGM x WGN
     static constexpr int NT = NW * 64;
     static constexpr int WROW = FP4 ? BK / 2 : BK;    // W bytes per row per step
-    static constexpr int A_STAGE = BM * BK;
+    static constexpr int AROW = FP4A ? BK / 2 : BK;   // A bytes per row per step
+    static constexpr int A_STAGE = BM * AROW;
     static constexpr int W_STAGE = BN * WROW;
     static constexpr int SC_OFF = A_STAGE + W_STAGE;  // one 4-byte scale slot per thread
-    static constexpr int STAGE = SC_OFF + 4 * NT;
+    static constexpr int SCA_OFF = SC_OFF + 4 * NT;   // fp4 activations: their scale slots
+    static constexpr int STAGE = SC_OFF + 4 * NT * (FP4A ? 2 : 1);
     static constexpr int A_LD = A_STAGE / 16 / NT;    // 16-byte loads per thread per step
     static constexpr int W_LD = W_STAGE / 16 / NT;
-    static constexpr int LPS = A_LD + W_LD + 1;       // loads per thread per stage
+    static constexpr int LPS = A_LD + W_LD + 1 + (FP4A ? 1 : 0);   // loads per thread per stage
     static constexpr int TM = BM / WGM / 32;
     static constexpr int TN = BN / WGN / 32;
     static constexpr int SC_ROWS = FP4 ? BN : BN / 32;
@@ -399,18 +401,22 @@ struct DCfg {
     static constexpr int LDS = NBUF * STAGE > EP_ALL ? NBUF * STAGE : EP_ALL;
     static_assert(A_STAGE % (16 * NT) == 0 && W_STAGE % (16 * NT) == 0, "stage split");
     static_assert(SC_ROWS <= NT, "one scale row per thread");
+    static_assert(!FP4A || BM <= NT, "one activation scale row per thread");
     static_assert(NBUF >= 4, "the ring needs NBUF - 1 >= 3 stages in flight");
     static_assert(LPS * (NBUF - 3) <= 63, "vmcnt range");
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <bool FP4, int BM, int BN, int NBUF, int WGM, int WGN>
+// FP4A: fp4 activations [M, K/2] with E8M0 scales AS [M, K/32] (W4A4); then
+// a_scale is unused (1).
+template <bool FP4, int BM, int BN, int NBUF, int WGM, int WGN, bool FP4A = false>
 __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     const uint8_t *__restrict__ A, int64_t lda, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ W, int64_t ldw, const uint8_t *__restrict__ WS,
     const float *__restrict__ colscale, const uint16_t *__restrict__ bias, int epi,
-    uint16_t *__restrict__ Y, int64_t ldy, int M, int N, int K, int group_m) {
-    using C = DCfg<FP4, BM, BN, NBUF, WGM, WGN>;
+    uint16_t *__restrict__ Y, int64_t ldy, int M, int N, int K, int group_m,
+    const uint8_t *__restrict__ AS = nullptr) {
+    using C = DCfg<FP4, BM, BN, NBUF, WGM, WGN, FP4A>;
     __shared__ __align__(16) uint8_t lds[C::LDS];
 
     // ---- tile of this workgroup (XCD-aware grouped order)
@@ -443,13 +449,21 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         (void *)(WS ? WS + (int64_t)srow0 * KB : WS), (short)0,
         (int)(s_bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : s_bytes), 0x00020000);
 
+    const int64_t sa_bytes = FP4A ? (int64_t)(M - m0) * KB : 0;
+    const __amdgpu_buffer_rsrc_t rsSA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(FP4A ? AS + (int64_t)m0 * KB : AS), (short)0,
+        (int)(sa_bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : sa_bytes), 0x00020000);
+
     // This thread's 16-byte chunk of each load: physical chunk j*NT + tid of
     // a stage (where the LDS-mode load of wave w, lane l, puts its bytes)
     // holds logical chunk c of its row, c = physical column ^ swizzle(row).
-    constexpr int A_ROWS_PER_J = C::NT / 4;
+    constexpr int A_ROWS_PER_J = FP4A ? C::NT / 2 : C::NT / 4;
     constexpr int W_ROWS_PER_J = FP4 ? C::NT / 2 : C::NT / 4;
     uint32_t a_off, w_off;
-    {
+    if (FP4A) {
+        const int row = tid >> 1, c = (tid & 1) ^ swz2(row);
+        a_off = (uint32_t)(row * lda) + 16 * c;
+    } else {
         const int row = tid >> 2, c = (tid & 3) ^ swz4(row);
         a_off = (uint32_t)(row * lda) + 16 * c;
     }
@@ -461,6 +475,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         w_off = (uint32_t)(row * ldw) + 16 * c;
     }
     const uint32_t s_off = tid < C::SC_ROWS ? (uint32_t)(tid * KB) : OOB;
+    const uint32_t sa_off = tid < BM ? (uint32_t)(tid * KB) : OOB;
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t *)lds);
 
     // Load i (0 .. LPS-1) of step s into ring buffer s % NBUF: the A chunks,
@@ -472,14 +487,17 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         const uint32_t base = lds0 + (uint32_t)((s % NBUF) * C::STAGE) + (uint32_t)wave * 1024u;
         if (i < C::A_LD) {
             dma_b128(rsA, base + i * C::NT * 16, live ? a_off : OOB,
-                     (uint32_t)(i * A_ROWS_PER_J * lda) + kbase);
+                     (uint32_t)(i * A_ROWS_PER_J * lda) + (FP4A ? kbase / 2 : kbase));
         } else if (i < C::A_LD + C::W_LD) {
             const int j = i - C::A_LD;
             dma_b128(rsW, base + C::A_STAGE + j * C::NT * 16, live ? w_off : OOB,
                      (uint32_t)(j * W_ROWS_PER_J * ldw) + (FP4 ? kbase / 2 : kbase));
-        } else {
+        } else if (i == C::A_LD + C::W_LD) {
             dma_u16(rsS, lds0 + (uint32_t)((s % NBUF) * C::STAGE + C::SC_OFF) + (uint32_t)wave * 256u,
                     live ? s_off + (kbase >> 5) : OOB);
+        } else {   // FP4A: the activation rows' scale pairs
+            dma_u16(rsSA, lds0 + (uint32_t)((s % NBUF) * C::STAGE + C::SCA_OFF) + (uint32_t)wave * 256u,
+                    live ? sa_off + (kbase >> 5) : OOB);
         }
     };
 
@@ -495,14 +513,22 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         v8i a[C::TM];
         v8i b[C::TN];
         int sc[C::TN];
+        int sa[C::TM];
     };
     // fragments of step s (ring buffer s % NBUF): A tile a, W tile b (+ its scales)
     auto read_a = [&](Frags &f, int s, int a) {
         const uint8_t *sa = lds + (s % NBUF) * C::STAGE;
         const int row = wm * (BM / WGM) + a * 32 + li;
-        const int fz = swz4(row);
-        const uint8_t *p = sa + row * BK;
-        f.a[a] = pack8(lds16(p + 16 * (lg ^ fz)), lds16(p + 16 * ((2 + lg) ^ fz)));
+        if (FP4A) {
+            f.a[a] = pack8(lds16(sa + row * C::AROW + 16 * (lg ^ swz2(row))),
+                           make_uint4(0u, 0u, 0u, 0u));
+            f.sa[a] = (sa + C::SCA_OFF)[4 * row + lg];
+        } else {
+            const int fz = swz4(row);
+            const uint8_t *p = sa + row * BK;
+            f.a[a] = pack8(lds16(p + 16 * (lg ^ fz)), lds16(p + 16 * ((2 + lg) ^ fz)));
+            f.sa[a] = E8M0_ONE;
+        }
     };
     auto read_b = [&](Frags &f, int s, int b) {
         const uint8_t *sw = lds + (s % NBUF) * C::STAGE + C::A_STAGE;
@@ -543,7 +569,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         for (int a = 0; a < C::TM; ++a)
 #pragma unroll
             for (int b = 0; b < C::TN; ++b)
-                acc[a][b] = mfma32_wt<FP4>(f.b[b], f.a[a], acc[a][b], f.sc[b]);
+                acc[a][b] = mfma32_wt2<FP4, FP4A>(f.b[b], f.a[a], acc[a][b], f.sc[b], f.sa[a]);
     };
     auto interleave = [&]() {
         constexpr int NM = C::TM * C::TN;
@@ -609,7 +635,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
 #pragma unroll
     for (int a = 0; a < C::TM; ++a) {
         const int m = m0 + wm * (BM / WGM) + a * 32 + li;
-        asv[a] = a_scale[m < M ? m : 0];   // rows past M are not stored
+        asv[a] = FP4A ? 1.0f : a_scale[m < M ? m : 0];   // rows past M are not stored
     }
 #pragma unroll
     for (int a = 0; a < C::TM; ++a) {
@@ -646,15 +672,15 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     }
 }
 
-template <bool FP4, int BM, int BN, int NBUF, int WGM = 2, int WGN = 2>
+template <bool FP4, int BM, int BN, int NBUF, int WGM = 2, int WGN = 2, bool FP4A = false>
 hipError_t launch_tile_dma(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w,
                            int64_t ldw, const uint8_t *ws, const float *cs, const uint16_t *bias,
                            int epi, uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
-                           hipStream_t st) {
-    auto kern = gemm_prefill_dma_kernel<FP4, BM, BN, NBUF, WGM, WGN>;
+                           hipStream_t st, const uint8_t *a_e8m0 = nullptr) {
+    auto kern = gemm_prefill_dma_kernel<FP4, BM, BN, NBUF, WGM, WGN, FP4A>;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(WGM * WGN * 64), 0, st, a, lda, as, w,
-                       ldw, ws, cs, bias, epi, y, ldy, (int)M, (int)N, (int)K, 8);
+                       ldw, ws, cs, bias, epi, y, ldy, (int)M, (int)N, (int)K, 8, a_e8m0);
     return hipGetLastError();
 }
 
@@ -691,7 +717,23 @@ int best_shape(bool fp4, int64_t M, int64_t N, int64_t K, int num_cus, double *c
 hipError_t launch_shape(int shape, bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
                         const uint8_t *w, int64_t ldw, const uint8_t *ws, const float *cs,
                         const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
-                        int64_t N, int64_t K, hipStream_t st) {
+                        int64_t N, int64_t K, hipStream_t st, const uint8_t *a_e8m0) {
+    if (a_e8m0) {   // W4A4: fp4 activations with their E8M0 scales, MXFP4 weights
+        switch (shape) {
+        case 0:
+            return launch_tile_dma<true, 256, 256, 4, 4, 2, true>(a, lda, a_scale, w, ldw, ws, cs,
+                                                                  bias, epi, y, ldy, M, N, K, st,
+                                                                  a_e8m0);
+        case 1:
+            return launch_tile_dma<true, 256, 128, 4, 2, 2, true>(a, lda, a_scale, w, ldw, ws, cs,
+                                                                  bias, epi, y, ldy, M, N, K, st,
+                                                                  a_e8m0);
+        default:
+            return launch_tile_dma<true, 128, 128, 4, 2, 2, true>(a, lda, a_scale, w, ldw, ws, cs,
+                                                                  bias, epi, y, ldy, M, N, K, st,
+                                                                  a_e8m0);
+        }
+    }
     switch (shape) {
     case 0:
         // MXFP4 weights: eight waves (4 x 2, each 64 x 128) measured faster
@@ -721,7 +763,8 @@ hipError_t launch_shape(int shape, bool fp4, const uint8_t *a, int64_t lda, cons
 hipError_t launch_prefill_dma(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
                               const uint8_t *w, int64_t ldw, const uint8_t *ws, const float *cs,
                               const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
-                              int64_t N, int64_t K, int num_cus, hipStream_t st) {
+                              int64_t N, int64_t K, int num_cus, hipStream_t st,
+                              const uint8_t *a_e8m0 = nullptr) {
     double one_cost = 0.0;
     const int one = best_shape(fp4, M, N, K, num_cus, &one_cost);
     const int64_t mt = (M + 255) / 256, t256 = mt * ((N + 255) / 256);
@@ -734,7 +777,7 @@ hipError_t launch_prefill_dma(bool fp4, const uint8_t *a, int64_t lda, const flo
         const int two = best_shape(fp4, M, N - n1, K, num_cus, &c2);
         if (c1 + c2 + LAUNCH_COST < one_cost) {
             hipError_t e = launch_shape(0, fp4, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy,
-                                        M, n1, K, st);
+                                        M, n1, K, st, a_e8m0);
             if (e != hipSuccess) return e;
             const int64_t kb = K / 32;
             const uint8_t *w2 = w + n1 * ldw;
@@ -742,13 +785,22 @@ hipError_t launch_prefill_dma(bool fp4, const uint8_t *a, int64_t lda, const flo
             const float *cs2 = cs ? cs + n1 : nullptr;
             const uint16_t *bias2 = bias ? bias + n1 : nullptr;
             return launch_shape(two, fp4, a, lda, a_scale, w2, ldw, ws2, cs2, bias2, epi, y + n1,
-                                ldy, M, N - n1, K, st);
+                                ldy, M, N - n1, K, st, a_e8m0);
         }
     }
-    return launch_shape(one, fp4, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
+    return launch_shape(one, fp4, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st,
+                        a_e8m0);
 }
 
 }  // namespace
+
+hipError_t launch_gemm_prefill_w4a4(const uint8_t *a, int64_t lda, const uint8_t *a_e8m0,
+                                    const uint8_t *w, int64_t ldw, const uint8_t *ws,
+                                    const uint16_t *bias, int epi, uint16_t *y, int64_t ldy,
+                                    int64_t M, int64_t N, int64_t K, int num_cus, hipStream_t st) {
+    return launch_prefill_dma(true, a, lda, nullptr, w, ldw, ws, nullptr, bias, epi, y, ldy, M, N,
+                              K, num_cus, st, a_e8m0);
+}
 
 hipError_t launch_gemm_prefill(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
                                const uint8_t *w, int64_t ldw, const uint8_t *ws, const float *cs,

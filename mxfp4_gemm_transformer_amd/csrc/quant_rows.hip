@@ -422,6 +422,58 @@ __global__ __launch_bounds__(256) void quant_static_kernel(const uint16_t *__res
     }
 }
 
+// MXFP4 quantization (OCP MX): per 32-element block, the E8M0 byte of
+// floor(log2 amax) - 2 (the exponent field of the bf16 amax minus 2, clamped
+// at 0; a zero block gets 0), and each element's e2m1 code of x / 2^(byte -
+// 127), nearest with ties to the even code, saturating at 6, sign kept. The
+// division by a power of two is an exact scaling (a product that would be
+// subnormal is far below the first rounding threshold, 0.25).
+__device__ __forceinline__ uint32_t e2m1_mag(float a) {
+    return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+           (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+           (uint32_t)(a > 5.0f);
+}
+
+__global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t *__restrict__ x,
+                                                          int64_t ldx, uint8_t *__restrict__ q,
+                                                          int64_t ldq, uint8_t *__restrict__ sc,
+                                                          int64_t M, int K) {
+    const int KB = K >> 5;
+    const int64_t total = M * KB;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * 256) {
+        const int64_t m = idx / KB;
+        const int b = (int)(idx - m * KB);
+        const uint16_t *xb = x + m * ldx + 32 * b;
+        uint4 c[4];
+        uint32_t amax = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            c[j] = ldg16(xb + 8 * j);
+            amax = max(amax, absmax8(c[j]));
+        }
+        const uint32_t e = amax >> 7;                       // bf16 exponent field of amax
+        const uint32_t byte = e >= 2 ? e - 2 : 0;
+        const float inv = __uint_as_float((254u - byte) << 23);   // 2^(127 - byte)
+        uint32_t out[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w[4] = {c[j].x, c[j].y, c[j].z, c[j].w};
+            uint32_t word = 0;
+#pragma unroll
+            for (int h = 0; h < 8; ++h) {
+                const uint32_t bits = (w[h >> 1] >> (16 * (h & 1))) & 0xFFFFu;
+                const float v = bf16_to_f32(bits & 0x7FFFu) * inv;
+                const uint32_t code = e2m1_mag(v) | ((bits >> 12) & 8u);
+                word |= code << (4 * h);
+            }
+            out[j] = word;
+        }
+        *reinterpret_cast<uint4 *>(q + m * ldq + 16 * b) = make_uint4(out[0], out[1], out[2], out[3]);
+        sc[m * KB + b] = (uint8_t)byte;
+    }
+}
+
 // Thread count per row for a producer: the quantizer's choice, widened
 // until each thread holds at most 16 chunks (8 for 128 threads per row).
 template <int PROD>
@@ -460,6 +512,15 @@ hipError_t launch_add_rms_quant(const uint16_t *x, int64_t ld_x, uint16_t *resid
         ? launch_producer<PROD_ADD_RMS>(x, ld_x, q, ld_q, scale, M, (int)K, pp, stream)
         : launch_producer<PROD_RMS>(x, ld_x, q, ld_q, scale, M, (int)K, pp, stream);
     return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+hipError_t launch_quant_mxfp4_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_t ld_q,
+                                   uint8_t *scale, int64_t M, int64_t K, hipStream_t stream) {
+    const int64_t blocks32 = M * (K / 32);
+    const int64_t grid = (blocks32 + 255) / 256;
+    hipLaunchKernelGGL(quant_mxfp4_kernel, dim3((unsigned)(grid < 8192 ? grid : 8192)), dim3(256),
+                       0, stream, x, ld_x, q, ld_q, scale, M, (int)K);
+    return hipGetLastError();
 }
 
 hipError_t launch_quant_rows_static(const uint16_t *x, int64_t ld_x, const float *scale_in,

@@ -21,6 +21,8 @@ fused gate_up):
   ffn_up   M=2048, N=4096, K=1024, e4m3 W, bias + tanh-GELU (second variant
            bias only)
   gate_up  M in {1,16,512,4096}, N=34816, K=5120, MXFP4 W (e2m1 + 1x32 E8M0)
+  gate_up_w4a4  the gate_up layer with MXFP4 activations too (W4A4: the
+           activations quantized per 32 by the OCP MX rule)
   lm_head  M in {1,8,16}, N=248320, K=5120, e4m3 W with one fp32 scale per
            output channel (the sly-radiance README's fp8 lm_head: weight
            quantized per output channel, per-token fp8 activations)
@@ -60,7 +62,7 @@ class Workload:
     M: int
     N: int
     K: int
-    fmt: str               # "fp8" (e4m3 W, 32x32 scales), "mxfp4" or "fp8_rowwise"
+    fmt: str               # "fp8" (e4m3 W, 32x32 scales), "mxfp4", "mxfp4_w4a4" or "fp8_rowwise"
     epilogue: int
     outlier_frac: float = 0.0
     m_sweep: tuple = ()
@@ -73,6 +75,8 @@ WORKLOADS = {
     "ffn_up": Workload("ffn_up", 2048, 4096, 1024, "fp8", EPI_BIAS_GELU_TANH),
     "ffn_up_bias": Workload("ffn_up_bias", 2048, 4096, 1024, "fp8", EPI_BIAS),
     "gate_up": Workload("gate_up", 16, 34816, 5120, "mxfp4", EPI_NONE, m_sweep=(1, 16, 512, 4096)),
+    "gate_up_w4a4": Workload("gate_up_w4a4", 4096, 34816, 5120, "mxfp4_w4a4", EPI_NONE,
+                             m_sweep=(16, 512, 4096)),
     "lm_head": Workload("lm_head", 8, 248320, 5120, "fp8_rowwise", EPI_NONE, m_sweep=(1, 8, 16)),
 }
 

@@ -141,6 +141,28 @@ def test_rowwise_and_static_argument_checks():
     assert st(ldq=72) == A
 
 
+def test_w4a4_argument_checks():
+    lib = bs.load_library()
+    E, A, W = bs.BS_EINVAL, bs.BS_EALIGN, bs.BS_EWORKSPACE
+    fn = lib.gemm_mxfp4_w4a4
+    need = bs.bs_workspace_bytes(3, 8, 64, 64)
+    assert need > 0 and bs.bs_workspace_bytes(3, 65, 64, 64) == 0
+    ok = dict(work=FAKE, work_bytes=need)
+    assert _gemm(fn, a=None, **ok) == E
+    assert _gemm(fn, s=None, **ok) == E
+    assert _gemm(fn, lda=16, **ok) == E                              # < K/2
+    assert _gemm(fn, M=100, K=96, lda=48, ldw=48, **ok) == E         # prefill needs K % 64 == 0
+    assert _gemm(fn, lda=40, ldw=32, **ok) == A
+    assert _gemm(fn, M=8, lda=32, ldw=32) == W                       # missing workspace
+    q = lambda x=FAKE, ldx=64, qq=FAKE, ldq=32, s=FAKE, M=4, K=64: lib.fp4_quant_rows(x, ldx, qq, ldq, s, M, K, None)
+    assert q(x=None) == E
+    assert q(s=None) == E
+    assert q(K=48) == E
+    assert q(ldq=16) == E                                            # < K/2
+    assert q(ldq=40) == A
+    assert q(x=ctypes.c_void_p(0x10008)) == A
+
+
 def test_producer_argument_checks():
     lib = bs.load_library()
     E, A = bs.BS_EINVAL, bs.BS_EALIGN
