@@ -24,6 +24,9 @@ Parity status of each function (the pins are the ``-m "not gpu"`` tests in
 * bf16 rounding of fp64 values: pinned (torch's fp32 -> bf16 cast on values
   exact in fp32, exact rational nearest-neighbour search on values that are
   not, overflow and signed zeros).
+* grouped (MoE) W4A8 GEMM: pinned (each expert's rows equal the dense W4A8
+  GEMM on that expert alone; empty experts, one expert holding every row;
+  the expert order of the rows).
 * MXFP4 activation quantizer and the W4A4 GEMM: pinned (the quantizer is
   the weight conversion applied to activation rows, checked against the
   generator's independent numpy conversion; the GEMM against
@@ -106,6 +109,9 @@ def _load():
         lib.or_encode_e4m3.restype = None
         lib.or_quant_mxfp4_weights.argtypes = [vp, i64, i64, vp, vp]
         lib.or_quant_mxfp4_weights.restype = None
+        lib.or_gemm_mxfp4_w4a8_grouped.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, vp, vp,
+                                                   ctypes.c_int, i64, i64, i64, vp, vp]
+        lib.or_gemm_mxfp4_w4a8_grouped.restype = None
         lib.or_quant_mxfp4_rows.argtypes = [vp, i64, i64, i64, vp, vp]
         lib.or_quant_mxfp4_rows.restype = None
         w4 = [vp, i64, vp, vp, i64, vp, vp, ctypes.c_int, i64, i64, i64, vp, vp]
@@ -313,6 +319,30 @@ def gemm_sampled(fmt, a_codes, a_scale, w, w_scale, bias_bf16, epilogue, ms, ns)
         fn, ldw = _load().or_gemm_mxfp4_w4a8_sampled, K // 2
     fn(_ptr(a), K, _ptr(s), _ptr(w), ldw, _ptr(ws), _ptr(b), int(epilogue), K,
        ms.size, _ptr(ms), _ptr(ns), _ptr(out), _ptr(absum))
+    return out, absum
+
+
+def gemm_mxfp4_w4a8_grouped(a_codes, a_scale, offsets, w_packed, w_scale, bias_bf16=None,
+                            epilogue=EPI_NONE):
+    """Grouped (MoE) W4A8 GEMM: rows [offsets[e], offsets[e+1]) of A use
+    expert e's weights w_packed[e] [N, K/2] with scales w_scale[e] [N, K/32]
+    and bias_bf16[e] [N]. Returns fp64 out and absum [offsets[-1], N]."""
+    a = _c(a_codes, np.uint8)
+    s = _c(a_scale, np.float32)
+    off = _c(offsets, np.int32)
+    w = _c(w_packed, np.uint8)
+    ws = _c(w_scale, np.uint8)
+    E, N, K2 = w.shape
+    K = 2 * K2
+    T = int(off[-1])
+    assert off.shape == (E + 1,) and off[0] == 0 and np.all(np.diff(off) >= 0)
+    assert a.shape[0] >= T and a.shape[1] == K and ws.shape == (E, N, K // 32)
+    b = None if bias_bf16 is None else _c(bias_bf16, np.uint16)
+    out = np.empty((T, N), dtype=np.float64)
+    absum = np.empty((T, N), dtype=np.float64)
+    _load().or_gemm_mxfp4_w4a8_grouped(_ptr(a), K, _ptr(s), _ptr(off), E, _ptr(w), K2, N * K2,
+                                       _ptr(ws), _ptr(b), int(epilogue), T, N, K, _ptr(out),
+                                       _ptr(absum))
     return out, absum
 
 

@@ -482,6 +482,33 @@ void or_gemm_mxfp4_w4a4_sampled(const uint8_t *a, int64_t lda, const uint8_t *a_
     }
 }
 
+/* Grouped (MoE) W4A8 GEMM: token rows grouped by expert, rows
+ * [off[e], off[e+1]) of A use expert e's MXFP4 weights (mono runner page,
+ * MonoLayerWeights.check: the routed experts' w13 [experts, 2 inter,
+ * hidden / 2] fp4x2 with uint8 scales [experts * 2 inter, hidden / 32]).
+ * For t in expert e's rows, n < N:
+ *   y[t, n] = one_mxfp4(a[t], a_scale[t], W_e[n], S_e[n], bias_e[n])
+ * W_e = w + e * w_estride (bytes), S_e = ws + e * N * (K / 32),
+ * bias_e = bias + e * N (or none). out/absum are [T, N]. */
+void or_gemm_mxfp4_w4a8_grouped(const uint8_t *a, int64_t lda, const float *a_scale,
+                                const int32_t *off, int64_t E,
+                                const uint8_t *w, int64_t ldw, int64_t w_estride,
+                                const uint8_t *ws, const uint16_t *bias, int epi,
+                                int64_t T, int64_t N, int64_t K, double *out, double *absum)
+{
+    int64_t idx;
+    (void)T;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (idx = 0; idx < (int64_t)off[E] * N; ++idx) {
+        int64_t t = idx / N, n = idx % N, e = 0;
+        while (off[e + 1] <= t)
+            ++e;
+        one_mxfp4(a + t * lda, a_scale[t], w + e * w_estride + n * ldw,
+                  ws + (e * N + n) * (K / 32), bias ? bias + e * N + n : NULL, epi, K,
+                  out + idx, absum + idx);
+    }
+}
+
 /* One output of the row-wise scaled e4m3 GEMM: per-token activation scale
  * times per-output-channel weight scale (sly-radiance README, lm_head row of
  * its file table: the head's weight quantized to fp8 per output channel and

@@ -220,6 +220,48 @@ def make(name: str, M: int | None = None, seed: int = 0) -> dict:
             "w": w, "w_scale": ws, "bias": bias(wl, seed), "epilogue": wl.epilogue}
 
 
+# grouped MoE W4A8: the mono runner page's routed-expert layout (w13
+# [experts, 2 inter, hidden / 2] fp4x2, scales [experts * 2 inter, hidden/32])
+# at hidden = 7168 (its projection widths); the expert count, intermediate
+# size and routing are this workload's choice: 32 local experts, 2 inter =
+# 4096, top-8 routing of a decode batch of 8 tokens.
+MOE = {"E": 32, "N": 4096, "K": 7168, "tokens": 8, "topk": 8}
+_T_ROUTE = 8
+
+
+def moe_routing(tokens: int, E: int, topk: int, seed: int = 0):
+    """(row_token [tokens * topk], offsets [E + 1] int32): each token picks
+    topk distinct experts uniformly; rows are the (token, expert) pairs
+    sorted by expert (then token)."""
+    rng = _rng(seed, _T_ROUTE)
+    pairs = [(int(e), t) for t in range(tokens) for e in rng.choice(E, size=topk, replace=False)]
+    pairs.sort()
+    row_token = np.array([t for _, t in pairs], dtype=np.int64)
+    counts = np.bincount([e for e, _ in pairs], minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return row_token, offsets
+
+
+def moe_weights(E: int, N: int, K: int, seed: int = 0, distinct: int | None = None):
+    """MXFP4 expert weights [E, N, K/2] and scales [E, N, K/32] from
+    N(0, 0.02) samples by the OCP MX conversion; with `distinct`, expert e
+    holds a copy of expert e % distinct (a large bench configuration drawn
+    quickly)."""
+    distinct = E if distinct is None else distinct
+    packed = np.empty((E, N, K // 2), dtype=np.uint8)
+    scales = np.empty((E, N, K // 32), dtype=np.uint8)
+    rng = _rng(seed, _T_W)
+    for e in range(distinct):
+        for r0 in range(0, N, 2048):
+            r1 = min(N, r0 + 2048)
+            v = rng.standard_normal((r1 - r0, K), dtype=np.float32) * np.float32(0.02)
+            packed[e, r0:r1], scales[e, r0:r1] = _mx_quantize_rows(v)
+    for e in range(distinct, E):
+        packed[e] = packed[e % distinct]
+        scales[e] = scales[e % distinct]
+    return packed, scales
+
+
 # fused producers: name -> (row width at full size, M sweep)
 PRODUCERS = {
     "add_rms": (5120, (1, 16, 512, 4096)),
