@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", default="decode",
                    choices=["tiny", "decode", "prefill", "ffn_up", "ffn_up_bias", "gate_up",
-                            "gate_up_w4a4", "lm_head", "add_rms", "silu_mul"],
+                            "gate_up_w4a4", "lm_head", "moe", "add_rms", "silu_mul"],
                    help="a GEMM workload (quantize + GEMM per step), or a fused producer "
                         "(add_rms: residual add + RMSNorm + quantize on [M, 5120]; silu_mul: "
                         "SiLU(gate) * up + quantize on [M, 2 x 17408])")
@@ -126,6 +126,9 @@ def main():
 
     if args.workload in synth.PRODUCERS:
         bench_producer(args)
+        return
+    if args.workload == "moe":
+        bench_moe(args)
         return
 
     wl = synth.WORKLOADS[args.workload]
@@ -311,6 +314,114 @@ def cpu_baseline(d, wl, M, alg, compute_bound, budget_s):
             "sample": "%d of %d token rows (all %d outputs each), %d passes of quantize + GEMM + "
                       "epilogue in %.1f s" % (rows, M, wl.N, runs, t_total),
             "cpu_model": _cpu_model()}
+
+
+def bench_moe(args):
+    """One step = per-token quantization of the expert-sorted rows and one
+    grouped W4A8 GEMM over every expert (32 experts [4096, 7168] MXFP4, top-8
+    routing of 8 decode tokens); expert-weight copies rotate over >= 512 MiB."""
+    import torch
+    import mxfp4_gemm_transformer_amd as bs
+    import synth
+
+    m = synth.MOE
+    E, N, K, tokens, topk = m["E"], m["N"], m["K"], m["tokens"], m["topk"]
+    steps = args.steps if args.steps is not None else 500
+    warmup = args.warmup if args.warmup is not None else 20
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rng = np.random.default_rng(0)
+    xt = synth.to_bf16_bits(rng.standard_normal((tokens, K)).astype(np.float32))
+    row_token, off = synth.moe_routing(tokens, E, topk, seed=0)
+    T = len(row_token)
+    w_host, ws_host = synth.moe_weights(E, N, K, seed=0, distinct=4)
+    copies = max(2, math.ceil(ROTATION_BYTES / (w_host.nbytes + ws_host.nbytes)))
+    w0 = torch.from_numpy(w_host).to(dev)
+    ws0 = torch.from_numpy(ws_host).to(dev)
+    w_list = [w0] + [w0.clone() for _ in range(copies - 1)]
+    ws_list = [ws0] + [ws0.clone() for _ in range(copies - 1)]
+    x = torch.from_numpy(xt[row_token].view(np.int16)).view(torch.bfloat16).to(dev)
+    offsets = torch.from_numpy(off).to(dev)
+    q = torch.empty((T, K), dtype=torch.uint8, device=dev)
+    s = torch.empty((T,), dtype=torch.float32, device=dev)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+
+    def gemm(i):
+        bs.gemm_mxfp4_w4a8_grouped(q, s, offsets, w_list[i % copies], ws_list[i % copies], y=y,
+                                   max_rows_per_expert=tokens)
+
+    def step(i):
+        bs.fp8_quant_rows(x, q, s)
+        gemm(i)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step(i)
+    torch.cuda.synchronize()
+    graphs = {}
+    for name, fn in (("step", step), ("gemm", gemm)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                fn(i)
+        g.replay()
+        graphs[name] = g
+    torch.cuda.synchronize()
+
+    def timed(g):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / steps
+
+    t0 = time.perf_counter()
+    step_s = timed(graphs["step"])
+    wall_s = time.perf_counter() - t0
+    gemm_s = timed(graphs["gemm"])
+    active = int(np.count_nonzero(np.diff(off)))
+    w_alg = active * (N * K // 2 + N * (K // 32))
+    gemm_bytes = w_alg + T * K + 4 * T + 2 * T * N
+    quant_bytes = 3 * T * K + 4 * T
+    gbs = (gemm_bytes + quant_bytes) / step_s / 1e9
+    achieved = gemm_bytes / gemm_s / 1e9
+    result = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(step_s * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 x fp4_e2m1", "data": "synthetic",
+        "config": {"workload": "moe E=%d N=%d K=%d, %d tokens top-%d = %d rows over %d active experts "
+                               "(grouped MXFP4 W4A8)" % (E, N, K, tokens, topk, T, active),
+                   "E": E, "N": N, "K": K, "rows": T, "active_experts": active,
+                   "weight_copies_rotated": copies, "step": "fp8_quant_rows + gemm_mxfp4_w4a8_grouped",
+                   "graph_replay": True},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemm_mxfp4_w4a8_grouped", "avg_launch_us": round(gemm_s * 1e6, 3),
+                     "algorithmic_bytes_per_launch": gemm_bytes},
+        "kernels_us": {"fp8_quant_rows+gemm": round(step_s * 1e6, 3),
+                       "gemm_mxfp4_w4a8_grouped": round(gemm_s * 1e6, 3)},
+        "step_bytes": gemm_bytes + quant_bytes, "wall_s_timed_region": round(wall_s, 6),
+    }
+    if args.cpu_seconds > 0:
+        import oracle
+        oracle.build()
+        runs, t_total = 0, 0.0
+        while t_total < args.cpu_seconds or runs == 0:
+            t1 = time.perf_counter()
+            qh, sh = oracle.quant_rows(xt[row_token])
+            oracle.gemm_mxfp4_w4a8_grouped(qh, sh, off, w_host, ws_host)
+            t_total += time.perf_counter() - t1
+            runs += 1
+        result["cpu_baseline"] = {
+            "value": round((gemm_bytes + quant_bytes) * runs / t_total / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "the whole step (%d rows), %d passes in %.1f s" % (T, runs, t_total),
+            "cpu_model": _cpu_model()}
+    print(json.dumps(result))
 
 
 def producer_bytes(name, M, width):

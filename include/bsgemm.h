@@ -10,7 +10,8 @@
  *   4. gemm_fp8_rowwise  e4m3 weights with one fp32 scale per output channel;
  *      fp8_quant_rows_static  quantization with a given per-tensor scale
  *   5. fp4_quant_rows, gemm_mxfp4_w4a4  MXFP4 activations x MXFP4 weights
- *   6. add_rms_norm_quant_fp8, silu_mul_quant_fp8
+ *   6. gemm_mxfp4_w4a8_grouped  MoE: many experts' MXFP4 weights, one launch
+ *   7. add_rms_norm_quant_fp8, silu_mul_quant_fp8
  *                       fused producers: RMSNorm (with an optional residual
  *                       add) or SiLU(gate) * up, then step 1, in one kernel
  *
@@ -217,6 +218,36 @@ int gemm_mxfp4_w4a4(const void *a_fp4x2, int64_t ld_a, const uint8_t *a_scale,
                     void *y_bf16, int64_t ld_y,
                     int64_t M, int64_t N, int64_t K,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Grouped (MoE) W4A8 GEMM: many experts' MXFP4 weights in one launch over
+ * expert-sorted token rows (mono runner page, MonoLayerWeights.check: the
+ * routed experts' w13 [experts, 2 inter, hidden / 2] fp4x2 with uint8
+ * scales [experts * 2 inter, hidden / 32]). For every expert e and token row
+ * t in [expert_offsets[e], expert_offsets[e+1]):
+ *     y[t,n] = epilogue(a_scale[t] * sum_kb 2^(S_e[n,kb]-127) sum_k a[t,k] W_e[n,k] (+ bias[e,n]))
+ *   a_e4m3 [T, K], a_scale [T] fp32: the token rows, grouped by expert
+ *   expert_offsets  DEVICE pointer to E + 1 int32, nondecreasing, from 0 to
+ *                   at most T (read by the kernel; rows outside [0, T) are
+ *                   never touched whatever they hold)
+ *   max_rows_per_expert  an upper bound on any expert's rows (picks how many
+ *                   tokens a pass takes; a wrong bound costs time, not
+ *                   correctness)
+ *   w_fp4x2  expert e's [N, K/2] at w + e * w_expert_stride bytes, row
+ *            stride ld_w bytes; w_scale [E, N, K/32] E8M0 dense
+ *   bias     [E, N] bf16 or NULL; y_bf16 [T, N], row stride ld_y
+ *   E <= 65535. Rows of y outside every expert's range are not written.
+ *   This is the decode-sized grouped kernel (rows per expert small: each
+ *   workgroup streams its 8 weight rows of one expert once per pass of up
+ *   to 32 rows).
+ */
+int gemm_mxfp4_w4a8_grouped(const void *a_e4m3, int64_t ld_a, const float *a_scale,
+                            const int32_t *expert_offsets, int64_t E,
+                            int64_t max_rows_per_expert,
+                            const void *w_fp4x2, int64_t ld_w, int64_t w_expert_stride,
+                            const uint8_t *w_scale, const void *bias_bf16, int epilogue,
+                            void *y_bf16, int64_t ld_y, int64_t T, int64_t N, int64_t K,
+                            void *stream);
 
 /*
  * Row-wise scaled e4m3 GEMM: one fp32 scale per token and one per output

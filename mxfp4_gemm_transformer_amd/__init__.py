@@ -21,7 +21,7 @@ import torch
 
 __all__ = ["fp8_quant_rows", "fp8_quant_rows_static", "add_rms_norm_quant_fp8",
            "silu_mul_quant_fp8", "gemm_bs_fp8", "gemm_mxfp4_w4a8", "gemm_fp8_rowwise",
-           "fp4_quant_rows", "gemm_mxfp4_w4a4", "bs_workspace_bytes",
+           "fp4_quant_rows", "gemm_mxfp4_w4a4", "gemm_mxfp4_w4a8_grouped", "bs_workspace_bytes",
            "bs_status_string", "BsError", "EPI_NONE", "EPI_BIAS", "EPI_BIAS_GELU_TANH",
            "weight_shape", "w_scale_shape", "library_path", "load_library",
            "EXPORTED_SYMBOLS"]
@@ -31,7 +31,7 @@ BS_OK, BS_EINVAL, BS_EALIGN, BS_EARCH, BS_EWORKSPACE, BS_ELAUNCH = 0, -1, -2, -3
 
 EXPORTED_SYMBOLS = ("fp8_quant_rows", "fp8_quant_rows_static", "add_rms_norm_quant_fp8",
                     "silu_mul_quant_fp8", "gemm_bs_fp8", "gemm_mxfp4_w4a8", "gemm_fp8_rowwise",
-                    "fp4_quant_rows", "gemm_mxfp4_w4a4", "bs_workspace_bytes", "bs_status_string")
+                    "fp4_quant_rows", "gemm_mxfp4_w4a4", "gemm_mxfp4_w4a8_grouped", "bs_workspace_bytes", "bs_status_string")
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsgemm.so")
 _lib = None
@@ -72,6 +72,9 @@ def load_library():
         lib.gemm_fp8_rowwise.restype = i32
         lib.gemm_mxfp4_w4a4.argtypes = gemm
         lib.gemm_mxfp4_w4a4.restype = i32
+        lib.gemm_mxfp4_w4a8_grouped.argtypes = [vp, i64, vp, vp, i64, i64, vp, i64, i64, vp, vp,
+                                                i32, vp, i64, i64, i64, i64, vp]
+        lib.gemm_mxfp4_w4a8_grouped.restype = i32
         lib.fp4_quant_rows.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp]
         lib.fp4_quant_rows.restype = i32
         lib.fp8_quant_rows_static.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, vp]
@@ -285,6 +288,46 @@ def fp8_quant_rows_static(x: torch.Tensor, scale: torch.Tensor, q: torch.Tensor 
     if st != BS_OK:
         raise BsError(st, "fp8_quant_rows_static")
     return q, scale_out
+
+
+def gemm_mxfp4_w4a8_grouped(a, a_scale, expert_offsets, w, w_scale, bias=None,
+                            epilogue=EPI_NONE, y=None, max_rows_per_expert=None, stream=None):
+    """Grouped (MoE) W4A8 GEMM. a: e4m3 [T, K] rows sorted by expert;
+    expert_offsets: int32 device [E + 1]; w: fp4x2 [E, N, K/2]; w_scale:
+    uint8 [E, N, K/32]; bias: bf16 [E, N] or None. Returns y bf16 [T, N]
+    (rows outside every expert's range are left as they are)."""
+    a = _u8(a, "a")
+    w = _u8(w, "w")
+    T, K = a.shape
+    E, N, K2 = w.shape
+    if K2 * 2 != K:
+        raise ValueError("w must be [E, N, K/2]")
+    lda = _matrix(a, "a", T, K)
+    if w.stride(2) != 1 or w.stride(1) < K2 or not w.is_cuda:
+        raise ValueError("w must be a device [E, N, K/2] tensor with unit column stride")
+    if a_scale.dtype != torch.float32 or a_scale.shape != (T,) or not a_scale.is_contiguous():
+        raise ValueError("a_scale must be a contiguous fp32 [T] tensor")
+    if expert_offsets.dtype != torch.int32 or expert_offsets.shape != (E + 1,) \
+            or not expert_offsets.is_contiguous() or not expert_offsets.is_cuda:
+        raise ValueError("expert_offsets must be a contiguous int32 device [E + 1] tensor")
+    if w_scale.dtype != torch.uint8 or tuple(w_scale.shape) != (E, N, K // 32) \
+            or not w_scale.is_contiguous():
+        raise ValueError("w_scale must be a contiguous uint8 [E, N, K/32] tensor")
+    if epilogue != EPI_NONE:
+        if bias is None or bias.dtype != torch.bfloat16 or tuple(bias.shape) != (E, N) \
+                or not bias.is_contiguous():
+            raise ValueError("this epilogue needs a contiguous bf16 bias [E, N]")
+    if y is None:
+        y = torch.zeros((T, N), dtype=torch.bfloat16, device=a.device)
+    ldy = _matrix(y, "y", T, N)
+    mr = T if max_rows_per_expert is None else int(max_rows_per_expert)
+    st = load_library().gemm_mxfp4_w4a8_grouped(
+        _ptr(a), lda, _ptr(a_scale), _ptr(expert_offsets), E, mr, _ptr(w), w.stride(1),
+        w.stride(0), _ptr(w_scale), _ptr(bias if epilogue != EPI_NONE else None), int(epilogue),
+        _ptr(y), ldy, T, N, K, ctypes.c_void_p(_stream(stream)))
+    if st != BS_OK:
+        raise BsError(st, "gemm_mxfp4_w4a8_grouped")
+    return y
 
 
 def fp4_quant_rows(x: torch.Tensor, q: torch.Tensor | None = None,

@@ -58,6 +58,16 @@ hipError_t launch_gemm_decode_w4a4(const uint8_t *a, int64_t lda, const uint8_t 
                                    int64_t M, int64_t N, int64_t K, void *workspace,
                                    hipStream_t stream);
 size_t decode_workspace_bytes_w4a4(int64_t M, int64_t N, int64_t K);
+
+// Grouped (MoE) GEMM over expert-sorted rows: offsets [E + 1] on the device,
+// expert e's weights at w + e * w_estride ([N, K/2] fp4x2 or [N, K] e4m3)
+// with scales [E, N, K/32] (fp4) or [E, N/32, K/32] (e4m3), bias [E, N].
+// max_rows bounds the rows of any expert (it picks the tokens per pass).
+hipError_t launch_gemm_grouped(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
+                               const int32_t *offsets, int64_t E, int64_t max_rows,
+                               const uint8_t *w, int64_t ldw, int64_t w_estride,
+                               const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y,
+                               int64_t ldy, int64_t T, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_gemm_prefill_w4a4(const uint8_t *a, int64_t lda, const uint8_t *a_e8m0,
                                     const uint8_t *w, int64_t ldw, const uint8_t *ws,
                                     const uint16_t *bias, int epi, uint16_t *y, int64_t ldy,

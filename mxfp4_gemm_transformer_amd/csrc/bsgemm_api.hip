@@ -249,6 +249,34 @@ int gemm_mxfp4_w4a4(const void *a_fp4x2, int64_t ld_a, const uint8_t *a_scale, c
     return e == hipSuccess ? BS_OK : BS_ELAUNCH;
 }
 
+int gemm_mxfp4_w4a8_grouped(const void *a_e4m3, int64_t ld_a, const float *a_scale,
+                            const int32_t *expert_offsets, int64_t E, int64_t max_rows_per_expert,
+                            const void *w_fp4x2, int64_t ld_w, int64_t w_expert_stride,
+                            const uint8_t *w_scale, const void *bias_bf16, int epilogue,
+                            void *y_bf16, int64_t ld_y, int64_t T, int64_t N, int64_t K,
+                            void *stream) {
+    if (!a_e4m3 || !a_scale || !expert_offsets || !w_fp4x2 || !w_scale || !y_bf16) return BS_EINVAL;
+    if (T < 1 || E < 1 || E > 65535 || N < 32 || K < 32 || N % 32 || K % 32) return BS_EINVAL;
+    if (T > INT32_MAX || N > INT32_MAX || K > INT32_MAX || max_rows_per_expert < 1) return BS_EINVAL;
+    if (epilogue < BS_EPI_NONE || epilogue > BS_EPI_BIAS_GELU_TANH) return BS_EINVAL;
+    if (epilogue != BS_EPI_NONE && !bias_bf16) return BS_EINVAL;
+    if (ld_a < K || ld_w < K / 2 || ld_y < N || w_expert_stride < N * ld_w) return BS_EINVAL;
+    if (!aligned16(a_e4m3) || !aligned16(w_fp4x2) || !aligned16(y_bf16)) return BS_EALIGN;
+    if (ld_a % 16 || ld_w % 16 || (2 * ld_y) % 16 || w_expert_stride % 16) return BS_EALIGN;
+    if ((reinterpret_cast<uintptr_t>(a_scale) & 3u) || (reinterpret_cast<uintptr_t>(expert_offsets) & 3u))
+        return BS_EALIGN;
+    if (bias_bf16 && (reinterpret_cast<uintptr_t>(bias_bf16) & 1u) != 0) return BS_EALIGN;
+    int num_cus = 0;
+    int st = device_check(&num_cus);
+    if (st != BS_OK) return st;
+    hipError_t e = bsg::launch_gemm_grouped(
+        true, static_cast<const uint8_t *>(a_e4m3), ld_a, a_scale, expert_offsets, E,
+        max_rows_per_expert, static_cast<const uint8_t *>(w_fp4x2), ld_w, w_expert_stride, w_scale,
+        static_cast<const uint16_t *>(bias_bf16), epilogue, static_cast<uint16_t *>(y_bf16), ld_y,
+        T, N, K, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BS_OK : BS_ELAUNCH;
+}
+
 size_t bs_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
     if (M < 1 || N < 1 || K < 1) return 0;
     if (op == 3) return bsg::decode_workspace_bytes_w4a4(M, N, K);   // W4A4: split-K decode

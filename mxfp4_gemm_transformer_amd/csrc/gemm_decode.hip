@@ -723,6 +723,96 @@ hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const flo
     }
 }
 
+// ---------------------------------------------------------------------------
+// Grouped (MoE) decode: one launch over (8-row weight group) x expert.
+// Expert e's token rows are [off[e], off[e+1]) of A, sorted by expert; a
+// workgroup of 8 waves (K split between them, folded layout as above)
+// streams its 8 weight rows of expert e once and applies them to up to G
+// folded 8-token groups per pass; more tokens take further passes (the rows
+// come back from L2). Experts without rows exit at once. Offsets are read on
+// the device and clamped to [0, T], so any offsets stay inside A and Y.
+template <bool FP4, int G>
+__global__ __launch_bounds__(512) void gemm_grouped_decode_kernel(
+    const uint8_t *__restrict__ A, int64_t lda, const float *__restrict__ a_scale,
+    const int32_t *__restrict__ off, const uint8_t *__restrict__ W, int64_t ldw,
+    int64_t w_estride, const uint8_t *__restrict__ WS, const uint16_t *__restrict__ bias, int epi,
+    uint16_t *__restrict__ Y, int64_t ldy, int T, int N, int K) {
+    constexpr int NW = 8, COLS = 8, KSTEP = 256;
+    __shared__ float red[NW][G][8][COLS + 1];
+    const int e = blockIdx.y;
+    const int r0 = min(max(off[e], 0), T);
+    const int r1 = max(r0, min(off[e + 1], T));
+    if (r0 == r1) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i = lane & 15, g = lane >> 4;
+    const int col = i & 7, half = i >> 3;
+    const int KB = K >> 5;
+    const int nsteps = (K + KSTEP - 1) / KSTEP;
+    const int64_t n = (int64_t)blockIdx.x * COLS + col;   // this lane's weight row
+    const uint8_t *wrow = W + (int64_t)e * w_estride + n * ldw;
+    const uint8_t *wsrow = FP4 ? WS + ((int64_t)e * N + n) * KB
+                               : WS + ((int64_t)e * (N >> 5) + (n >> 5)) * KB;
+    const uint16_t *bias_e = bias ? bias + (int64_t)e * N : nullptr;
+
+    for (int p0 = r0; p0 < r1; p0 += 8 * G) {
+        v4f acc[G];
+#pragma unroll
+        for (int q = 0; q < G; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int s = wave; s < nsteps; s += NW) {
+            const int k0 = s * KSTEP + half * 128;
+            const int kblk = k0 + 32 * g, klo = k0 + 16 * g, khi = k0 + 64 + 16 * g;
+            uint4 lo = make_uint4(0u, 0u, 0u, 0u), hi = lo;
+            int sc = E8M0_ONE;
+            if (FP4) {
+                if (kblk < K) {
+                    lo = ldg16(wrow + (kblk >> 1));
+                    sc = wsrow[kblk >> 5];
+                }
+            } else {
+                if (klo < K) lo = ldg16(wrow + klo);
+                if (khi < K) hi = ldg16(wrow + khi);
+                if (kblk < K) sc = wsrow[kblk >> 5];
+            }
+            const v8i wv = pack8(lo, hi);
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+                const int m = p0 + 8 * q + (i & 7);
+                uint4 alo = make_uint4(0u, 0u, 0u, 0u), ahi = alo;
+                if (m < r1) {
+                    const uint8_t *arow = A + (int64_t)m * lda;
+                    if (klo < K) alo = ldg16(arow + klo);
+                    if (khi < K) ahi = ldg16(arow + khi);
+                }
+                acc[q] = mfma16<FP4>(pack8(alo, ahi), wv, acc[q], E8M0_ONE, sc);
+            }
+        }
+        // the two diagonal 8x8 blocks (K halves) meet in lanes g < 2, i < 8
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[q][v] += __shfl_down(acc[q][v], 40, 64);
+            if (g < 2 && i < 8) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) red[wave][q][4 * g + v][i] = acc[q][v];
+            }
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < G * 8 * COLS; idx += NW * 64) {
+            const int q = idx / (8 * COLS), r = (idx / COLS) % 8, c = idx % COLS;
+            const int m = p0 + 8 * q + r;
+            if (m < r1) {
+                float sum = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) sum += red[w][q][r][c];
+                const int64_t nn = (int64_t)blockIdx.x * COLS + c;
+                const float b = (epi != EPI_NONE) ? bf16_to_f32(bias_e[nn]) : 0.f;
+                Y[(int64_t)m * ldy + nn] = (uint16_t)f32_to_bf16(epilogue(sum, a_scale[m], b, epi));
+            }
+        }
+        __syncthreads();   // red is reused by the next pass
+    }
+}
+
 // W4A4 decode: the split-K kernel for every M <= DECODE_MAX_M (fp4
 // activations staged with their scales); no per-token scale.
 hipError_t launch_gemm_decode_w4a4(const uint8_t *a, int64_t lda, const uint8_t *a_e8m0,
@@ -737,6 +827,23 @@ hipError_t launch_gemm_decode_w4a4(const uint8_t *a, int64_t lda, const uint8_t 
     case 3: return launch_splitk<true, 3, true>(a, lda, nullptr, w, ldw, ws, nullptr, bias, epi, y, ldy, M, N, K, part, st, a_e8m0);
     default: return launch_splitk<true, 4, true>(a, lda, nullptr, w, ldw, ws, nullptr, bias, epi, y, ldy, M, N, K, part, st, a_e8m0);
     }
+}
+
+hipError_t launch_gemm_grouped(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
+                               const int32_t *offsets, int64_t E, int64_t max_rows,
+                               const uint8_t *w, int64_t ldw, int64_t w_estride,
+                               const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y,
+                               int64_t ldy, int64_t T, int64_t N, int64_t K, hipStream_t st) {
+    const dim3 grid((unsigned)(N / 8), (unsigned)E);
+#define BSG_GROUPED(FP4_, G_)                                                                      \
+    hipLaunchKernelGGL((gemm_grouped_decode_kernel<FP4_, G_>), grid, dim3(512), 0, st, a, lda,      \
+                       a_scale, offsets, w, ldw, w_estride, ws, bias, epi, y, ldy, (int)T, (int)N,  \
+                       (int)K)
+    if (max_rows <= 8) { if (fp4) BSG_GROUPED(true, 1); else BSG_GROUPED(false, 1); }
+    else if (max_rows <= 16) { if (fp4) BSG_GROUPED(true, 2); else BSG_GROUPED(false, 2); }
+    else { if (fp4) BSG_GROUPED(true, 4); else BSG_GROUPED(false, 4); }
+#undef BSG_GROUPED
+    return hipGetLastError();
 }
 
 size_t decode_workspace_bytes_w4a4(int64_t M, int64_t N, int64_t K) {

@@ -163,6 +163,29 @@ def test_w4a4_argument_checks():
     assert q(x=ctypes.c_void_p(0x10008)) == A
 
 
+def test_grouped_argument_checks():
+    lib = bs.load_library()
+    E_, A = bs.BS_EINVAL, bs.BS_EALIGN
+
+    def g(a=FAKE, lda=64, s=FAKE, off=FAKE, E=4, mr=8, w=FAKE, ldw=32, wst=32 * 64, ws=FAKE,
+          b=None, epi=0, y=FAKE, ldy=64, T=8, N=64, K=64):
+        return lib.gemm_mxfp4_w4a8_grouped(a, lda, s, off, E, mr, w, ldw, wst, ws, b, epi, y, ldy,
+                                           T, N, K, None)
+
+    assert g(off=None) == E_
+    assert g(a=None) == E_
+    assert g(E=0) == E_
+    assert g(E=70000) == E_
+    assert g(mr=0) == E_
+    assert g(N=48) == E_
+    assert g(wst=32 * 63) == E_                 # experts overlap
+    assert g(ldw=16) == E_                      # < K/2
+    assert g(epi=1) == E_                       # bias required
+    assert g(off=ctypes.c_void_p(0x10002)) == A
+    assert g(wst=32 * 64 + 8) == A
+    assert g(ldw=40, wst=40 * 64) == A
+
+
 def test_producer_argument_checks():
     lib = bs.load_library()
     E, A = bs.BS_EINVAL, bs.BS_EALIGN
