@@ -35,6 +35,16 @@ namespace {
 constexpr int BK = 64;
 constexpr int NXCD = 8;
 
+// E8M0 1.0 (127) bytes. When the weights carry no E8M0 grid (one fp32 scale
+// per output channel instead), the scale loads read these, so the fragment
+// reads hand the MFMA its scale byte straight from LDS in either case: a
+// select on the loaded byte (or a branch around the read) would put a VALU
+// instruction that waits on the next step's LDS reads inside the current
+// step, and a branch also splits the step into blocks the scheduler cannot
+// interleave across.
+__device__ const uint8_t kE8M0Ones[16] = {127, 127, 127, 127, 127, 127, 127, 127,
+                                          127, 127, 127, 127, 127, 127, 127, 127};
+
 template <bool FP4, int BM, int BN, int WGM, int WGN>
 struct Cfg {
     static constexpr int NW = WGM * WGN;
@@ -115,12 +125,14 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
 
     // the scale rows of this tile: [N/32, KB] for e4m3 weights, [N, KB] for
     // MXFP4; rows past the end and K blocks past KB read as zero (a zero
-    // E8M0 byte scales zero data there)
-    // (no WS: per-channel fp32 scales instead, an empty range here)
+    // E8M0 byte scales zero data there). No WS (per-channel fp32 scales
+    // instead): every thread reads byte 0 of kE8M0Ones.
     const int srow0 = FP4 ? n0 : (n0 >> 5);
-    const int64_t s_bytes = WS ? (int64_t)((FP4 ? N : (N >> 5)) - srow0) * KB : 0;
+    const bool ws_on = WS != nullptr;
+    const int64_t s_bytes = ws_on ? (int64_t)((FP4 ? N : (N >> 5)) - srow0) * KB
+                                  : (int64_t)sizeof(kE8M0Ones);
     const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(WS ? WS + (int64_t)srow0 * KB : WS), (short)0,
+        ws_on ? (void *)(WS + (int64_t)srow0 * KB) : (void *)kE8M0Ones, (short)0,
         (int)(s_bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : s_bytes), 0x00020000);
     const uint32_t s_off = (uint32_t)(tid * KB);   // this thread's scale row
 
@@ -172,8 +184,8 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
             // bitwise conditions: a short-circuit here becomes a branch that
             // splits the scheduling region and stalls the MFMA stream
             const bool row_ok = tid < C::SC_ROWS;
-            const uint32_t o0 = (row_ok & (kb < KB)) ? s_off + kb : OOB;
-            const uint32_t o1 = (row_ok & (kb + 1 < KB)) ? s_off + kb + 1 : OOB;
+            const uint32_t o0 = !ws_on ? 0u : (row_ok & (kb < KB)) ? s_off + kb : OOB;
+            const uint32_t o1 = !ws_on ? 0u : (row_ok & (kb + 1 < KB)) ? s_off + kb + 1 : OOB;
             r.sc0 = __builtin_amdgcn_raw_buffer_load_b8(rsS, o0, 0, 0);
             r.sc1 = __builtin_amdgcn_raw_buffer_load_b8(rsS, o1, 0, 0);
         }
@@ -224,7 +236,7 @@ __global__ __launch_bounds__(256, 1) void gemm_prefill_kernel(
                 const int fz = swz4(row);
                 const uint8_t *base = sw + row * C::WROW;
                 f.b[b] = pack8(lds16(base + 16 * (lg ^ fz)), lds16(base + 16 * ((2 + lg) ^ fz)));
-                f.sc[b] = WS ? ss[2 * (row >> 5) + lg] : E8M0_ONE;
+                f.sc[b] = ss[2 * (row >> 5) + lg];
             }
         }
     };
@@ -444,9 +456,11 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         (void *)(W + (int64_t)n0 * ldw), (short)0, (int)(w_bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : w_bytes),
         0x00020000);
     const int srow0 = FP4 ? n0 : (n0 >> 5);
-    const int64_t s_bytes = WS ? (int64_t)((FP4 ? N : (N >> 5)) - srow0) * KB : 0;   // no WS: empty
+    const bool ws_on = WS != nullptr;
+    const int64_t s_bytes = ws_on ? (int64_t)((FP4 ? N : (N >> 5)) - srow0) * KB
+                                  : (int64_t)sizeof(kE8M0Ones);
     const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(WS ? WS + (int64_t)srow0 * KB : WS), (short)0,
+        ws_on ? (void *)(WS + (int64_t)srow0 * KB) : (void *)kE8M0Ones, (short)0,
         (int)(s_bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : s_bytes), 0x00020000);
 
     const int64_t sa_bytes = FP4A ? (int64_t)(M - m0) * KB : 0;
@@ -474,7 +488,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         const int row = tid >> 2, c = (tid & 3) ^ swz4(row);
         w_off = (uint32_t)(row * ldw) + 16 * c;
     }
-    const uint32_t s_off = tid < C::SC_ROWS ? (uint32_t)(tid * KB) : OOB;
+    // without a grid every thread reads the first two bytes of kE8M0Ones
+    const uint32_t s_off = !ws_on ? 0u : tid < C::SC_ROWS ? (uint32_t)(tid * KB) : OOB;
+    const uint32_t s_kshift = ws_on ? 5u : 31u;   // k / 32 (the step's block), or 0
     const uint32_t sa_off = tid < BM ? (uint32_t)(tid * KB) : OOB;
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t *)lds);
 
@@ -494,7 +510,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
                      (uint32_t)(j * W_ROWS_PER_J * ldw) + (FP4 ? kbase / 2 : kbase));
         } else if (i == C::A_LD + C::W_LD) {
             dma_u16(rsS, lds0 + (uint32_t)((s % NBUF) * C::STAGE + C::SC_OFF) + (uint32_t)wave * 256u,
-                    live ? s_off + (kbase >> 5) : OOB);
+                    live ? s_off + (kbase >> s_kshift) : OOB);
         } else {   // FP4A: the activation rows' scale pairs
             dma_u16(rsSA, lds0 + (uint32_t)((s % NBUF) * C::STAGE + C::SCA_OFF) + (uint32_t)wave * 256u,
                     live ? sa_off + (kbase >> 5) : OOB);
@@ -542,7 +558,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
             const int fz = swz4(row);
             const uint8_t *p = sw + row * C::WROW;
             f.b[b] = pack8(lds16(p + 16 * (lg ^ fz)), lds16(p + 16 * ((2 + lg) ^ fz)));
-            f.sc[b] = WS ? ss[4 * (row >> 5) + lg] : E8M0_ONE;   // no WS: per-channel scales
+            f.sc[b] = ss[4 * (row >> 5) + lg];
         }
     };
     // The loads of a step go one before each fragment read, so that with the
@@ -596,11 +612,17 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     // step s: MFMAs on step s's fragments, interleaved with the reads of
     // step s + 1's and the loads of step s + NBUF - 1; then wait until step
     // s + 2's stage has landed.
+    // The scheduling barriers keep each step's MFMAs on their side of the
+    // wait: the inline assembly orders memory operations only, so without
+    // them the compiler moves MFMAs across it and the steps lose their
+    // even MFMA / read / load mix.
     auto step = [&](const Frags &cur, Frags &nxt, int s) {
         mfmas(cur);
         reads_and_loads(nxt, s + 1, s + NBUF - 1);
         interleave();
+        __builtin_amdgcn_sched_barrier(0);
         wait_loads_and_barrier<C::LPS * (NBUF - 3)>();
+        __builtin_amdgcn_sched_barrier(0);
     };
     int s = 0;
     for (; s + 1 < nsteps; s += 2) {

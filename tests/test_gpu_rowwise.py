@@ -63,11 +63,14 @@ def test_rowwise_padded_and_bias(M):
     assert_within(got, ref, absum, "rowwise padded M=%d" % M)
 
 
-def test_rowwise_uniform_power_of_two_scales_equal_block_scaled():
+@pytest.mark.parametrize("M,N,K", [(8, 512, 1024), (300, 4192, 256), (2048, 8192, 256),
+                                   (257, 160, 1056)])
+def test_rowwise_uniform_power_of_two_scales_equal_block_scaled(M, N, K):
     """Channel scales that are one power of two per 32-row block give the
-    block-scaled GEMM's exact bits on the same kernels."""
-    rng = np.random.default_rng(61)
-    M, N, K = 8, 512, 1024
+    block-scaled GEMM's exact bits on the same kernels (decode, the prefill
+    tiles including a whole round of 256x256 ones, and the K % 64 == 32
+    kernel)."""
+    rng = np.random.default_rng(61 + M)
     a, s = oracle.quant_rows(synth.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32)))
     w = oracle.encode_e4m3((rng.standard_normal((N, K)) * 0.05).astype(np.float32))
     byte = rng.integers(120, 131, size=N // 32).astype(np.uint8)
