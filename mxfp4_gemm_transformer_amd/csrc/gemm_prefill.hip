@@ -71,10 +71,18 @@ struct Cfg {
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-// Swizzle of the 16-byte chunk column within a 64-byte row (4 chunks) and a
-// 32-byte row (2 chunks).
+// Swizzle of the 16-byte chunk column within a 128-byte row (8 chunks), a
+// 64-byte row (4 chunks) and a 32-byte row (2 chunks). A ds_read_b128 serves
+// 16 lanes at a time from 64 four-byte banks; a fragment read puts those 16
+// lanes on 16 consecutive rows at one logical chunk, and each swizzle maps
+// them to 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int swz2(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+template <int CHUNKS>
+__device__ __forceinline__ int swz(int r) {
+    return CHUNKS == 8 ? swz8(r) : CHUNKS == 4 ? swz4(r) : swz2(r);
+}
 
 __device__ __forceinline__ uint4 lds16(const uint8_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
@@ -369,6 +377,14 @@ __device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t rs, uint32_t m0,
                  : "memory", "m0");
 }
 
+// One 4-byte LDS-mode buffer load: lane l's bytes land at m0 + 4 l.
+__device__ __forceinline__ void dma_u32(__amdgpu_buffer_rsrc_t rs, uint32_t m0, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rs)
+                 : "memory", "m0");
+}
+
 // One 2-byte LDS-mode buffer load: lane l's two bytes land zero-extended in
 // the 4-byte slot m0 + 4 l.
 __device__ __forceinline__ void dma_u16(__amdgpu_buffer_rsrc_t rs, uint32_t m0, uint32_t voff) {
@@ -387,20 +403,36 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-template <bool FP4, int BM, int BN, int NBUF, int WGM, int WGN, bool FP4A = false>
+// SPS: K steps (of BK) per LDS stage. SPS = 1: a ring of NBUF >= 4 stages,
+// one barrier per step. SPS = 2: two stages of 128 K each, one barrier per
+// two steps; each load then covers whole 128-byte lines of e4m3 rows (with
+// 64-byte stages the two halves of a line are fetched a step apart, and the
+// 32 KB L1 has evicted the line in between, so L2 serves it twice).
+//
+// SLAB_KB > 0 (MXFP4 weights, fp4 activations): the tile's E8M0 rows for
+// all of K (K / 32 <= SLAB_KB bytes each, K % 128 == 0) are loaded into LDS
+// once, ahead of the first stage, as contiguous 4-byte pieces. Per-row
+// scales read a step at a time gather two bytes from each of the tile's 256
+// rows, a separate cache line each, every step: more L2 requests than the
+// tiles themselves.
+template <bool FP4, int BM, int BN, int NBUF, int WGM, int WGN, bool FP4A = false, int SPS = 1,
+          int SLAB_KB = 0>
 struct DCfg {
     static constexpr int NW = WGM * WGN;              // waves, WGM x WGN
     static constexpr int NT = NW * 64;
-    static constexpr int WROW = FP4 ? BK / 2 : BK;    // W bytes per row per step
-    static constexpr int AROW = FP4A ? BK / 2 : BK;   // A bytes per row per step
+    static constexpr int KS = BK * SPS;               // K per stage
+    static constexpr int WROW = FP4 ? KS / 2 : KS;    // W bytes per row per stage
+    static constexpr int AROW = FP4A ? KS / 2 : KS;   // A bytes per row per stage
+    static constexpr int A_CH = AROW / 16, W_CH = WROW / 16;   // 16-byte chunks per row
     static constexpr int A_STAGE = BM * AROW;
     static constexpr int W_STAGE = BN * WROW;
-    static constexpr int SC_OFF = A_STAGE + W_STAGE;  // one 4-byte scale slot per thread
-    static constexpr int SCA_OFF = SC_OFF + 4 * NT;   // fp4 activations: their scale slots
-    static constexpr int STAGE = SC_OFF + 4 * NT * (FP4A ? 2 : 1);
-    static constexpr int A_LD = A_STAGE / 16 / NT;    // 16-byte loads per thread per step
+    static constexpr bool SLAB = SLAB_KB > 0;
+    static constexpr int SC_OFF = A_STAGE + W_STAGE;  // per step: one 4-byte scale slot per thread
+    static constexpr int SCA_OFF = SC_OFF + 4 * NT * SPS;   // fp4 activations: their scale slots
+    static constexpr int STAGE = SLAB ? SC_OFF : SC_OFF + 4 * NT * SPS * (FP4A ? 2 : 1);
+    static constexpr int A_LD = A_STAGE / 16 / NT;    // 16-byte loads per thread per stage
     static constexpr int W_LD = W_STAGE / 16 / NT;
-    static constexpr int LPS = A_LD + W_LD + 1 + (FP4A ? 1 : 0);   // loads per thread per stage
+    static constexpr int LPS = A_LD + W_LD + (SLAB ? 0 : SPS * (FP4A ? 2 : 1));   // loads per thread per stage
     static constexpr int TM = BM / WGM / 32;
     static constexpr int TN = BN / WGN / 32;
     static constexpr int SC_ROWS = FP4 ? BN : BN / 32;
@@ -410,25 +442,34 @@ struct DCfg {
     static constexpr int EP_BIAS = NW * EP_WAVE;      // then each wave's TN*32 bias values
     static constexpr int EP_CS = EP_BIAS + NW * TN * 32 * 4;   // and per-channel scales
     static constexpr int EP_ALL = EP_CS + NW * TN * 32 * 4;
-    static constexpr int LDS = NBUF * STAGE > EP_ALL ? NBUF * STAGE : EP_ALL;
+    // scale slabs after the stages: weight rows, then (fp4 activations) A
+    // rows, each rounded up to whole rounds of 4-byte loads
+    static constexpr int SLAB_ROUND = 4 * NT;
+    static constexpr int WSLAB = SLAB ? (SC_ROWS * SLAB_KB + SLAB_ROUND - 1) / SLAB_ROUND * SLAB_ROUND : 0;
+    static constexpr int ASLAB = SLAB && FP4A ? (BM * SLAB_KB + SLAB_ROUND - 1) / SLAB_ROUND * SLAB_ROUND : 0;
+    static constexpr int WSLAB_OFF = NBUF * STAGE, ASLAB_OFF = WSLAB_OFF + WSLAB;
+    static constexpr int MAIN = NBUF * STAGE + WSLAB + ASLAB;
+    static constexpr int LDS = MAIN > EP_ALL ? MAIN : EP_ALL;
     static_assert(A_STAGE % (16 * NT) == 0 && W_STAGE % (16 * NT) == 0, "stage split");
     static_assert(SC_ROWS <= NT, "one scale row per thread");
     static_assert(!FP4A || BM <= NT, "one activation scale row per thread");
-    static_assert(NBUF >= 4, "the ring needs NBUF - 1 >= 3 stages in flight");
-    static_assert(LPS * (NBUF - 3) <= 63, "vmcnt range");
+    static_assert(SPS == 1 ? NBUF >= 4 : (SPS == 2 && NBUF == 2), "pipeline shape");
+    static_assert(SPS != 1 || LPS * (NBUF - 3) <= 63, "vmcnt range");
+    static_assert(!SLAB || FP4, "scale slabs hold per-row (MXFP4) scales");
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
 // FP4A: fp4 activations [M, K/2] with E8M0 scales AS [M, K/32] (W4A4); then
 // a_scale is unused (1).
-template <bool FP4, int BM, int BN, int NBUF, int WGM, int WGN, bool FP4A = false>
+template <bool FP4, int BM, int BN, int NBUF, int WGM, int WGN, bool FP4A = false, int SPS = 1,
+          int SLAB_KB = 0>
 __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     const uint8_t *__restrict__ A, int64_t lda, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ W, int64_t ldw, const uint8_t *__restrict__ WS,
     const float *__restrict__ colscale, const uint16_t *__restrict__ bias, int epi,
     uint16_t *__restrict__ Y, int64_t ldy, int M, int N, int K, int group_m,
     const uint8_t *__restrict__ AS = nullptr) {
-    using C = DCfg<FP4, BM, BN, NBUF, WGM, WGN, FP4A>;
+    using C = DCfg<FP4, BM, BN, NBUF, WGM, WGN, FP4A, SPS, SLAB_KB>;
     __shared__ __align__(16) uint8_t lds[C::LDS];
 
     // ---- tile of this workgroup (XCD-aware grouped order)
@@ -447,6 +488,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     const int li = lane & 31, lg = lane >> 5;
     const int KB = K >> 5;
     const int nsteps = K / BK;
+    const int nstages = (nsteps + SPS - 1) / SPS;   // a last half stage reads unused bytes
 
     const int64_t a_bytes = (int64_t)(M - m0) * lda, w_bytes = (int64_t)(N - n0) * ldw;
     const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
@@ -471,21 +513,15 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     // This thread's 16-byte chunk of each load: physical chunk j*NT + tid of
     // a stage (where the LDS-mode load of wave w, lane l, puts its bytes)
     // holds logical chunk c of its row, c = physical column ^ swizzle(row).
-    constexpr int A_ROWS_PER_J = FP4A ? C::NT / 2 : C::NT / 4;
-    constexpr int W_ROWS_PER_J = FP4 ? C::NT / 2 : C::NT / 4;
+    constexpr int A_ROWS_PER_J = C::NT / C::A_CH;
+    constexpr int W_ROWS_PER_J = C::NT / C::W_CH;
     uint32_t a_off, w_off;
-    if (FP4A) {
-        const int row = tid >> 1, c = (tid & 1) ^ swz2(row);
-        a_off = (uint32_t)(row * lda) + 16 * c;
-    } else {
-        const int row = tid >> 2, c = (tid & 3) ^ swz4(row);
+    {
+        const int row = tid / C::A_CH, c = (tid % C::A_CH) ^ swz<C::A_CH>(row);
         a_off = (uint32_t)(row * lda) + 16 * c;
     }
-    if (FP4) {
-        const int row = tid >> 1, c = (tid & 1) ^ swz2(row);
-        w_off = (uint32_t)(row * ldw) + 16 * c;
-    } else {
-        const int row = tid >> 2, c = (tid & 3) ^ swz4(row);
+    {
+        const int row = tid / C::W_CH, c = (tid % C::W_CH) ^ swz<C::W_CH>(row);
         w_off = (uint32_t)(row * ldw) + 16 * c;
     }
     // without a grid every thread reads the first two bytes of kE8M0Ones
@@ -494,13 +530,15 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     const uint32_t sa_off = tid < BM ? (uint32_t)(tid * KB) : OOB;
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t *)lds);
 
-    // Load i (0 .. LPS-1) of step s into ring buffer s % NBUF: the A chunks,
-    // the W chunks, then the scale pairs. Past the last step every lane
-    // reads outside the buffers' ranges, which writes zeros.
-    auto issue_one = [&](int s, int i) {
-        const bool live = s < nsteps;
-        const uint32_t kbase = (uint32_t)__builtin_amdgcn_readfirstlane(live ? s * BK : 0);
-        const uint32_t base = lds0 + (uint32_t)((s % NBUF) * C::STAGE) + (uint32_t)wave * 1024u;
+    // Load i (0 .. LPS-1) of stage p into buffer p % NBUF: the A chunks, the
+    // W chunks, then each step's scale pairs (weights, then fp4 activations).
+    // Past the last stage every lane reads outside the buffers' ranges,
+    // which writes zeros.
+    auto issue_one = [&](int p, int i) {
+        const bool live = p < nstages;
+        const uint32_t kbase = (uint32_t)__builtin_amdgcn_readfirstlane(live ? p * C::KS : 0);
+        const uint32_t sbase = lds0 + (uint32_t)((p % NBUF) * C::STAGE);
+        const uint32_t base = sbase + (uint32_t)wave * 1024u;
         if (i < C::A_LD) {
             dma_b128(rsA, base + i * C::NT * 16, live ? a_off : OOB,
                      (uint32_t)(i * A_ROWS_PER_J * lda) + (FP4A ? kbase / 2 : kbase));
@@ -508,12 +546,16 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
             const int j = i - C::A_LD;
             dma_b128(rsW, base + C::A_STAGE + j * C::NT * 16, live ? w_off : OOB,
                      (uint32_t)(j * W_ROWS_PER_J * ldw) + (FP4 ? kbase / 2 : kbase));
-        } else if (i == C::A_LD + C::W_LD) {
-            dma_u16(rsS, lds0 + (uint32_t)((s % NBUF) * C::STAGE + C::SC_OFF) + (uint32_t)wave * 256u,
-                    live ? s_off + (kbase >> s_kshift) : OOB);
+        } else if (C::SLAB) {
+            // unreachable: with scale slabs a stage has only tile loads
+        } else if (i < C::A_LD + C::W_LD + SPS) {
+            const int q = i - C::A_LD - C::W_LD;   // the stage's step q
+            dma_u16(rsS, sbase + (uint32_t)(C::SC_OFF + q * 4 * C::NT) + (uint32_t)wave * 256u,
+                    live ? s_off + ((kbase + q * BK) >> s_kshift) : OOB);
         } else {   // FP4A: the activation rows' scale pairs
-            dma_u16(rsSA, lds0 + (uint32_t)((s % NBUF) * C::STAGE + C::SCA_OFF) + (uint32_t)wave * 256u,
-                    live ? sa_off + (kbase >> 5) : OOB);
+            const int q = i - C::A_LD - C::W_LD - SPS;
+            dma_u16(rsSA, sbase + (uint32_t)(C::SCA_OFF + q * 4 * C::NT) + (uint32_t)wave * 256u,
+                    live ? sa_off + ((kbase + q * BK) >> 5) : OOB);
         }
     };
 
@@ -531,33 +573,38 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         int sc[C::TN];
         int sa[C::TM];
     };
-    // fragments of step s (ring buffer s % NBUF): A tile a, W tile b (+ its scales)
+    // fragments of step s (stage s / SPS in buffer (s / SPS) % NBUF, its
+    // step q = s % SPS): A tile a, W tile b (+ their scales). A step takes
+    // 32 bytes of an e4m3 row (chunks 4q + lg and 4q + 2 + lg) or 16 bytes
+    // of an fp4 row (chunk 2q + lg).
     auto read_a = [&](Frags &f, int s, int a) {
-        const uint8_t *sa = lds + (s % NBUF) * C::STAGE;
+        const int q = s % SPS;
+        const uint8_t *sa = lds + ((s / SPS) % NBUF) * C::STAGE;
         const int row = wm * (BM / WGM) + a * 32 + li;
+        const int fz = swz<C::A_CH>(row);
+        const uint8_t *p = sa + row * C::AROW;
         if (FP4A) {
-            f.a[a] = pack8(lds16(sa + row * C::AROW + 16 * (lg ^ swz2(row))),
-                           make_uint4(0u, 0u, 0u, 0u));
-            f.sa[a] = (sa + C::SCA_OFF)[4 * row + lg];
+            f.a[a] = pack8(lds16(p + 16 * ((2 * q + lg) ^ fz)), make_uint4(0u, 0u, 0u, 0u));
+            if (C::SLAB) f.sa[a] = (lds + C::ASLAB_OFF)[row * KB + 2 * s + lg];
+            else f.sa[a] = (sa + C::SCA_OFF + q * 4 * C::NT)[4 * row + lg];
         } else {
-            const int fz = swz4(row);
-            const uint8_t *p = sa + row * BK;
-            f.a[a] = pack8(lds16(p + 16 * (lg ^ fz)), lds16(p + 16 * ((2 + lg) ^ fz)));
+            f.a[a] = pack8(lds16(p + 16 * ((4 * q + lg) ^ fz)), lds16(p + 16 * ((4 * q + 2 + lg) ^ fz)));
             f.sa[a] = E8M0_ONE;
         }
     };
     auto read_b = [&](Frags &f, int s, int b) {
-        const uint8_t *sw = lds + (s % NBUF) * C::STAGE + C::A_STAGE;
-        const uint8_t *ss = lds + (s % NBUF) * C::STAGE + C::SC_OFF;
+        const int q = s % SPS;
+        const uint8_t *sw = lds + ((s / SPS) % NBUF) * C::STAGE + C::A_STAGE;
+        const uint8_t *ss = lds + ((s / SPS) % NBUF) * C::STAGE + C::SC_OFF + q * 4 * C::NT;
         const int row = wn * (BN / WGN) + b * 32 + li;
+        const int fz = swz<C::W_CH>(row);
+        const uint8_t *p = sw + row * C::WROW;
         if (FP4) {
-            f.b[b] = pack8(lds16(sw + row * C::WROW + 16 * (lg ^ swz2(row))),
-                           make_uint4(0u, 0u, 0u, 0u));
-            f.sc[b] = ss[4 * row + lg];
+            f.b[b] = pack8(lds16(p + 16 * ((2 * q + lg) ^ fz)), make_uint4(0u, 0u, 0u, 0u));
+            if (C::SLAB) f.sc[b] = (lds + C::WSLAB_OFF)[row * KB + 2 * s + lg];
+            else f.sc[b] = ss[4 * row + lg];
         } else {
-            const int fz = swz4(row);
-            const uint8_t *p = sw + row * C::WROW;
-            f.b[b] = pack8(lds16(p + 16 * (lg ^ fz)), lds16(p + 16 * ((2 + lg) ^ fz)));
+            f.b[b] = pack8(lds16(p + 16 * ((4 * q + lg) ^ fz)), lds16(p + 16 * ((4 * q + 2 + lg) ^ fz)));
             f.sc[b] = ss[4 * (row >> 5) + lg];
         }
     };
@@ -565,20 +612,17 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     // MFMAs interleaved between the reads they spread over the whole step:
     // issued as one block they stall the wave's instruction stream, which
     // (one wave per SIMD) is the MFMA stream.
-    auto reads_and_loads = [&](Frags &f, int s_read, int s_load) {
+    // (nl loads of stage p_load, spread evenly before the TM + TN reads)
+    auto reads_and_loads = [&](Frags &f, int s_read, int p_load, int nl) {
+        constexpr int R = C::TM + C::TN;
         int k = 0;
 #pragma unroll
-        for (int a = 0; a < C::TM; ++a) {
-            if (k < C::LPS) issue_one(s_load, k++);
-            read_a(f, s_read, a);
-        }
+        for (int r = 0; r < R; ++r) {
 #pragma unroll
-        for (int b = 0; b < C::TN; ++b) {
-            if (k < C::LPS) issue_one(s_load, k++);
-            read_b(f, s_read, b);
+            for (; k < (r + 1) * nl / R; ++k) issue_one(p_load, k);
+            if (r < C::TM) read_a(f, s_read, r);
+            else read_b(f, s_read, r - C::TM);
         }
-#pragma unroll
-        for (; k < C::LPS; ++k) issue_one(s_load, k);
     };
     auto mfmas = [&](const Frags &f) {
 #pragma unroll
@@ -597,12 +641,36 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         }
     };
 
-    // prologue: steps 0 .. NBUF-2 in flight; wait for steps 0 and 1
+    // prologue: SPS = 1, stages 0 .. NBUF-2 in flight, wait for stages 0 and
+    // 1; SPS = 2, both stages in flight, wait for stage 0
+    constexpr int PRO = SPS == 1 ? NBUF - 1 : 2;
+    if constexpr (C::SLAB) {
+        // the tile's scale rows, [rows, KB] bytes, in 4-byte pieces: piece d
+        // of the flattened slab comes from row d / (KB / 4); pieces past the
+        // last row of the tile or of the matrix read zeros
+        const int kq = KB >> 2;
+        const int w_pieces = C::SC_ROWS * kq;
+        for (int j = 0; j * C::NT < w_pieces; ++j) {
+            const int d = j * C::NT + tid, r = d / kq;
+            const uint32_t off = d < w_pieces ? (uint32_t)(r * KB + 4 * (d - r * kq)) : OOB;
+            dma_u32(rsS, (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + C::WSLAB_OFF + j * C::NT * 4 + wave * 256),
+                    off);
+        }
+        if constexpr (FP4A) {
+            const int a_pieces = BM * kq;
+            for (int j = 0; j * C::NT < a_pieces; ++j) {
+                const int d = j * C::NT + tid, r = d / kq;
+                const uint32_t off = d < a_pieces ? (uint32_t)(r * KB + 4 * (d - r * kq)) : OOB;
+                dma_u32(rsSA, (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + C::ASLAB_OFF + j * C::NT * 4 + wave * 256),
+                        off);
+            }
+        }
+    }
 #pragma unroll
-    for (int s = 0; s < NBUF - 1; ++s)
+    for (int p = 0; p < PRO; ++p)
 #pragma unroll
-        for (int i = 0; i < C::LPS; ++i) issue_one(s, i);
-    wait_loads_and_barrier<C::LPS * (NBUF - 3)>();
+        for (int i = 0; i < C::LPS; ++i) issue_one(p, i);
+    wait_loads_and_barrier<SPS == 1 ? C::LPS * (NBUF - 3) : C::LPS>();
     Frags f0, f1;
 #pragma unroll
     for (int a = 0; a < C::TM; ++a) read_a(f0, 0, a);
@@ -618,16 +686,44 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     // even MFMA / read / load mix.
     auto step = [&](const Frags &cur, Frags &nxt, int s) {
         mfmas(cur);
-        reads_and_loads(nxt, s + 1, s + NBUF - 1);
+        reads_and_loads(nxt, s + 1, s + NBUF - 1, C::LPS);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
         wait_loads_and_barrier<C::LPS * (NBUF - 3)>();
         __builtin_amdgcn_sched_barrier(0);
     };
+    // SPS = 2, steps 2p and 2p + 1 of stage p. Even step 2p: MFMAs, the
+    // reads of step 2p + 1 (stage p), then wait until this wave's reads
+    // are done and stage p + 1 has landed, and meet: stage p is then free
+    // in every wave. Odd step 2p + 1: MFMAs, the reads of step 2p + 2
+    // (stage p + 1) and the loads of stage p + 2 into stage p's buffer,
+    // which have until the end of step 2p + 2 to land.
+    auto step_even = [&](const Frags &cur, Frags &nxt, int s) {
+        mfmas(cur);
+        reads_and_loads(nxt, s + 1, 0, 0);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+        wait_loads_and_barrier<0>();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto step_odd = [&](const Frags &cur, Frags &nxt, int s) {
+        mfmas(cur);
+        reads_and_loads(nxt, s + 1, (s + 3) / 2, C::LPS);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+    };
     int s = 0;
-    for (; s + 1 < nsteps; s += 2) {
-        step(f0, f1, s);
-        step(f1, f0, s + 1);
+    if constexpr (SPS == 1) {
+        for (; s + 1 < nsteps; s += 2) {
+            step(f0, f1, s);
+            step(f1, f0, s + 1);
+        }
+    } else {
+        for (; s + 1 < nsteps; s += 2) {
+            step_even(f0, f1, s);
+            step_odd(f1, f0, s + 1);
+        }
     }
     if (s < nsteps) mfmas(f0);
 
@@ -694,12 +790,13 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     }
 }
 
-template <bool FP4, int BM, int BN, int NBUF, int WGM = 2, int WGN = 2, bool FP4A = false>
+template <bool FP4, int BM, int BN, int NBUF, int WGM = 2, int WGN = 2, bool FP4A = false,
+          int SPS = 1, int SLAB_KB = 0>
 hipError_t launch_tile_dma(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w,
                            int64_t ldw, const uint8_t *ws, const float *cs, const uint16_t *bias,
                            int epi, uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                            hipStream_t st, const uint8_t *a_e8m0 = nullptr) {
-    auto kern = gemm_prefill_dma_kernel<FP4, BM, BN, NBUF, WGM, WGN, FP4A>;
+    auto kern = gemm_prefill_dma_kernel<FP4, BM, BN, NBUF, WGM, WGN, FP4A, SPS, SLAB_KB>;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(WGM * WGN * 64), 0, st, a, lda, as, w,
                        ldw, ws, cs, bias, epi, y, ldy, (int)M, (int)N, (int)K, 8, a_e8m0);
@@ -736,46 +833,51 @@ int best_shape(bool fp4, int64_t M, int64_t N, int64_t K, int num_cus, double *c
     return best;
 }
 
+// MXFP4 tiles with their E8M0 rows in LDS (two-step stages): the largest
+// K / 32 each variant holds.
+constexpr int SLAB_KB_W4A8 = 192;   // K <= 6144
+constexpr int SLAB_KB_W4A4 = 160;   // K <= 5120 (weight and activation slabs)
+
 hipError_t launch_shape(int shape, bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
                         const uint8_t *w, int64_t ldw, const uint8_t *ws, const float *cs,
                         const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
                         int64_t N, int64_t K, hipStream_t st, const uint8_t *a_e8m0) {
+#define BSG_ARGS a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st
     if (a_e8m0) {   // W4A4: fp4 activations with their E8M0 scales, MXFP4 weights
+        if (K % 128 == 0 && K / 32 <= SLAB_KB_W4A4) {
+            switch (shape) {
+            case 0: return launch_tile_dma<true, 256, 256, 2, 4, 2, true, 2, SLAB_KB_W4A4>(BSG_ARGS, a_e8m0);
+            case 1: return launch_tile_dma<true, 256, 128, 2, 2, 2, true, 2, SLAB_KB_W4A4>(BSG_ARGS, a_e8m0);
+            default: return launch_tile_dma<true, 128, 128, 2, 2, 2, true, 2, SLAB_KB_W4A4>(BSG_ARGS, a_e8m0);
+            }
+        }
         switch (shape) {
-        case 0:
-            return launch_tile_dma<true, 256, 256, 4, 4, 2, true>(a, lda, a_scale, w, ldw, ws, cs,
-                                                                  bias, epi, y, ldy, M, N, K, st,
-                                                                  a_e8m0);
-        case 1:
-            return launch_tile_dma<true, 256, 128, 4, 2, 2, true>(a, lda, a_scale, w, ldw, ws, cs,
-                                                                  bias, epi, y, ldy, M, N, K, st,
-                                                                  a_e8m0);
-        default:
-            return launch_tile_dma<true, 128, 128, 4, 2, 2, true>(a, lda, a_scale, w, ldw, ws, cs,
-                                                                  bias, epi, y, ldy, M, N, K, st,
-                                                                  a_e8m0);
+        case 0: return launch_tile_dma<true, 256, 256, 4, 4, 2, true>(BSG_ARGS, a_e8m0);
+        case 1: return launch_tile_dma<true, 256, 128, 4, 2, 2, true>(BSG_ARGS, a_e8m0);
+        default: return launch_tile_dma<true, 128, 128, 4, 2, 2, true>(BSG_ARGS, a_e8m0);
+        }
+    }
+    if (fp4 && K % 128 == 0 && K / 32 <= SLAB_KB_W4A8) {
+        switch (shape) {
+        case 0: return launch_tile_dma<true, 256, 256, 2, 4, 2, false, 2, SLAB_KB_W4A8>(BSG_ARGS);
+        case 1: return launch_tile_dma<true, 256, 128, 2, 2, 2, false, 2, SLAB_KB_W4A8>(BSG_ARGS);
+        default: return launch_tile_dma<true, 128, 128, 2, 2, 2, false, 2, SLAB_KB_W4A8>(BSG_ARGS);
         }
     }
     switch (shape) {
     case 0:
         // MXFP4 weights: eight waves (4 x 2, each 64 x 128) measured faster
         // than four for 256x256 tiles; e4m3 weights: four
-        if (fp4)
-            return launch_tile_dma<true, 256, 256, 4, 4, 2>(a, lda, a_scale, w, ldw, ws, cs, bias, epi,
-                                                            y, ldy, M, N, K, st);
-        return launch_tile_dma<false, 256, 256, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy,
-                                                   M, N, K, st);
+        if (fp4) return launch_tile_dma<true, 256, 256, 4, 4, 2>(BSG_ARGS);
+        return launch_tile_dma<false, 256, 256, 4>(BSG_ARGS);
     case 1:
-        return fp4 ? launch_tile_dma<true, 256, 128, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y,
-                                                        ldy, M, N, K, st)
-                   : launch_tile_dma<false, 256, 128, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y,
-                                                         ldy, M, N, K, st);
+        return fp4 ? launch_tile_dma<true, 256, 128, 4>(BSG_ARGS)
+                   : launch_tile_dma<false, 256, 128, 4>(BSG_ARGS);
     default:
-        return fp4 ? launch_tile_dma<true, 128, 128, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y,
-                                                        ldy, M, N, K, st)
-                   : launch_tile_dma<false, 128, 128, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y,
-                                                         ldy, M, N, K, st);
+        return fp4 ? launch_tile_dma<true, 128, 128, 4>(BSG_ARGS)
+                   : launch_tile_dma<false, 128, 128, 4>(BSG_ARGS);
     }
+#undef BSG_ARGS
 }
 
 // One launch of the cheapest tile shape, or two launches over column ranges

@@ -85,10 +85,12 @@ def test_prefill_shapes(fmt, M, N, K):
 
 
 # ---- prefill with K a multiple of 64 (tiles staged by LDS-mode loads):
-# ragged M and N on each tile size, outputs past M / N untouched
+# ragged M and N on each tile size, outputs past M / N untouched; MXFP4
+# weights with their E8M0 rows in LDS (K % 128 == 0, K <= 6144, up to the
+# limit) and without (K % 128 == 64, or K past the limit)
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
 @pytest.mark.parametrize("M,N,K", [(65, 96, 64), (200, 320, 640), (129, 416, 128),
-                                   (300, 288, 1024)])
+                                   (300, 288, 1024), (130, 96, 6144), (70, 160, 6272)])
 def test_prefill_dma_shapes(fmt, M, N, K):
     for epi in EPIS:
         _full_check(fmt, M, N, K, epi, seed=M + N + K + epi)

@@ -86,7 +86,8 @@ def _run(a, sa, w, sw, b, epi, pad=0):
 
 @pytest.mark.parametrize("M,N,K", [
     (1, 96, 1056), (5, 2048, 512), (16, 32768 + 32, 640), (40, 2080, 1184), (64, 512, 4096),
-    (65, 256, 128), (200, 320, 512), (300, 4192, 256), (513, 1024, 2048), (260, 35 * 256, 1024)])
+    (65, 256, 128), (200, 320, 512), (300, 4192, 256), (513, 1024, 2048), (260, 35 * 256, 1024),
+    (130, 96, 5120), (70, 160, 5248), (97, 160, 1088)])   # E8M0 rows in LDS up to K = 5120
 @pytest.mark.parametrize("epi", [synth.EPI_NONE, synth.EPI_BIAS_GELU_TANH])
 def test_w4a4_shapes(M, N, K, epi):
     a, sa, w, sw, b = _problem(M, N, K, seed=M + N + K + epi)
