@@ -149,11 +149,14 @@ __device__ __forceinline__ v4f mfma16x(const v8i &a, const v8i &b, const v4f &c,
 }
 
 // Weights as the instruction's A operand (scale sw), activations as its B
-// operand (scale sa: E8M0_ONE for e4m3 activations).
-template <bool FP4W, bool FP4A>
+// operand (scale sa: E8M0_ONE for e4m3 activations). SEL picks the byte of
+// each 32-bit scale operand the instruction uses (measured on gfx950: byte
+// SEL, little-endian).
+template <bool FP4W, bool FP4A, int SEL = 0>
 __device__ __forceinline__ v16f mfma32_wt2(const v8i &w, const v8i &a, const v16f &c, int sw, int sa) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-        w, a, c, FP4W ? MFMA_FMT_FP4 : MFMA_FMT_FP8, FP4A ? MFMA_FMT_FP4 : MFMA_FMT_FP8, 0, sw, 0, sa);
+        w, a, c, FP4W ? MFMA_FMT_FP4 : MFMA_FMT_FP8, FP4A ? MFMA_FMT_FP4 : MFMA_FMT_FP8, SEL, sw,
+        FP4A ? SEL : 0, sa);
 }
 
 __device__ __forceinline__ v8i pack8(const uint4 &lo, const uint4 &hi) {

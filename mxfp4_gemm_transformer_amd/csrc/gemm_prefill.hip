@@ -26,6 +26,8 @@
 // Workgroups are numbered so that consecutive tiles in a grouped order land
 // on the same XCD (workgroups are dispatched round-robin over the 8 XCDs),
 // which keeps the A and W panels a group shares in that XCD's L2.
+#include <type_traits>
+
 #include "bs_device.hpp"
 #include "bs_kernels.hpp"
 
@@ -574,26 +576,34 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         int sa[C::TM];
     };
     // fragments of step s (stage s / SPS in buffer (s / SPS) % NBUF, its
-    // step q = s % SPS): A tile a, W tile b (+ their scales). A step takes
-    // 32 bytes of an e4m3 row (chunks 4q + lg and 4q + 2 + lg) or 16 bytes
-    // of an fp4 row (chunk 2q + lg).
-    auto read_a = [&](Frags &f, int s, int a) {
-        const int q = s % SPS;
+    // step q = s % SPS, given as the constant qk): A tile a, W tile b (+
+    // their scales). A step takes 32 bytes of an e4m3 row (chunks 4q + lg and
+    // 4q + 2 + lg) or 16 bytes of an fp4 row (chunk 2q + lg). With scale
+    // slabs, step q = 0 reads the stage's 4 E8M0 bytes of the row as one
+    // word, shifted so that byte 2q is this lane's block for step q (the
+    // MFMA selects it); step q = 1 reuses that word (copied by the caller).
+    auto read_a = [&](Frags &f, int s, int a, int qk) {
+        const int q = SPS == 1 ? 0 : qk;
         const uint8_t *sa = lds + ((s / SPS) % NBUF) * C::STAGE;
         const int row = wm * (BM / WGM) + a * 32 + li;
         const int fz = swz<C::A_CH>(row);
         const uint8_t *p = sa + row * C::AROW;
         if (FP4A) {
             f.a[a] = pack8(lds16(p + 16 * ((2 * q + lg) ^ fz)), make_uint4(0u, 0u, 0u, 0u));
-            if (C::SLAB) f.sa[a] = (lds + C::ASLAB_OFF)[row * KB + 2 * s + lg];
-            else f.sa[a] = (sa + C::SCA_OFF + q * 4 * C::NT)[4 * row + lg];
+            if (C::SLAB) {
+                if (q == 0)
+                    f.sa[a] = (int)(*reinterpret_cast<const uint32_t *>(lds + C::ASLAB_OFF + row * KB + 2 * s) >>
+                                    (8 * lg));
+            } else {
+                f.sa[a] = (sa + C::SCA_OFF + q * 4 * C::NT)[4 * row + lg];
+            }
         } else {
             f.a[a] = pack8(lds16(p + 16 * ((4 * q + lg) ^ fz)), lds16(p + 16 * ((4 * q + 2 + lg) ^ fz)));
             f.sa[a] = E8M0_ONE;
         }
     };
-    auto read_b = [&](Frags &f, int s, int b) {
-        const int q = s % SPS;
+    auto read_b = [&](Frags &f, int s, int b, int qk) {
+        const int q = SPS == 1 ? 0 : qk;
         const uint8_t *sw = lds + ((s / SPS) % NBUF) * C::STAGE + C::A_STAGE;
         const uint8_t *ss = lds + ((s / SPS) % NBUF) * C::STAGE + C::SC_OFF + q * 4 * C::NT;
         const int row = wn * (BN / WGN) + b * 32 + li;
@@ -601,8 +611,13 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         const uint8_t *p = sw + row * C::WROW;
         if (FP4) {
             f.b[b] = pack8(lds16(p + 16 * ((2 * q + lg) ^ fz)), make_uint4(0u, 0u, 0u, 0u));
-            if (C::SLAB) f.sc[b] = (lds + C::WSLAB_OFF)[row * KB + 2 * s + lg];
-            else f.sc[b] = ss[4 * row + lg];
+            if (C::SLAB) {
+                if (q == 0)
+                    f.sc[b] = (int)(*reinterpret_cast<const uint32_t *>(lds + C::WSLAB_OFF + row * KB + 2 * s) >>
+                                    (8 * lg));
+            } else {
+                f.sc[b] = ss[4 * row + lg];
+            }
         } else {
             f.b[b] = pack8(lds16(p + 16 * ((4 * q + lg) ^ fz)), lds16(p + 16 * ((4 * q + 2 + lg) ^ fz)));
             f.sc[b] = ss[4 * (row >> 5) + lg];
@@ -613,24 +628,28 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     // issued as one block they stall the wave's instruction stream, which
     // (one wave per SIMD) is the MFMA stream.
     // (nl loads of stage p_load, spread evenly before the TM + TN reads)
-    auto reads_and_loads = [&](Frags &f, int s_read, int p_load, int nl) {
+    auto reads_and_loads = [&](Frags &f, int s_read, int p_load, int nl, int qk) {
         constexpr int R = C::TM + C::TN;
         int k = 0;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
 #pragma unroll
             for (; k < (r + 1) * nl / R; ++k) issue_one(p_load, k);
-            if (r < C::TM) read_a(f, s_read, r);
-            else read_b(f, s_read, r - C::TM);
+            if (r < C::TM) read_a(f, s_read, r, qk);
+            else read_b(f, s_read, r - C::TM, qk);
         }
     };
-    auto mfmas = [&](const Frags &f) {
+    // MFMAs of a step with stage step qk (slab scales: byte 2 qk of each word)
+    auto mfmas = [&](const Frags &f, auto qk) {
+        constexpr int SEL = C::SLAB ? 2 * decltype(qk)::value : 0;
 #pragma unroll
         for (int a = 0; a < C::TM; ++a)
 #pragma unroll
             for (int b = 0; b < C::TN; ++b)
-                acc[a][b] = mfma32_wt2<FP4, FP4A>(f.b[b], f.a[a], acc[a][b], f.sc[b], f.sa[a]);
+                acc[a][b] = mfma32_wt2<FP4, FP4A, SEL>(f.b[b], f.a[a], acc[a][b], f.sc[b], f.sa[a]);
     };
+    using Q0 = std::integral_constant<int, 0>;
+    using Q1 = std::integral_constant<int, 1>;
     auto interleave = [&]() {
         constexpr int NM = C::TM * C::TN;
         constexpr int NR = 2 * (C::TM + C::TN) + C::TN;
@@ -673,9 +692,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     wait_loads_and_barrier<SPS == 1 ? C::LPS * (NBUF - 3) : C::LPS>();
     Frags f0, f1;
 #pragma unroll
-    for (int a = 0; a < C::TM; ++a) read_a(f0, 0, a);
+    for (int a = 0; a < C::TM; ++a) read_a(f0, 0, a, 0);
 #pragma unroll
-    for (int b = 0; b < C::TN; ++b) read_b(f0, 0, b);
+    for (int b = 0; b < C::TN; ++b) read_b(f0, 0, b, 0);
 
     // step s: MFMAs on step s's fragments, interleaved with the reads of
     // step s + 1's and the loads of step s + NBUF - 1; then wait until step
@@ -685,8 +704,8 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     // them the compiler moves MFMAs across it and the steps lose their
     // even MFMA / read / load mix.
     auto step = [&](const Frags &cur, Frags &nxt, int s) {
-        mfmas(cur);
-        reads_and_loads(nxt, s + 1, s + NBUF - 1, C::LPS);
+        mfmas(cur, Q0{});
+        reads_and_loads(nxt, s + 1, s + NBUF - 1, C::LPS, 0);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
         wait_loads_and_barrier<C::LPS * (NBUF - 3)>();
@@ -699,8 +718,14 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     // (stage p + 1) and the loads of stage p + 2 into stage p's buffer,
     // which have until the end of step 2p + 2 to land.
     auto step_even = [&](const Frags &cur, Frags &nxt, int s) {
-        mfmas(cur);
-        reads_and_loads(nxt, s + 1, 0, 0);
+        mfmas(cur, Q0{});
+        reads_and_loads(nxt, s + 1, 0, 0, 1);
+        if (C::SLAB) {   // step 2p + 1 uses step 2p's scale words
+#pragma unroll
+            for (int b = 0; b < C::TN; ++b) nxt.sc[b] = cur.sc[b];
+#pragma unroll
+            for (int a = 0; a < C::TM; ++a) nxt.sa[a] = cur.sa[a];
+        }
         interleave();
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
@@ -708,8 +733,8 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         __builtin_amdgcn_sched_barrier(0);
     };
     auto step_odd = [&](const Frags &cur, Frags &nxt, int s) {
-        mfmas(cur);
-        reads_and_loads(nxt, s + 1, (s + 3) / 2, C::LPS);
+        mfmas(cur, Q1{});
+        reads_and_loads(nxt, s + 1, (s + 3) / 2, C::LPS, 0);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -725,7 +750,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
             step_odd(f1, f0, s + 1);
         }
     }
-    if (s < nsteps) mfmas(f0);
+    if (s < nsteps) mfmas(f0, Q0{});
 
     // ---- epilogue: every load has landed and every wave is done with the
     // ring. Each wave scales one 32-row slab of its tile by the per-token
