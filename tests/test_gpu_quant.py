@@ -52,7 +52,11 @@ def test_quant_prefill_full_size():
 
 
 @pytest.mark.parametrize("M,K", [(3, 32), (17, 96), (5, 544), (300, 4128), (33, 8192 + 32),
-                                 (2, 65536 + 64), (1, 131072)])
+                                 (2, 65536 + 64), (1, 131072),
+                                 # many rows: 64 / 256 / 512 threads a row, 1-3 chunks a
+                                 # thread, and rows too long for 512 threads
+                                 (513, 96), (700, 2080), (600, 4128), (1030, 8224),
+                                 (512, 16384), (520, 32768)])
 def test_quant_ragged_shapes(M, K):
     rng = np.random.default_rng(M * 1000 + K)
     x = synth.to_bf16_bits((rng.standard_normal((M, K)) * rng.uniform(0.01, 50, (M, 1))).astype(np.float32))
