@@ -81,7 +81,7 @@ def test_add_rms_workload_full_size(M):
 
 @pytest.mark.parametrize("M,K", [(1, 32), (3, 96), (7, 256), (64, 1056), (65, 2080), (100, 5120),
                                  (513, 512), (600, 8192), (20, 17408), (300, 17408),
-                                 (2, 32768), (530, 32768)])
+                                 (2, 32768), (530, 32768), (520, 12288), (512, 5120)])
 @pytest.mark.parametrize("with_res", [True, False])
 def test_rms_shapes(M, K, with_res):
     d = synth.producer_inputs("add_rms", M, K, seed=M + K)
@@ -115,7 +115,7 @@ def test_silu_mul_workload_full_size(M):
 
 
 @pytest.mark.parametrize("M,I", [(1, 32), (5, 96), (9, 256), (64, 2048), (65, 1056), (513, 512),
-                                 (33, 17408), (530, 32768)])
+                                 (33, 17408), (530, 32768), (520, 16384), (512, 17408)])
 def test_silu_mul_shapes(M, I):
     d = synth.producer_inputs("silu_mul", M, I, seed=M + I)
     _check_silu(d["gate_up"], what="silu M=%d I=%d" % (M, I))
