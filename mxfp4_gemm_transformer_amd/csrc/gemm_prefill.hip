@@ -357,7 +357,9 @@ hipError_t launch_tile(const uint8_t *a, int64_t lda, const float *as, const uin
 // write LDS themselves. A ring of NBUF stages keeps NBUF - 1 steps of loads
 // in flight; one wait on the vector-memory counter and one barrier per step
 // publish the stage the next step reads. The weight scales of a step travel
-// as one 2-byte load per scale row into a 4-byte slot per thread.
+// as one 2-byte load per scale row into a 4-byte slot per thread, except in
+// the MXFP4 tiles with scale slabs (two-step stages, see DCfg), which load
+// their tile's E8M0 rows for all of K once, ahead of the first stage.
 //
 // The waits are written out because the compiler does not track LDS-mode
 // loads issued from inline assembly: every thread issues the same loads in
