@@ -844,21 +844,30 @@ hipError_t launch_tile_dma(const uint8_t *a, int64_t lda, const float *as, const
 // ---- DMA-path planning. Workgroups run in rounds of one per CU; a round of
 // tiles of one shape costs c * K + e (in units of one k of a 256x256 tile),
 // c and e fitted to MI355X timings per tile shape: smaller tiles do less work
-// per round at a lower MFMA efficiency.
+// per round at a lower MFMA efficiency. 128x128 tiles need at most 72 KB of
+// LDS, so two share a CU and overlap one's prologue and epilogue with the
+// other's MFMAs: a CU with two or more of them runs them in pairs, a pair
+// costing PAIR x the work of two plus one e (fitted on 2048x4096x1024, where
+// 512 such tiles run in 18.8 us against 20.0 us for 256 of 256x128).
 struct TileShape {
     int bm, bn;
     double c, e;
+    int per_cu;   // workgroups resident on a CU at once
 };
 constexpr TileShape SHAPES[] = {
-    {256, 256, 1.0, 930.0},
-    {256, 128, 0.73, 465.0},
-    {128, 128, 0.415, 236.0},
+    {256, 256, 1.0, 930.0, 1},
+    {256, 128, 0.73, 465.0, 1},
+    {128, 128, 0.415, 236.0, 2},
 };
 constexpr double LAUNCH_COST = 200.0;   // a second launch, same units
+constexpr double PAIR = 1.06;
 
 double shape_cost(const TileShape &t, int64_t M, int64_t N, int64_t K, int num_cus) {
     const int64_t tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
-    return (double)((tiles + num_cus - 1) / num_cus) * (t.c * (double)K + t.e);
+    const int64_t per_cu = (tiles + num_cus - 1) / num_cus;
+    if (t.per_cu == 2 && per_cu >= 2)
+        return (double)((per_cu + 1) / 2) * (2.0 * PAIR * t.c * (double)K + t.e);
+    return (double)per_cu * (t.c * (double)K + t.e);
 }
 
 int best_shape(bool fp4, int64_t M, int64_t N, int64_t K, int num_cus, double *cost) {

@@ -97,13 +97,13 @@ def test_prefill_dma_shapes(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
-@pytest.mark.parametrize("M,N,K", [(4000, 2016, 192), (3900, 4064, 128), (4000, 4192, 128),
-                                   (4096, 7168, 128)])
+@pytest.mark.parametrize("M,N,K", [(4000, 2016, 2048), (3900, 4064, 1024), (3900, 4064, 1088),
+                                   (4000, 4192, 1024)])
 def test_prefill_dma_large_tiles(fmt, M, N, K):
-    # 256x128 and 256x256 tiles (the tile count reaches the CU count), ragged
-    # in M and N; the last two shapes run as two launches over column ranges
-    # (256x256 tiles in one whole round, then 256x128 tiles over a 96-column
-    # rest, or 256x192 tiles for e4m3 weights); y is a view into a larger
+    # the launch plans past one round of small tiles, ragged in M and N: one
+    # launch of 256x128 tiles, one of 256x256 (K % 128 == 0 and == 64), and
+    # two launches over column ranges (256x256 tiles in one whole round, then
+    # 128x128 tiles, two to a CU, over the rest); y is a view into a larger
     # NaN-filled buffer
     for epi in (synth.EPI_NONE, synth.EPI_BIAS_GELU_TANH):
         a, s, w, ws, b = _random_problem(fmt, M, N, K, seed=M + N + epi)
