@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", default="decode",
-                   choices=["tiny", "decode", "prefill", "ffn_up", "ffn_up_bias", "gate_up",
+                   choices=["tiny", "decode", "prefill", "prefill_shard", "ffn_up", "ffn_up_bias", "gate_up",
                             "gate_up_w4a4", "lm_head", "moe", "add_rms", "silu_mul"],
                    help="a GEMM workload (quantize + GEMM per step), or a fused producer "
                         "(add_rms: residual add + RMSNorm + quantize on [M, 5120]; silu_mul: "

@@ -17,15 +17,16 @@ constexpr int QBLOCK = 256;
 
 // Largest |bf16| of the 8 values in a 16-byte chunk, as a magnitude bit
 // pattern (for finite values, integer order of exp|mantissa = value order).
+// Both halves of a word at once with packed 16-bit maxima.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t absmax8(const uint4 &c) {
-    uint32_t m = 0;
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m = max(m, w[i] & 0x7FFFu);
-        m = max(m, (w[i] >> 16) & 0x7FFFu);
-    }
-    return m;
+    const u16x2 a = __builtin_bit_cast(u16x2, c.x & 0x7FFF7FFFu);
+    const u16x2 b = __builtin_bit_cast(u16x2, c.y & 0x7FFF7FFFu);
+    const u16x2 d = __builtin_bit_cast(u16x2, c.z & 0x7FFF7FFFu);
+    const u16x2 e = __builtin_bit_cast(u16x2, c.w & 0x7FFF7FFFu);
+    const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                              __builtin_elementwise_max(d, e));
+    return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
 // The e4m3 codes of fl32(x / s) for the 8 bf16 values x of a 16-byte chunk,
@@ -62,26 +63,35 @@ __device__ __forceinline__ uint2 encode8(const uint4 &c, float s, float r, bool 
         return make_uint2(out[0], out[1]);
     }
     float xv[8], q[8];
-    bool exact = r_ok;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         xv[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
         xv[2 * i + 1] = bf16_to_f32(w[i] >> 16);
     }
+    // Two running minima instead of a flag per value (one shift-add and
+    // half a min3 per value): dmin, over (low 20 bits - 0x80000 + 4) mod
+    // 2^20 moved to the top of the word, is at most 8 << 12 exactly when
+    // some product's low 20 bits lie within 4 of 0x80000; qmin is the
+    // smallest |product| (finite here whenever r is, so no NaN reaches it).
+    uint32_t dmin = 0xFFFFFFFFu;
+    float qmin = 448.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         q[i] = xv[i] * r;
-        const uint32_t mag = __float_as_uint(q[i]) & 0x7FFFFFFFu;
-        const uint32_t d = (mag & 0xFFFFFu) - 0x80000u + 4u;   // in [0, 8] near a midpoint
-        exact &= (mag >= 0x3C800000u) & (d > 8u);
+        dmin = min(dmin, (__float_as_uint(q[i]) << 12) + 0x80004000u);
+        qmin = fminf(qmin, fabsf(q[i]));
     }
+    const bool exact = r_ok & (dmin > 0x8000u) & (qmin >= 0x1p-6f);
     if (!exact) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) q[i] = xv[i] / s;   // correctly rounded fp32 division
     }
-    uint32_t lo = cvt2_e4m3<false>(q[0], q[1], 0u);
+    // the low-half conversions keep whatever is in the upper half (the
+    // high-half ones overwrite it), so they start from a value already in
+    // a register rather than a zero of their own
+    uint32_t lo = cvt2_e4m3<false>(q[0], q[1], __float_as_uint(q[0]));
     lo = cvt2_e4m3<true>(q[2], q[3], lo);
-    uint32_t hi = cvt2_e4m3<false>(q[4], q[5], 0u);
+    uint32_t hi = cvt2_e4m3<false>(q[4], q[5], __float_as_uint(q[4]));
     hi = cvt2_e4m3<true>(q[6], q[7], hi);
     return make_uint2(lo, hi);
 }

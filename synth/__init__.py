@@ -18,6 +18,9 @@ fused gate_up):
   decode   M in {1,4,8,16,64}, N=2048, K=7168, e4m3 W (wqkv's [2048, 7168]
            with its [64, 224] scale grid), no bias
   prefill  M=4096, N=7168, K=8192, e4m3 W, 1% of A's columns scaled x20
+  prefill_shard  the prefill layer's share on one of eight GPUs when its
+           output columns are split: M=4096, N=896, K=8192 (28 scale-block
+           rows), the same laws and its own draws
   ffn_up   M=2048, N=4096, K=1024, e4m3 W, bias + tanh-GELU (second variant
            bias only)
   gate_up  M in {1,16,512,4096}, N=34816, K=5120, MXFP4 W (e2m1 + 1x32 E8M0)
@@ -72,6 +75,8 @@ WORKLOADS = {
     "tiny": Workload("tiny", 16, 256, 256, "fp8", EPI_BIAS),
     "decode": Workload("decode", 8, 2048, 7168, "fp8", EPI_NONE, m_sweep=(1, 4, 8, 16, 64)),
     "prefill": Workload("prefill", 4096, 7168, 8192, "fp8", EPI_NONE, outlier_frac=0.01),
+    "prefill_shard": Workload("prefill_shard", 4096, 896, 8192, "fp8", EPI_NONE,
+                              outlier_frac=0.01),
     "ffn_up": Workload("ffn_up", 2048, 4096, 1024, "fp8", EPI_BIAS_GELU_TANH),
     "ffn_up_bias": Workload("ffn_up_bias", 2048, 4096, 1024, "fp8", EPI_BIAS),
     "gate_up": Workload("gate_up", 16, 34816, 5120, "mxfp4", EPI_NONE, m_sweep=(1, 16, 512, 4096)),

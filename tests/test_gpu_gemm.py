@@ -246,7 +246,8 @@ def _sample_positions(M, N, count, seed):
 
 @pytest.mark.parametrize("name,M", [("tiny", None), ("decode", 1), ("decode", 4), ("decode", 8),
                                     ("decode", 16), ("decode", 64), ("ffn_up", None),
-                                    ("ffn_up_bias", None), ("prefill", None), ("gate_up", 1),
+                                    ("ffn_up_bias", None), ("prefill", None),
+                                    ("prefill_shard", None), ("gate_up", 1),
                                     ("gate_up", 16), ("gate_up", 512), ("gate_up", 4096)])
 def test_workload_full_size_sampled(name, M):
     d = synth.make(name, M)
