@@ -443,52 +443,49 @@ __global__ __launch_bounds__(256) void quant_static_kernel(const uint16_t *__res
 // MXFP4 quantization (OCP MX): per 32-element block, the E8M0 byte of
 // floor(log2 amax) - 2 (the exponent field of the bf16 amax minus 2, clamped
 // at 0; a zero block gets 0), and each element's e2m1 code of x / 2^(byte -
-// 127), nearest with ties to the even code, saturating at 6, sign kept. The
-// division by a power of two is an exact scaling (a product that would be
-// subnormal is far below the first rounding threshold, 0.25).
-__device__ __forceinline__ uint32_t e2m1_mag(float a) {
-    return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-           (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-           (uint32_t)(a > 5.0f);
+// 127), nearest with ties to the even code, saturating at 6, sign kept.
+//
+// Each lane takes one 16-byte chunk (8 values), so a wave's load reads 1 KiB
+// of consecutive bytes and its store writes 256; a block's 4 chunks sit in
+// a quad of lanes, whose maxima meet through two DPP quad permutations. The
+// codes come from gfx950's scaled bf16-pair to fp4 conversion with the
+// scale 2^(byte - 127), one instruction per pair of values: on MI355X it
+// divides by the scale, rounds to nearest even and saturates, and it gave
+// the same code as the threshold rule above for every finite bf16 value at
+// every scale byte this kernel can produce (0..252), subnormal scale
+// (byte 0) and signed zeros included.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+    // quad_perm [1,0,3,2] then [2,3,0,1]
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));
+    return v;
 }
 
 __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t *__restrict__ x,
                                                           int64_t ldx, uint8_t *__restrict__ q,
                                                           int64_t ldq, uint8_t *__restrict__ sc,
                                                           int64_t M, int K) {
-    const int KB = K >> 5;
-    const int64_t total = M * KB;
+    const int CPR = K >> 3;                          // 16-byte chunks per row (a multiple of 4)
+    const int64_t total = M * CPR;
+    // the stride is a multiple of 4 and so is total: a quad is in or out as a whole
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * 256) {
-        const int64_t m = idx / KB;
-        const int b = (int)(idx - m * KB);
-        const uint16_t *xb = x + m * ldx + 32 * b;
-        uint4 c[4];
-        uint32_t amax = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            c[j] = ldg16(xb + 8 * j);
-            amax = max(amax, absmax8(c[j]));
-        }
-        const uint32_t e = amax >> 7;                       // bf16 exponent field of amax
+        const int64_t m = idx / CPR;
+        const int c = (int)(idx - m * CPR);
+        const uint4 v = ldg16(x + m * ldx + 8 * c);
+        const uint32_t amax = quad_max(absmax8(v));
+        const uint32_t e = amax >> 7;                // bf16 exponent field of amax
         const uint32_t byte = e >= 2 ? e - 2 : 0;
-        const float inv = __uint_as_float((254u - byte) << 23);   // 2^(127 - byte)
-        uint32_t out[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t w[4] = {c[j].x, c[j].y, c[j].z, c[j].w};
-            uint32_t word = 0;
-#pragma unroll
-            for (int h = 0; h < 8; ++h) {
-                const uint32_t bits = (w[h >> 1] >> (16 * (h & 1))) & 0xFFFFu;
-                const float v = bf16_to_f32(bits & 0x7FFFu) * inv;
-                const uint32_t code = e2m1_mag(v) | ((bits >> 12) & 8u);
-                word |= code << (4 * h);
-            }
-            out[j] = word;
-        }
-        *reinterpret_cast<uint4 *>(q + m * ldq + 16 * b) = make_uint4(out[0], out[1], out[2], out[3]);
-        sc[m * KB + b] = (uint8_t)byte;
+        const float scl = __uint_as_float(byte ? byte << 23 : 0x00400000u);   // 2^(byte - 127)
+        uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+            v.x, __builtin_bit_cast(bf16x2_t, v.x), scl, 0);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2_t, v.y), scl, 1);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2_t, v.z), scl, 2);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2_t, v.w), scl, 3);
+        *reinterpret_cast<uint32_t *>(q + m * ldq + 4 * c) = word;
+        if ((c & 3) == 0) sc[m * (CPR >> 2) + (c >> 2)] = (uint8_t)byte;
     }
 }
 
@@ -540,8 +537,8 @@ hipError_t launch_add_rms_quant(const uint16_t *x, int64_t ld_x, uint16_t *resid
 
 hipError_t launch_quant_mxfp4_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_t ld_q,
                                    uint8_t *scale, int64_t M, int64_t K, hipStream_t stream) {
-    const int64_t blocks32 = M * (K / 32);
-    const int64_t grid = (blocks32 + 255) / 256;
+    const int64_t chunks = M * (K / 8);
+    const int64_t grid = (chunks + 255) / 256;
     hipLaunchKernelGGL(quant_mxfp4_kernel, dim3((unsigned)(grid < 8192 ? grid : 8192)), dim3(256),
                        0, stream, x, ld_x, q, ld_q, scale, M, (int)K);
     return hipGetLastError();
