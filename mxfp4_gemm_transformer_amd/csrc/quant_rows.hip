@@ -382,12 +382,15 @@ hipError_t launch_quant_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_
     const int nch = k / 8;
     // Few rows: spread each row over a whole block (up to 1024 threads) to
     // cut the per-row latency, which is all a decode-sized call costs. Many
-    // rows: one or two 16-byte chunks per thread, up to 512 threads a row
-    // (a sweep on MI355X with inputs read from HBM: 4096 x 8192 in 28.8 us
-    // against 35.0 us with 128 threads of 8 chunks, 4096 x 2048 in 9.9
-    // against 10.9 us).
+    // rows (a sweep on MI355X with inputs read from HBM): from 2048 rows, 256
+    // threads a row with up to 4 chunks each past 4096 values, else 128
+    // (4096 x 8192 in 26.3 us against 27.2 with 512 threads of 2 chunks,
+    // 4096 x 5120 in 18.3 against 19.9); from 512 rows, one or two chunks
+    // per thread, up to 512 threads a row (512 x 8192 in 6.2 us).
     int tpr = M <= 64 ? 1024 : 256;
-    if (M >= 512) {
+    if (M >= 2048) {
+        tpr = nch > 512 ? 256 : 128;
+    } else if (M >= 512) {
         tpr = 64;
         while (tpr < nch && tpr < 512) tpr <<= 1;
     }
