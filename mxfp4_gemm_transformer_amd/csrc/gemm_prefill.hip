@@ -858,6 +858,10 @@ constexpr TileShape SHAPES[] = {
     {256, 256, 1.0, 930.0, 1},
     {256, 128, 0.73, 465.0, 1},
     {128, 128, 0.415, 236.0, 2},
+    // 64x64: a round of 256 at K = 5120 (the 512 x 2048 rest of the MXFP4
+    // gate_up at M = 512) took 24.6 us next to 70.6 us for a round of
+    // 256x256; no credit is given for their co-residence
+    {64, 64, 0.388, 120.0, 1},
 };
 constexpr double LAUNCH_COST = 200.0;   // a second launch, same units
 constexpr double PAIR = 1.06;
@@ -870,9 +874,12 @@ double shape_cost(const TileShape &t, int64_t M, int64_t N, int64_t K, int num_c
     return (double)per_cu * (t.c * (double)K + t.e);
 }
 
-int best_shape(bool fp4, int64_t M, int64_t N, int64_t K, int num_cus, double *cost) {
+// nshapes: how many of SHAPES the kernel variant in use offers (64x64 tiles
+// need whole 16-byte loads per thread per stage: e4m3 weights, or MXFP4
+// weights in two-step stages)
+int best_shape(int64_t M, int64_t N, int64_t K, int num_cus, int nshapes, double *cost) {
     int best = -1;
-    for (int i = 0; i < (int)(sizeof(SHAPES) / sizeof(SHAPES[0])); ++i) {
+    for (int i = 0; i < nshapes; ++i) {
         const double c = shape_cost(SHAPES[i], M, N, K, num_cus);
         if (best < 0 || c < *cost) { best = i; *cost = c; }
     }
@@ -894,7 +901,8 @@ hipError_t launch_shape(int shape, bool fp4, const uint8_t *a, int64_t lda, cons
             switch (shape) {
             case 0: return launch_tile_dma<true, 256, 256, 2, 4, 2, true, 2, SLAB_KB_W4A4>(BSG_ARGS, a_e8m0);
             case 1: return launch_tile_dma<true, 256, 128, 2, 2, 2, true, 2, SLAB_KB_W4A4>(BSG_ARGS, a_e8m0);
-            default: return launch_tile_dma<true, 128, 128, 2, 2, 2, true, 2, SLAB_KB_W4A4>(BSG_ARGS, a_e8m0);
+            case 2: return launch_tile_dma<true, 128, 128, 2, 2, 2, true, 2, SLAB_KB_W4A4>(BSG_ARGS, a_e8m0);
+            default: return launch_tile_dma<true, 64, 64, 2, 2, 2, true, 2, SLAB_KB_W4A4>(BSG_ARGS, a_e8m0);
             }
         }
         switch (shape) {
@@ -907,7 +915,8 @@ hipError_t launch_shape(int shape, bool fp4, const uint8_t *a, int64_t lda, cons
         switch (shape) {
         case 0: return launch_tile_dma<true, 256, 256, 2, 4, 2, false, 2, SLAB_KB_W4A8>(BSG_ARGS);
         case 1: return launch_tile_dma<true, 256, 128, 2, 2, 2, false, 2, SLAB_KB_W4A8>(BSG_ARGS);
-        default: return launch_tile_dma<true, 128, 128, 2, 2, 2, false, 2, SLAB_KB_W4A8>(BSG_ARGS);
+        case 2: return launch_tile_dma<true, 128, 128, 2, 2, 2, false, 2, SLAB_KB_W4A8>(BSG_ARGS);
+        default: return launch_tile_dma<true, 64, 64, 2, 2, 2, false, 2, SLAB_KB_W4A8>(BSG_ARGS);
         }
     }
     switch (shape) {
@@ -919,9 +928,12 @@ hipError_t launch_shape(int shape, bool fp4, const uint8_t *a, int64_t lda, cons
     case 1:
         return fp4 ? launch_tile_dma<true, 256, 128, 4>(BSG_ARGS)
                    : launch_tile_dma<false, 256, 128, 4>(BSG_ARGS);
-    default:
+    case 2:
         return fp4 ? launch_tile_dma<true, 128, 128, 4>(BSG_ARGS)
                    : launch_tile_dma<false, 128, 128, 4>(BSG_ARGS);
+    default:   // 64x64: e4m3 weights only here (the planner offers it to MXFP4 only with slabs)
+        return fp4 ? launch_tile_dma<true, 128, 128, 4>(BSG_ARGS)
+                   : launch_tile_dma<false, 64, 64, 4>(BSG_ARGS);
     }
 #undef BSG_ARGS
 }
@@ -935,8 +947,10 @@ hipError_t launch_prefill_dma(bool fp4, const uint8_t *a, int64_t lda, const flo
                               const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
                               int64_t N, int64_t K, int num_cus, hipStream_t st,
                               const uint8_t *a_e8m0 = nullptr) {
+    const bool slab = fp4 && K % 128 == 0 && K / 32 <= (a_e8m0 ? SLAB_KB_W4A4 : SLAB_KB_W4A8);
+    const int nshapes = (int)(sizeof(SHAPES) / sizeof(SHAPES[0])) - (fp4 && !slab ? 1 : 0);
     double one_cost = 0.0;
-    const int one = best_shape(fp4, M, N, K, num_cus, &one_cost);
+    const int one = best_shape(M, N, K, num_cus, nshapes, &one_cost);
     const int64_t mt = (M + 255) / 256, t256 = mt * ((N + 255) / 256);
     const int64_t rounds = t256 / num_cus;
     const int64_t nt1 = rounds > 0 ? rounds * num_cus / mt : 0;
@@ -944,7 +958,7 @@ hipError_t launch_prefill_dma(bool fp4, const uint8_t *a, int64_t lda, const flo
     if (n1 > 0 && n1 < N) {
         const double c1 = shape_cost(SHAPES[0], M, n1, K, num_cus);
         double c2 = 0.0;
-        const int two = best_shape(fp4, M, N - n1, K, num_cus, &c2);
+        const int two = best_shape(M, N - n1, K, num_cus, nshapes, &c2);
         if (c1 + c2 + LAUNCH_COST < one_cost) {
             hipError_t e = launch_shape(0, fp4, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy,
                                         M, n1, K, st, a_e8m0);

@@ -103,7 +103,7 @@ def test_prefill_dma_large_tiles(fmt, M, N, K):
     # the launch plans past one round of small tiles, ragged in M and N: one
     # launch of 256x128 tiles, one of 256x256 (K % 128 == 0 and == 64), and
     # two launches over column ranges (256x256 tiles in one whole round, then
-    # 128x128 tiles, two to a CU, over the rest); y is a view into a larger
+    # 64x64 tiles over the 96-column rest); y is a view into a larger
     # NaN-filled buffer
     for epi in (synth.EPI_NONE, synth.EPI_BIAS_GELU_TANH):
         a, s, w, ws, b = _random_problem(fmt, M, N, K, seed=M + N + epi)
