@@ -453,10 +453,10 @@ __global__ __launch_bounds__(256) void quant_static_kernel(const uint16_t *__res
 // a quad of lanes, whose maxima meet through two DPP quad permutations. The
 // codes come from gfx950's scaled bf16-pair to fp4 conversion with the
 // scale 2^(byte - 127), one instruction per pair of values: on MI355X it
-// divides by the scale, rounds to nearest even and saturates, and it gave
-// the same code as the threshold rule above for every finite bf16 value at
-// every scale byte this kernel can produce (0..252), subnormal scale
-// (byte 0) and signed zeros included.
+// divides by the scale, rounds to nearest even and saturates: it gave the
+// same code as the rule above for every finite bf16 value at every scale
+// byte this kernel can produce (0..252), subnormal scale (byte 0) and
+// signed zeros included.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
