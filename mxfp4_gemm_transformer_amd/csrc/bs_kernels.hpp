@@ -56,7 +56,7 @@ hipError_t launch_gemm_decode_w4a4(const uint8_t *a, int64_t lda, const uint8_t 
                                    const uint8_t *w, int64_t ldw, const uint8_t *ws,
                                    const uint16_t *bias, int epi, uint16_t *y, int64_t ldy,
                                    int64_t M, int64_t N, int64_t K, void *workspace,
-                                   hipStream_t stream);
+                                   int num_cus, hipStream_t stream);
 size_t decode_workspace_bytes_w4a4(int64_t M, int64_t N, int64_t K);
 
 // Grouped (MoE) GEMM over expert-sorted rows: offsets [E + 1] on the device,

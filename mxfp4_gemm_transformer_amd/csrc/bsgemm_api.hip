@@ -242,7 +242,7 @@ int gemm_mxfp4_w4a4(const void *a_fp4x2, int64_t ld_a, const uint8_t *a_scale, c
     hipError_t e;
     if (M <= bsg::DECODE_MAX_M)
         e = bsg::launch_gemm_decode_w4a4(a, ld_a, a_scale, w, ld_w, w_scale, bias, epilogue, y,
-                                         ld_y, M, N, K, workspace, s);
+                                         ld_y, M, N, K, workspace, num_cus, s);
     else
         e = bsg::launch_gemm_prefill_w4a4(a, ld_a, a_scale, w, ld_w, w_scale, bias, epilogue, y,
                                           ld_y, M, N, K, num_cus, s);

@@ -240,10 +240,15 @@ void launch_spw(int per_wave, const uint8_t *a, int64_t lda, const float *as, co
 // Needs K % 128 == 0 (scale rows in whole 4-byte words).
 constexpr int UNIT_WAVES = 16;
 
-template <bool FP4, int MT>
+template <bool FP4, int MT, bool FP4A = false>
 struct UnitsLds {
     static constexpr int TOK = 8 * MT;
-    __host__ __device__ static size_t a_bytes(int K) { return (size_t)TOK * (K + 16); }
+    // a padded activation row per token (fp4 activations: K / 2 bytes, then
+    // each token's K / 32 E8M0 bytes after the rows)
+    __host__ __device__ static int a_row(int K) { return (FP4A ? K / 2 : K) + 16; }
+    __host__ __device__ static size_t a_bytes(int K) {
+        return (size_t)TOK * a_row(K) + (FP4A ? (size_t)TOK * (K / 32) : 0);
+    }
     // scale rows of the workgroup: one per weight row (fp4) or per 32 rows
     __host__ __device__ static int scale_rows(int gpw) { return FP4 ? 8 * gpw : (8 * gpw + 31) / 32 + 1; }
     // then the sums: one slot per group (groups a wave covers whole) and
@@ -257,18 +262,22 @@ struct UnitsLds {
     }
 };
 
-template <bool FP4, int MT, int P>
+// FP4A (W4A4): fp4 activations [M, K/2] with E8M0 scales AS [M, K/32] (rows
+// of whole 4-byte words), staged in LDS after the activation rows; no
+// per-token scale (a_scale is unused, 1).
+template <bool FP4, int MT, int P, bool FP4A = false>
 __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
     const uint8_t *__restrict__ A, int64_t lda, const float *__restrict__ a_scale,
     const uint8_t *__restrict__ W, int64_t ldw, const uint8_t *__restrict__ WS,
     const float *__restrict__ colscale, const uint16_t *__restrict__ bias, int epi,
-    uint16_t *__restrict__ Y, int64_t ldy, int M, int N, int K, int gpw) {
-    using L = UnitsLds<FP4, MT>;
+    uint16_t *__restrict__ Y, int64_t ldy, int M, int N, int K, int gpw,
+    const uint8_t *__restrict__ AS = nullptr) {
+    using L = UnitsLds<FP4, MT, FP4A>;
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int KSTEP = 256;
     constexpr int TOK = L::TOK;
     constexpr int PE = 64 * MT;                     // partial sums per group (tokens x rows)
-    const int lds_row = K + 16;
+    const int lds_row = L::a_row(K);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15, g = lane >> 4;
@@ -285,6 +294,7 @@ __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
     const int srow0 = FP4 ? row0 : (row0 >> 5);
     const int nsrows = FP4 ? ng * 8 : ((row0 + ng * 8 - 1) >> 5) - srow0 + 1;
     uint8_t *s_lds = lds + L::a_bytes(K);
+    uint8_t *as_lds = lds + (size_t)TOK * lds_row;   // FP4A: [TOK][KB] activation scales
     float *gsum = reinterpret_cast<float *>(s_lds + (size_t)L::scale_rows(gpw) * KB);
     float *part = gsum + gpw * PE;
     float *tok_scale = part + UNIT_WAVES * 2 * PE;   // [TOK]
@@ -301,8 +311,8 @@ __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
     const __amdgpu_buffer_rsrc_t rsS =
         WS ? make_rsrc(WS + (int64_t)srow0 * KB, (int64_t)nsrows * KB) : make_rsrc(WS, 0);
     const __amdgpu_buffer_rsrc_t rsW = make_rsrc(W + (int64_t)row0 * ldw, (int64_t)ng * 8 * ldw);
-    constexpr int ACH = 8 * MT * 8192 / 16 / 1024;   // 16-byte chunks per thread for K <= 8192
-    const int kc = K >> 4, chunks = TOK * kc;
+    constexpr int ACH = 8 * MT * (FP4A ? 4096 : 8192) / 16 / 1024;   // 16-byte chunks per thread for K <= 8192
+    const int kc = (FP4A ? K >> 1 : K) >> 4, chunks = TOK * kc;
     uint4 av[ACH];
 #pragma unroll
     for (int j = 0; j < ACH; ++j) {
@@ -315,7 +325,7 @@ __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
     // (range-checked buffer loads: branch-free, so the compiler counts them)
     float ep_val, ep_cs;
     {
-        const __amdgpu_buffer_rsrc_t rsT = make_rsrc(a_scale, (int64_t)M * 4);
+        const __amdgpu_buffer_rsrc_t rsT = make_rsrc(a_scale, FP4A ? 0 : (int64_t)M * 4);
         const __amdgpu_buffer_rsrc_t rsC =
             colscale ? make_rsrc(colscale + row0, (int64_t)(N - row0) * 4) : make_rsrc(colscale, 0);
         // bias of this workgroup's rows (no bias: an empty range, nothing read)
@@ -326,13 +336,23 @@ __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
             rsT, t < TOK ? (uint32_t)(4 * t) : OOB_OFF, 0, 0);
         const uint32_t bb = __builtin_amdgcn_raw_buffer_load_b16(
             rsB, ((t >= TOK) & (t < TOK + 8 * ng)) ? (uint32_t)(2 * (t - TOK)) : OOB_OFF, 0, 0);
-        ep_val = t < TOK ? __uint_as_float(ts) : bf16_to_f32(bb);
+        ep_val = t < TOK ? (FP4A ? 1.0f : __uint_as_float(ts)) : bf16_to_f32(bb);
         const uint32_t cw = __builtin_amdgcn_raw_buffer_load_b32(
             rsC, t < 8 * ng ? (uint32_t)(4 * t) : OOB_OFF, 0, 0);
         ep_cs = colscale ? __uint_as_float(cw) : 1.0f;
     }
     const int words = nsrows * (KB >> 2);
     constexpr int SCW = 8;                           // scale words per thread (the launcher checks the bound)
+    // FP4A: the activation scale rows, one 4-byte word per thread at most
+    // (TOK * K / 128 <= 1024 words for K <= 8192)
+    uint32_t asv = 0;
+    const int awords = TOK * (KB >> 2);
+    if (FP4A) {
+        const __amdgpu_buffer_rsrc_t rsAS = make_rsrc(AS, (int64_t)M * KB);
+        const int c = threadIdx.x, t = c / (KB >> 2);
+        asv = __builtin_amdgcn_raw_buffer_load_b32(
+            rsAS, ((c < awords) & (t < M)) ? (uint32_t)(4 * c) : OOB_OFF, 0, 0);
+    }
     uint32_t sv[SCW];
 #pragma unroll
     for (int j = 0; j < SCW; ++j) {
@@ -379,6 +399,7 @@ __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
         const int c = threadIdx.x + j * 1024;
         if (c < words) *reinterpret_cast<uint32_t *>(s_lds + 4 * c) = sv[j];
     }
+    if (FP4A && (int)threadIdx.x < awords) *reinterpret_cast<uint32_t *>(as_lds + 4 * threadIdx.x) = asv;
     if (threadIdx.x < TOK + 8 * ng) tok_scale[threadIdx.x] = ep_val;   // row_bias follows tok_scale
     if (threadIdx.x < 8 * ng) row_cs[threadIdx.x] = ep_cs;
     __syncthreads();
@@ -425,9 +446,18 @@ __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
             for (int mt = 0; mt < MT; ++mt) {
                 const uint8_t *arow = lds + (mt * 8 + col) * lds_row;
                 uint4 alo = make_uint4(0u, 0u, 0u, 0u), ahi = alo;
-                if (klo < K) alo = *reinterpret_cast<const uint4 *>(arow + klo);
-                if (khi < K) ahi = *reinterpret_cast<const uint4 *>(arow + khi);
-                acc[mt] = mfma16<FP4>(pack8(alo, ahi), wv, acc[mt], E8M0_ONE, sc);
+                if (FP4A) {   // 32 fp4 values at kblk and their scale byte
+                    int sa = E8M0_ONE;
+                    if (kblk < K) {
+                        alo = *reinterpret_cast<const uint4 *>(arow + (kblk >> 1));
+                        sa = as_lds[(mt * 8 + col) * KB + (kblk >> 5)];
+                    }
+                    acc[mt] = mfma16x<FP4, true>(pack8(alo, ahi), wv, acc[mt], sa, sc);
+                } else {
+                    if (klo < K) alo = *reinterpret_cast<const uint4 *>(arow + klo);
+                    if (khi < K) ahi = *reinterpret_cast<const uint4 *>(arow + khi);
+                    acc[mt] = mfma16<FP4>(pack8(alo, ahi), wv, acc[mt], E8M0_ONE, sc);
+                }
             }
             if (++cst == S) { cst = 0; ++cgl; }
         }
@@ -460,15 +490,16 @@ __global__ __launch_bounds__(1024) void gemm_decode_units_kernel(
     }
 }
 
-template <bool FP4, int MT, int P>
+template <bool FP4, int MT, int P, bool FP4A = false>
 void launch_units(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w, int64_t ldw,
                   const uint8_t *ws, const float *cs, const uint16_t *bias, int epi, uint16_t *y,
-                  int64_t ldy, int64_t M, int64_t N, int64_t K, int gpw, hipStream_t st) {
-    const size_t lds = UnitsLds<FP4, MT>::bytes((int)K, gpw);
+                  int64_t ldy, int64_t M, int64_t N, int64_t K, int gpw, hipStream_t st,
+                  const uint8_t *a_e8m0 = nullptr) {
+    const size_t lds = UnitsLds<FP4, MT, FP4A>::bytes((int)K, gpw);
     const int64_t groups = N / 8;
-    hipLaunchKernelGGL((gemm_decode_units_kernel<FP4, MT, P>),
+    hipLaunchKernelGGL((gemm_decode_units_kernel<FP4, MT, P, FP4A>),
                        dim3((unsigned)((groups + gpw - 1) / gpw)), dim3(1024), lds, st, a, lda, as,
-                       w, ldw, ws, cs, bias, epi, y, ldy, (int)M, (int)N, (int)K, gpw);
+                       w, ldw, ws, cs, bias, epi, y, ldy, (int)M, (int)N, (int)K, gpw, a_e8m0);
 }
 
 
@@ -840,13 +871,36 @@ __global__ __launch_bounds__(512) void gemm_grouped_decode_kernel(
     }
 }
 
-// W4A4 decode: the split-K kernel for every M <= DECODE_MAX_M (fp4
-// activations staged with their scales); no per-token scale.
+// W4A4 decode (fp4 activations staged with their scales; no per-token
+// scale): on wide layers with M <= 16 the balanced units kernel, under the
+// same conditions as for W4A8 (and 4-byte aligned activation scale rows);
+// otherwise the split-K kernel, for every M <= DECODE_MAX_M.
 hipError_t launch_gemm_decode_w4a4(const uint8_t *a, int64_t lda, const uint8_t *a_e8m0,
                                    const uint8_t *w, int64_t ldw, const uint8_t *ws,
                                    const uint16_t *bias, int epi, uint16_t *y, int64_t ldy,
                                    int64_t M, int64_t N, int64_t K, void *workspace,
-                                   hipStream_t st) {
+                                   int num_cus, hipStream_t st) {
+    const int64_t groups = N / 8;
+    const int gpw = (int)((groups + num_cus - 1) / num_cus);
+    if (M <= 16 && gpw >= 2 && K % 128 == 0 && K <= 8192 &&
+        (reinterpret_cast<uintptr_t>(ws) & 3u) == 0 && (reinterpret_cast<uintptr_t>(a_e8m0) & 3u) == 0) {
+        const int64_t S = (K + 255) / 256;
+        const int64_t upw = (gpw * S + UNIT_WAVES - 1) / UNIT_WAVES;
+        const int mt = M <= 8 ? 1 : 2;
+        const size_t lds = mt == 1 ? UnitsLds<true, 1, true>::bytes((int)K, gpw)
+                                   : UnitsLds<true, 2, true>::bytes((int)K, gpw);
+        const int64_t scale_words = 8 * gpw * (K / 128);
+        if (upw <= 32 && lds <= 160 * 1024 && scale_words <= 8 * 1024) {
+#define BSG_UNITS4(MT_)                                                                            \
+    if (upw <= 8) launch_units<true, MT_, 8, true>(a, lda, nullptr, w, ldw, ws, nullptr, bias, epi, y, ldy, M, N, K, gpw, st, a_e8m0); \
+    else if (upw <= 16) launch_units<true, MT_, 16, true>(a, lda, nullptr, w, ldw, ws, nullptr, bias, epi, y, ldy, M, N, K, gpw, st, a_e8m0); \
+    else if (upw <= 24) launch_units<true, MT_, 24, true>(a, lda, nullptr, w, ldw, ws, nullptr, bias, epi, y, ldy, M, N, K, gpw, st, a_e8m0); \
+    else launch_units<true, MT_, 32, true>(a, lda, nullptr, w, ldw, ws, nullptr, bias, epi, y, ldy, M, N, K, gpw, st, a_e8m0);
+            if (mt == 1) { BSG_UNITS4(1) } else { BSG_UNITS4(2) }
+#undef BSG_UNITS4
+            return hipGetLastError();
+        }
+    }
     float *part = static_cast<float *>(workspace);
     switch ((M + 15) / 16) {
     case 1: return launch_splitk<true, 1, true>(a, lda, nullptr, w, ldw, ws, nullptr, bias, epi, y, ldy, M, N, K, part, st, a_e8m0);

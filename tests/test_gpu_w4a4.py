@@ -96,6 +96,20 @@ def test_w4a4_shapes(M, N, K, epi):
     assert_within(got, ref, absum, "w4a4 M=%d N=%d K=%d epi=%d" % (M, N, K, epi))
 
 
+# wide layers with M <= 16 (at least two 8-row groups per CU): the balanced
+# decode kernel with fp4 activations and their scale rows staged in LDS;
+# ragged M, one to 32 K steps, the epilogues
+@pytest.mark.parametrize("M,N,K,epi", [
+    (1, 4096, 1024, synth.EPI_NONE), (5, 4160, 5120, synth.EPI_BIAS_GELU_TANH),
+    (9, 8192, 8192, synth.EPI_NONE), (13, 4096, 2048, synth.EPI_BIAS),
+    (16, 6144, 5120, synth.EPI_BIAS_GELU_TANH), (16, 4096, 128, synth.EPI_NONE)])
+def test_w4a4_wide_decode(M, N, K, epi):
+    a, sa, w, sw, b = _problem(M, N, K, seed=7 * M + N + K + epi)
+    got = _run(a, sa, w, sw, b, epi)
+    ref, absum = oracle.gemm_mxfp4_w4a4(a, sa, w, sw, b if epi else None, epi)
+    assert_within(got, ref, absum, "w4a4 wide decode M=%d N=%d K=%d epi=%d" % (M, N, K, epi))
+
+
 @pytest.mark.parametrize("M", [8, 100])
 def test_w4a4_padded_bias(M):
     a, sa, w, sw, b = _problem(M, 256, 512, seed=90 + M)
