@@ -56,6 +56,15 @@ def test_decode_wide_rows(fmt, M, K):
     _full_check(fmt, M, N, K, epi, seed=M + K)
 
 
+# e4m3 layers of at least 2^27 weights with 2 <= M <= 16 (split-K over many
+# column blocks); (32832, 4352) has a half K step at each row's end and a
+# half-full last column block
+@pytest.mark.parametrize("M,N,K,epi", [(3, 65536, 2304, synth.EPI_NONE),
+                                       (12, 32768 + 64, 4352, synth.EPI_BIAS_GELU_TANH)])
+def test_decode_wide_rows_windowed(M, N, K, epi):
+    _full_check("fp8", M, N, K, epi, seed=M + K)
+
+
 # split-K (8 < M <= 64, narrow layers): K cut into S slices of whole 128-k
 # steps; (2048, 1152) leaves the last three slices empty, (2080, 1184) adds
 # a half-full last column block and a 32-wide K tail

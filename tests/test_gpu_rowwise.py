@@ -82,7 +82,7 @@ def test_rowwise_uniform_power_of_two_scales_equal_block_scaled(M, N, K):
     assert torch.equal(y_rw.view(torch.int16), y_bs.view(torch.int16))
 
 
-@pytest.mark.parametrize("M", [1, 8, 16])
+@pytest.mark.parametrize("M", [1, 4, 8, 16])
 def test_lm_head_full_size_sampled(M):
     d = synth.make("lm_head", M)
     wl = d["wl"]
