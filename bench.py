@@ -223,11 +223,14 @@ def main():
     alg = algorithmic(wl, M)
     step_bytes = alg["quant_bytes"] + alg["gemm_bytes"]
     ms_per_step = step_s / steps * 1e3
-    compute_bound = alg["gemm_flops"] / alg["gemm_bytes"] > 1000.0
+    # the binding roof: the longer of the GEMM's FLOPs at the format's MFMA
+    # peak and its bytes at the HBM peak (ridge 625 flop/B for e4m3, 1262 for
+    # MXFP4)
+    peak = FP4_PEAK_TFLOPS if wl.fmt in ("mxfp4", "mxfp4_w4a4") else FP8_PEAK_TFLOPS
+    compute_bound = alg["gemm_flops"] / (peak * 1e12) >= alg["gemm_bytes"] / (HBM_PEAK_GBS * 1e9)
     if compute_bound:
         unit = "TFLOP/s"
         value = alg["gemm_flops"] * steps / step_s / 1e12
-        peak = FP4_PEAK_TFLOPS if wl.fmt in ("mxfp4", "mxfp4_w4a4") else FP8_PEAK_TFLOPS
         achieved = alg["gemm_flops"] / gemm_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
