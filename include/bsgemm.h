@@ -206,7 +206,8 @@ int gemm_mxfp4_w4a8(const void *a_e4m3, int64_t ld_a, const float *a_scale,
  *   a_fp4x2 [M, K/2], row stride ld_a bytes; a_scale [M, K/32] E8M0 dense
  *   w_fp4x2 [N, K/2], w_scale [N, K/32] as gemm_mxfp4_w4a8
  *   M > 64 needs K % 64 == 0; workspace: bs_workspace_bytes(3, M, N, K)
- *   (nonzero for every M <= 64: the small-M path always splits K).
+ *   (nonzero for every M <= 64, where the small-M path may split K; wide
+ *   layers with M <= 16 and 4-byte aligned scale rows do not use it).
  *   Other rules as gemm_bs_fp8.
  */
 int fp4_quant_rows(const void *x_bf16, int64_t ld_x, void *q_fp4x2, int64_t ld_q,
