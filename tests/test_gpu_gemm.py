@@ -258,8 +258,8 @@ def _sample_positions(M, N, count, seed):
                                     ("ffn_up_bias", None), ("prefill", None),
                                     ("prefill_shard", None), ("gate_up", 1),
                                     ("gate_up", 16), ("gate_up", 512), ("gate_up", 4096)])
-def test_workload_full_size_sampled(name, M):
-    d = synth.make(name, M)
+def test_workload_full_size_sampled(name, M, seed=0):
+    d = synth.make(name, M, seed=seed)
     wl = d["wl"]
     M = d["M"]
     x = bf16_dev(d["a_bf16"])
@@ -282,3 +282,10 @@ def test_workload_full_size_sampled(name, M):
                                          d["epilogue"], ms, ns)
         assert_within(got[ms, ns], ref, absum, name)
     assert np.isfinite(got).all()
+
+
+# the same checks on a second draw of every tensor (seed 1)
+@pytest.mark.parametrize("name,M", [("decode", 8), ("prefill", None), ("gate_up", 16),
+                                    ("gate_up", 512)])
+def test_workload_full_size_sampled_seed1(name, M):
+    test_workload_full_size_sampled(name, M, seed=1)
