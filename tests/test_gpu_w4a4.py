@@ -135,7 +135,7 @@ def test_w4a4_equals_w4a8_on_values_both_formats_hold():
         assert_within(y_host(y4), ref, absum, "w4a4 vs w4a8 values M=%d" % M)
 
 
-@pytest.mark.parametrize("M", [16, 4096])
+@pytest.mark.parametrize("M", [16, 512, 4096])
 def test_gate_up_w4a4_full_size(M):
     d = synth.make("gate_up", M)
     wl = d["wl"]
