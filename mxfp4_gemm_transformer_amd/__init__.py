@@ -123,6 +123,45 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _on(t: torch.Tensor, name: str, device: torch.device) -> torch.Tensor:
+    """Refuse a tensor that is not on `device` (a host pointer handed to a
+    kernel would fault on the GPU instead of raising here)."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError("%s must be a device tensor on %s, got %s" % (name, device, t.device))
+    return t
+
+
+def _torch_stream(stream):
+    if stream is None:
+        return None
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)))
+
+
+def _alloc(shape, dtype, device, stream, zero=False):
+    """A new tensor owned by the caching allocator on the stream the kernels
+    run on, so that its memory is not handed to other work before they end."""
+    s = _torch_stream(stream)
+    if s is None:
+        return torch.zeros(shape, dtype=dtype, device=device) if zero else \
+            torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(s):
+        return torch.zeros(shape, dtype=dtype, device=device) if zero else \
+            torch.empty(shape, dtype=dtype, device=device)
+
+
+def _workspace(workspace, need: int, device: torch.device, stream):
+    """The split-K workspace: the caller's (a contiguous device tensor on the
+    same device), or a new one of `need` bytes."""
+    if workspace is None:
+        return _alloc((need,), torch.uint8, device, stream) if need else None
+    _on(workspace, "workspace", device)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor")
+    return workspace
+
+
 def fp8_quant_rows(x: torch.Tensor, q: torch.Tensor | None = None,
                    scale: torch.Tensor | None = None, stream=None):
     """Per-token e4m3 quantization of bf16 x [M, K]. Returns (q uint8 [M, K],
@@ -131,14 +170,7 @@ def fp8_quant_rows(x: torch.Tensor, q: torch.Tensor | None = None,
         raise TypeError("x must be bfloat16")
     M, K = x.shape
     ldx = _matrix(x, "x", M, K)
-    if q is None:
-        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-    q = _u8(q, "q")
-    ldq = _matrix(q, "q", M, K)
-    if scale is None:
-        scale = torch.empty((M,), dtype=torch.float32, device=x.device)
-    if scale.dtype != torch.float32 or scale.shape != (M,) or not scale.is_contiguous():
-        raise ValueError("scale must be a contiguous fp32 [M] tensor")
+    q, ldq, scale = _quant_outputs(q, scale, M, K, x.device, stream)
     st = load_library().fp8_quant_rows(_ptr(x), ldx, _ptr(q), ldq, _ptr(scale), M, K,
                                        ctypes.c_void_p(_stream(stream)))
     if st != BS_OK:
@@ -146,15 +178,16 @@ def fp8_quant_rows(x: torch.Tensor, q: torch.Tensor | None = None,
     return q, scale
 
 
-def _quant_outputs(q, scale, M, K, device):
+def _quant_outputs(q, scale, M, K, device, stream):
     if q is None:
-        q = torch.empty((M, K), dtype=torch.uint8, device=device)
-    q = _u8(q, "q")
+        q = _alloc((M, K), torch.uint8, device, stream)
+    q = _on(_u8(q, "q"), "q", device)
     ldq = _matrix(q, "q", M, K)
     if scale is None:
-        scale = torch.empty((M,), dtype=torch.float32, device=device)
+        scale = _alloc((M,), torch.float32, device, stream)
     if scale.dtype != torch.float32 or scale.shape != (M,) or not scale.is_contiguous():
         raise ValueError("scale must be a contiguous fp32 [M] tensor")
+    _on(scale, "scale", device)
     return q, ldq, scale
 
 
@@ -172,10 +205,11 @@ def add_rms_norm_quant_fp8(x: torch.Tensor, residual: torch.Tensor | None, weigh
     if residual is not None:
         if residual.dtype != torch.bfloat16:
             raise TypeError("residual must be bfloat16")
-        ldr = _matrix(residual, "residual", M, K)
+        ldr = _matrix(_on(residual, "residual", x.device), "residual", M, K)
     if weight.shape != (K,) or not weight.is_contiguous():
         raise ValueError("weight must be a contiguous bf16 [K] tensor")
-    q, ldq, scale = _quant_outputs(q, scale, M, K, x.device)
+    _on(weight, "weight", x.device)
+    q, ldq, scale = _quant_outputs(q, scale, M, K, x.device, stream)
     st = load_library().add_rms_norm_quant_fp8(_ptr(x), ldx, _ptr(residual), ldr, _ptr(weight),
                                                float(eps), _ptr(q), ldq, _ptr(scale), M, K,
                                                ctypes.c_void_p(_stream(stream)))
@@ -195,7 +229,7 @@ def silu_mul_quant_fp8(gate_up: torch.Tensor, q: torch.Tensor | None = None,
         raise ValueError("gate_up must have an even number of columns")
     I = I2 // 2
     ldgu = _matrix(gate_up, "gate_up", M, I2)
-    q, ldq, scale = _quant_outputs(q, scale, M, I, gate_up.device)
+    q, ldq, scale = _quant_outputs(q, scale, M, I, gate_up.device, stream)
     st = load_library().silu_mul_quant_fp8(_ptr(gate_up), ldgu, _ptr(q), ldq, _ptr(scale), M, I,
                                            ctypes.c_void_p(_stream(stream)))
     if st != BS_OK:
@@ -237,14 +271,16 @@ def _gemm(fn_name, op, a, a_scale, w, w_scale, bias, epilogue, y, workspace, str
         if bias is None or bias.dtype != torch.bfloat16 or bias.shape != (N,) \
                 or not bias.is_contiguous():
             raise ValueError("this epilogue needs a contiguous bf16 bias [N]")
+        _on(bias, "bias", a.device)
+    _on(w, "w", a.device)
+    _on(a_scale, "a_scale", a.device)
+    _on(w_scale, "w_scale", a.device)
     if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+        y = _alloc((M, N), torch.bfloat16, a.device, stream)
     if y.dtype != torch.bfloat16:
         raise TypeError("y must be bfloat16")
-    ldy = _matrix(y, "y", M, N)
-    need = bs_workspace_bytes(op, M, N, K)
-    if need and workspace is None:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=a.device)
+    ldy = _matrix(_on(y, "y", a.device), "y", M, N)
+    workspace = _workspace(workspace, bs_workspace_bytes(op, M, N, K), a.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     fn = getattr(load_library(), fn_name)
     st = fn(_ptr(a), lda, _ptr(a_scale), _ptr(w), ldw, _ptr(w_scale),
@@ -281,7 +317,8 @@ def fp8_quant_rows_static(x: torch.Tensor, scale: torch.Tensor, q: torch.Tensor 
         raise ValueError("scale must be a one-element fp32 device tensor")
     M, K = x.shape
     ldx = _matrix(x, "x", M, K)
-    q, ldq, scale_out = _quant_outputs(q, scale_out, M, K, x.device)
+    _on(scale, "scale", x.device)
+    q, ldq, scale_out = _quant_outputs(q, scale_out, M, K, x.device, stream)
     st = load_library().fp8_quant_rows_static(_ptr(x), ldx, _ptr(scale), _ptr(q), ldq,
                                               _ptr(scale_out), M, K,
                                               ctypes.c_void_p(_stream(stream)))
@@ -317,9 +354,13 @@ def gemm_mxfp4_w4a8_grouped(a, a_scale, expert_offsets, w, w_scale, bias=None,
         if bias is None or bias.dtype != torch.bfloat16 or tuple(bias.shape) != (E, N) \
                 or not bias.is_contiguous():
             raise ValueError("this epilogue needs a contiguous bf16 bias [E, N]")
+        _on(bias, "bias", a.device)
+    for t, name in ((w, "w"), (a_scale, "a_scale"), (expert_offsets, "expert_offsets"),
+                    (w_scale, "w_scale")):
+        _on(t, name, a.device)
     if y is None:
-        y = torch.zeros((T, N), dtype=torch.bfloat16, device=a.device)
-    ldy = _matrix(y, "y", T, N)
+        y = _alloc((T, N), torch.bfloat16, a.device, stream, zero=True)
+    ldy = _matrix(_on(y, "y", a.device), "y", T, N)
     mr = T if max_rows_per_expert is None else int(max_rows_per_expert)
     st = load_library().gemm_mxfp4_w4a8_grouped(
         _ptr(a), lda, _ptr(a_scale), _ptr(expert_offsets), E, mr, _ptr(w), w.stride(1),
@@ -339,12 +380,13 @@ def fp4_quant_rows(x: torch.Tensor, q: torch.Tensor | None = None,
     M, K = x.shape
     ldx = _matrix(x, "x", M, K)
     if q is None:
-        q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
-    ldq = _matrix(_u8(q, "q"), "q", M, K // 2)
+        q = _alloc((M, K // 2), torch.uint8, x.device, stream)
+    ldq = _matrix(_on(_u8(q, "q"), "q", x.device), "q", M, K // 2)
     if scale is None:
-        scale = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+        scale = _alloc((M, K // 32), torch.uint8, x.device, stream)
     if scale.dtype != torch.uint8 or tuple(scale.shape) != (M, K // 32) or not scale.is_contiguous():
         raise ValueError("scale must be a contiguous uint8 [M, K/32] tensor")
+    _on(scale, "scale", x.device)
     st = load_library().fp4_quant_rows(_ptr(x), ldx, _ptr(q), ldq, _ptr(scale), M, K,
                                        ctypes.c_void_p(_stream(stream)))
     if st != BS_OK:
@@ -367,16 +409,19 @@ def gemm_mxfp4_w4a4(a, a_scale, w, w_scale, bias=None, epilogue=EPI_NONE, y=None
     for t, name, rows in ((a_scale, "a_scale", M), (w_scale, "w_scale", N)):
         if t.dtype != torch.uint8 or tuple(t.shape) != (rows, K // 32) or not t.is_contiguous():
             raise ValueError("%s must be a contiguous uint8 [%d, %d] tensor" % (name, rows, K // 32))
+        _on(t, name, a.device)
+    _on(w, "w", a.device)
     if epilogue != EPI_NONE:
         if bias is None or bias.dtype != torch.bfloat16 or bias.shape != (N,) \
                 or not bias.is_contiguous():
             raise ValueError("this epilogue needs a contiguous bf16 bias [N]")
+        _on(bias, "bias", a.device)
     if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    ldy = _matrix(y, "y", M, N)
-    need = bs_workspace_bytes(3, M, N, K)
-    if need and workspace is None:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=a.device)
+        y = _alloc((M, N), torch.bfloat16, a.device, stream)
+    if y.dtype != torch.bfloat16:
+        raise TypeError("y must be bfloat16")
+    ldy = _matrix(_on(y, "y", a.device), "y", M, N)
+    workspace = _workspace(workspace, bs_workspace_bytes(3, M, N, K), a.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().gemm_mxfp4_w4a4(_ptr(a), lda, _ptr(a_scale), _ptr(w), ldw, _ptr(w_scale),
                                         _ptr(bias if epilogue != EPI_NONE else None),

@@ -1,0 +1,143 @@
+// Microbenchmarks that set the ceilings the layer's kernels are measured
+// against on gfx950. They are not part of the layer: bench.py loads them
+// from libbsbench.so, a library of their own, to time
+//   - a plain streaming read of a buffer (the best an HBM-bound kernel of
+//     that size can do in one launch),
+//   - an empty kernel (the fixed cost of one launch in a graph), and
+//   - back-to-back scaled MFMAs with register operands, per operand-format
+//     pair (the matrix-core rate each GEMM variant can reach).
+// Every entry point launches asynchronously on `stream` and returns a
+// hipError_t value (0 on success).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Reads [p, p + bytes) once, 16 bytes per lane per load, `unroll` loads in
+// flight per lane; each workgroup covers contiguous chunks of
+// 16 * 256 * unroll bytes, grid-strided. The loaded words are folded into an
+// xor that is stored only if it equals a value the data never produces
+// (the buffers hold repeated non-zero bytes), so no load is dead code and
+// nothing is written.
+template <int UNROLL>
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restrict__ p, int64_t n16,
+                                                          uint32_t *__restrict__ sink) {
+    uint32_t acc = 0;
+    const int64_t chunk = 256 * UNROLL;
+    for (int64_t base = (int64_t)blockIdx.x * chunk; base < n16; base += (int64_t)gridDim.x * chunk) {
+        u32x4 v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t i = base + u * 256 + threadIdx.x;
+            v[u] = i < n16 ? __builtin_nontemporal_load(p + i) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    if (acc == 0xDEADBEEFu) sink[blockIdx.x & 255] = acc;
+}
+
+__global__ void empty_kernel() {}
+
+// `iters` rounds of 4 independent scaled MFMAs per wave (4 accumulators
+// hide the instruction's dependent-issue latency); operands stay in
+// registers. Formats per the instruction's cbsz / blgp encoding: 0 = fp8
+// e4m3, 4 = fp4 e2m1.
+template <int FA, int FB, bool BIG>
+__global__ __launch_bounds__(256) void mfma_rate_kernel(int iters, float *__restrict__ sink) {
+    v8i a, b;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        a[r] = (int)(0x38383838u + threadIdx.x + r);
+        b[r] = (int)(0x22222222u + threadIdx.x * 3 + r);
+    }
+    if (BIG) {
+        v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+        for (int it = 0; it < iters; ++it) {
+            c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, FA, FB, 0, 127, 0, 127);
+            c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c1, FA, FB, 0, 127, 0, 127);
+            c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c2, FA, FB, 0, 127, 0, 127);
+            c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c3, FA, FB, 0, 127, 0, 127);
+        }
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+        if (s == 1234.5f) sink[threadIdx.x] = s;
+    } else {
+        v4f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+        for (int it = 0; it < iters; ++it) {
+            c0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c0, FA, FB, 0, 127, 0, 127);
+            c1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c1, FA, FB, 0, 127, 0, 127);
+            c2 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c2, FA, FB, 0, 127, 0, 127);
+            c3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c3, FA, FB, 0, 127, 0, 127);
+        }
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+        if (s == 1234.5f) sink[threadIdx.x] = s;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+// Streaming read of `bytes` (a multiple of 16) at the 16-byte-aligned
+// device address `p` on `blocks` workgroups of 256 threads with `unroll`
+// (1, 2, 4, 8 or 16) loads in flight per lane. `sink` is 1 KiB of device
+// memory that is never written in practice.
+int bsb_stream_read(const void *p, int64_t bytes, void *sink, int blocks, int unroll, void *stream) {
+    if (!p || !sink || bytes <= 0 || bytes % 16 || blocks < 1) return (int)hipErrorInvalidValue;
+    const auto *q = static_cast<const u32x4 *>(p);
+    auto *s = static_cast<uint32_t *>(sink);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t n16 = bytes / 16;
+    switch (unroll) {
+    case 1: hipLaunchKernelGGL(stream_read_kernel<1>, dim3(blocks), dim3(256), 0, st, q, n16, s); break;
+    case 2: hipLaunchKernelGGL(stream_read_kernel<2>, dim3(blocks), dim3(256), 0, st, q, n16, s); break;
+    case 4: hipLaunchKernelGGL(stream_read_kernel<4>, dim3(blocks), dim3(256), 0, st, q, n16, s); break;
+    case 8: hipLaunchKernelGGL(stream_read_kernel<8>, dim3(blocks), dim3(256), 0, st, q, n16, s); break;
+    case 16: hipLaunchKernelGGL(stream_read_kernel<16>, dim3(blocks), dim3(256), 0, st, q, n16, s); break;
+    default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
+// One launch of a kernel with no body, `blocks` workgroups of 64 threads.
+int bsb_empty(int blocks, void *stream) {
+    if (blocks < 1) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(empty_kernel, dim3(blocks), dim3(64), 0, static_cast<hipStream_t>(stream));
+    return (int)hipGetLastError();
+}
+
+// `blocks` workgroups of `waves` (1..4) waves, each wave issuing 4 * iters
+// scaled MFMAs: shape 0 = 16x16x128, 1 = 32x32x64; formats (fa, fb) in
+// {(0,0) fp8 x fp8, (0,4) fp8 x fp4, (4,0) fp4 x fp8, (4,4) fp4 x fp4}.
+// FLOPs = blocks * waves * 4 * iters * (2 * 16 * 16 * 128, or 2 * 32 * 32 * 64).
+// `sink` is 1 KiB of device memory that is never written in practice.
+int bsb_mfma_rate(int shape, int fa, int fb, int iters, int blocks, int waves, void *sink,
+                  void *stream) {
+    if (!sink || iters < 1 || blocks < 1 || waves < 1 || waves > 4) return (int)hipErrorInvalidValue;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float *s = static_cast<float *>(sink);
+    const dim3 grid(blocks), block(64 * waves);
+#define BSB_MFMA(FA, FB)                                                                          \
+    if (fa == FA && fb == FB) {                                                                   \
+        if (shape) hipLaunchKernelGGL((mfma_rate_kernel<FA, FB, true>), grid, block, 0, st, iters, s); \
+        else hipLaunchKernelGGL((mfma_rate_kernel<FA, FB, false>), grid, block, 0, st, iters, s); \
+        return (int)hipGetLastError();                                                            \
+    }
+    BSB_MFMA(0, 0)
+    BSB_MFMA(0, 4)
+    BSB_MFMA(4, 0)
+    BSB_MFMA(4, 4)
+#undef BSB_MFMA
+    return (int)hipErrorInvalidValue;
+}
+
+}  // extern "C"

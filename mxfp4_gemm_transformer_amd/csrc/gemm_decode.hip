@@ -503,6 +503,35 @@ void launch_units(const uint8_t *a, int64_t lda, const float *as, const uint8_t 
 }
 
 
+// The units kernel's instantiation for a wave's unit count: windows of 4, 8
+// and 16 units for both weight formats, 24 and 32 for MXFP4 weights only
+// (their e4m3 window would not fit the register budget; the caller keeps
+// e4m3 at 16 units a wave, and any other count is refused here).
+template <bool FP4, int MT>
+hipError_t launch_units_upw(int64_t upw, const uint8_t *a, int64_t lda, const float *as,
+                            const uint8_t *w, int64_t ldw, const uint8_t *ws, const float *cs,
+                            const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
+                            int64_t N, int64_t K, int gpw, hipStream_t st) {
+    if (upw <= 4) launch_units<FP4, MT, 4>(a, lda, as, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st);
+    else if (upw <= 8) launch_units<FP4, MT, 8>(a, lda, as, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st);
+    else if (upw <= 16) launch_units<FP4, MT, 16>(a, lda, as, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st);
+    else {
+        if constexpr (FP4) {
+            if (upw <= 24) launch_units<FP4, MT, 24>(a, lda, as, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st);
+            else if (upw <= 32) launch_units<FP4, MT, 32>(a, lda, as, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st);
+            else return hipErrorInvalidValue;
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
+    return hipSuccess;
+}
+
+// The units kernel stages its epilogue operands (TOK per-token scales, then
+// the bias and the channel scales of its 8 gpw rows) one entry per thread of
+// its 1024.
+inline bool units_epilogue_fits(int mt, int gpw) { return 8 * mt + 8 * gpw <= 1024; }
+
 // ---------------------------------------------------------------------------
 // Split-K decode for 8 < M <= 64 on narrow layers. With every workgroup on
 // all of K, each one would read all M x K activations (M/8 times the bytes
@@ -745,16 +774,14 @@ hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const flo
         const size_t lds8 = mt == 1 ? UnitsLds<false, 1>::bytes((int)K, gpw)
                                     : UnitsLds<false, 2>::bytes((int)K, gpw);
         const int64_t scale_words = (fp4 ? 8 * gpw : (8 * gpw + 31) / 32 + 1) * (K / 128);
-        if (upw <= (fp4 ? 32 : 16) && (fp4 ? lds : lds8) <= 160 * 1024 && scale_words <= 8 * 1024) {
-#define BSG_UNITS(FP4_, MT_)                                                                       \
-    if (upw <= 4) launch_units<FP4_, MT_, 4>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st); \
-    else if (upw <= 8) launch_units<FP4_, MT_, 8>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st); \
-    else if (upw <= 16) launch_units<FP4_, MT_, 16>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st); \
-    else if (upw <= 24) launch_units<true, MT_, 24>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st); \
-    else launch_units<true, MT_, 32>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st);
-            if (fp4) { if (mt == 1) { BSG_UNITS(true, 1) } else { BSG_UNITS(true, 2) } }
-            else { if (mt == 1) { BSG_UNITS(false, 1) } else { BSG_UNITS(false, 2) } }
-#undef BSG_UNITS
+        if (upw <= (fp4 ? 32 : 16) && (fp4 ? lds : lds8) <= 160 * 1024 && scale_words <= 8 * 1024 &&
+            units_epilogue_fits(mt, gpw)) {
+            const hipError_t e =
+                fp4 ? (mt == 1 ? launch_units_upw<true, 1>(upw, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st)
+                               : launch_units_upw<true, 2>(upw, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st))
+                    : (mt == 1 ? launch_units_upw<false, 1>(upw, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st)
+                               : launch_units_upw<false, 2>(upw, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, gpw, st));
+            if (e != hipSuccess) return e;
             return hipGetLastError();
         }
     }
@@ -890,7 +917,7 @@ hipError_t launch_gemm_decode_w4a4(const uint8_t *a, int64_t lda, const uint8_t 
         const size_t lds = mt == 1 ? UnitsLds<true, 1, true>::bytes((int)K, gpw)
                                    : UnitsLds<true, 2, true>::bytes((int)K, gpw);
         const int64_t scale_words = 8 * gpw * (K / 128);
-        if (upw <= 32 && lds <= 160 * 1024 && scale_words <= 8 * 1024) {
+        if (upw <= 32 && lds <= 160 * 1024 && scale_words <= 8 * 1024 && units_epilogue_fits(mt, gpw)) {
 #define BSG_UNITS4(MT_)                                                                            \
     if (upw <= 8) launch_units<true, MT_, 8, true>(a, lda, nullptr, w, ldw, ws, nullptr, bias, epi, y, ldy, M, N, K, gpw, st, a_e8m0); \
     else if (upw <= 16) launch_units<true, MT_, 16, true>(a, lda, nullptr, w, ldw, ws, nullptr, bias, epi, y, ldy, M, N, K, gpw, st, a_e8m0); \

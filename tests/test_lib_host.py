@@ -245,3 +245,16 @@ def test_valid_call_without_a_gpu_is_refused_by_the_arch_gate():
                CUDA_VISIBLE_DEVICES="-1")
     out = subprocess.check_output([sys.executable, "-c", code], env=env, text=True, timeout=120)
     assert out.split() == [str(bs.BS_EARCH)] * 2
+
+
+def test_binding_refuses_tensors_off_the_device():
+    # every pointer argument must be a device tensor on the operands' device:
+    # a host tensor would reach a kernel as a host address
+    import torch
+    cpu = torch.zeros(4, dtype=torch.float32)
+    with pytest.raises(ValueError, match="a_scale must be a device tensor"):
+        bs._on(cpu, "a_scale", torch.device("cuda:0"))
+    with pytest.raises(ValueError, match="workspace"):
+        bs._workspace(torch.zeros(16, dtype=torch.uint8), 16, torch.device("cuda:0"), None)
+    # no workspace needed and none given: nothing is allocated
+    assert bs._workspace(None, 0, torch.device("cuda:0"), None) is None
