@@ -710,7 +710,7 @@ def bench_ceiling(args):
         nb = (nbytes + 15) // 16 * 16
         copies = max(2, math.ceil(ROTATION_BYTES / nb))
         bufs = [torch.full((nb,), 0x5A, dtype=torch.uint8, device=dev) for _ in range(copies)]
-        best = None
+        best, sweep = None, []
         for blocks_per_cu in (1, 2, 4, 8):
             for unroll in (1, 2, 4, 8, 16):
                 blocks = blocks_per_cu * num_cus
@@ -726,9 +726,11 @@ def bench_ceiling(args):
                 us = G.timed(g, flush=g_flush) / steps * 1e6
                 rec = {"bytes": nb, "blocks": blocks, "unroll": unroll, "us": round(us, 3),
                        "GBps": round(nb / us / 1e3, 1), "frac": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
+                sweep.append([blocks, unroll, round(us, 3)])
                 if best is None or us < best["us"]:
                     best = rec
         best["copies_rotated"] = copies
+        best["sweep_blocks_unroll_us"] = sweep
         out["stream_read"].append(best)
         del bufs
         torch.cuda.empty_cache()

@@ -34,6 +34,9 @@ EXPORTED_SYMBOLS = ("fp8_quant_rows", "fp8_quant_rows_static", "add_rms_norm_qua
                     "fp4_quant_rows", "gemm_mxfp4_w4a4", "gemm_mxfp4_w4a8_grouped", "bs_workspace_bytes", "bs_status_string")
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsgemm.so")
+# BSGEMM_LIB loads another build of the same sources (the host-sanitizer
+# build of _build.build_host_sanitized(), for the CPU tests)
+_LOAD_PATH = os.environ.get("BSGEMM_LIB") or _LIB_PATH
 _lib = None
 
 
@@ -51,10 +54,10 @@ def load_library():
     """Load libbsgemm.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            raise RuntimeError("libbsgemm.so is not built; run __graft_entry__.build() "
-                               "(hipcc --offload-arch=gfx950) first")
-        lib = ctypes.CDLL(_LIB_PATH)
+        if not os.path.exists(_LOAD_PATH):
+            raise RuntimeError("%s is not built; run __graft_entry__.build() "
+                               "(hipcc --offload-arch=gfx950) first" % os.path.basename(_LOAD_PATH))
+        lib = ctypes.CDLL(_LOAD_PATH)
         i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         lib.fp8_quant_rows.argtypes = [vp, i64, vp, i64, vp, i64, i64, vp]
         lib.fp8_quant_rows.restype = i32

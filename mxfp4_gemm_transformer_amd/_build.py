@@ -60,5 +60,42 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized() -> str:
+    """libbsgemm_hostsan.so: the C ABI's host code (argument checks, the
+    architecture gate, dispatch) built with AddressSanitizer and
+    UndefinedBehaviorSanitizer, linked with the kernels as built by build().
+    Device code is not instrumented. Load it through BSGEMM_LIB in a process
+    that preloads clang's ASan runtime (asan_runtime())."""
+    if not os.path.exists(os.path.join(OBJ_DIR, "gemm_decode.hip.o")):
+        build()
+    api = os.path.join(CSRC, "bsgemm_api.hip")
+    obj = os.path.join(OBJ_DIR, "bsgemm_api.hostsan.o")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g"]
+    r = subprocess.run([HIPCC, *flags, *san, "-c", api, "-o", obj], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (api, r.stderr))
+    kernels = [os.path.join(OBJ_DIR, os.path.basename(src) + ".o") for src in sources()
+               if os.path.basename(src) != "bsgemm_api.hip"]
+    out = os.path.join(PKG, "libbsgemm_hostsan.so")
+    tmp = out + ".tmp%d" % os.getpid()
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host",
+                        "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan",
+                        obj, *kernels, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s" % r.stderr)
+    os.replace(tmp, out)
+    return out
+
+
+def asan_runtime() -> str:
+    """clang's shared ASan runtime, which libbsgemm_hostsan.so links against."""
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise RuntimeError("clang's libclang_rt.asan-x86_64.so was not found under /opt/rocm/llvm")
+    return found[-1]
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

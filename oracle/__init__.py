@@ -55,6 +55,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "bs_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_SAN_LIB_PATH = os.path.join(_HERE, "liboracle_san.so")
+# BS_ORACLE_LIB loads another build of bs_oracle.c (the sanitizer build of
+# build_sanitized(), under a process started with its runtime preloaded)
+_LOAD_PATH = os.environ.get("BS_ORACLE_LIB") or None
 
 EPI_NONE, EPI_BIAS, EPI_BIAS_GELU_TANH = 0, 1, 2
 
@@ -73,10 +77,22 @@ def build(force: bool = False) -> str:
     return _LIB_PATH
 
 
+def build_sanitized() -> str:
+    """Compile bs_oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer
+    (gcc, -O1, OpenMP) into liboracle_san.so; load it through BS_ORACLE_LIB in
+    a process that preloads gcc's libasan."""
+    tmp = _SAN_LIB_PATH + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-std=c11", "-O1", "-g", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                           "-fno-omit-frame-pointer", _SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, _SAN_LIB_PATH)
+    return _SAN_LIB_PATH
+
+
 def _load():
     global _lib
     if _lib is None:
-        lib = ctypes.CDLL(build())
+        lib = ctypes.CDLL(_LOAD_PATH or build())
         u8, f64, i64 = ctypes.c_uint8, ctypes.c_double, ctypes.c_int64
         vp = ctypes.c_void_p
         lib.or_e4m3_value.argtypes = [u8]
