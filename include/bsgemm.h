@@ -170,6 +170,28 @@ int gemm_bs_fp8(const void *a_e4m3, int64_t ld_a, const float *a_scale,
                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gemm_bs_fp8 for callers that cannot allocate: code under HIP graph capture
+ * without a memory pool, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments and results as gemm_bs_fp8 without the
+ * workspace: where gemm_bs_fp8 would use one (bs_workspace_bytes(0, M, N, K)
+ * > 0: the split-K decode), its partial sums go to a scratch array the
+ * library holds on each device (BS_NOALLOC_SCRATCH_BYTES bytes, kept until
+ * the process ends). A shape that needs more returns BS_EWORKSPACE and
+ * launches nothing. The call allocates and frees nothing. Every call on one
+ * device shares that device's array, and its contents on entry do not
+ * matter (every byte read is written first by the same call): calls that
+ * overlap in time on one device (other streams, other threads) race on it
+ * and must be serialized by the caller.
+ */
+#define BS_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+int gemm_bs_fp8_noalloc(const void *a_e4m3, int64_t ld_a, const float *a_scale,
+                        const void *w_e4m3, int64_t ld_w, const uint8_t *w_scale,
+                        const void *bias_bf16, int epilogue,
+                        void *y_bf16, int64_t ld_y,
+                        int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
  * MXFP4-weight GEMM with e4m3 activations ("A8W4"):
  *     w[n,k]   = e2m1(nibble k of row n) * 2^(w_scale[n][k/32]-127)
  *     y[m,n]   = epilogue(a_scale[m] * sum_k e4m3(a[m,k]) w[n,k] (+ bias[n]))

@@ -20,7 +20,7 @@ import os
 import torch
 
 __all__ = ["fp8_quant_rows", "fp8_quant_rows_static", "add_rms_norm_quant_fp8",
-           "silu_mul_quant_fp8", "gemm_bs_fp8", "gemm_mxfp4_w4a8", "gemm_fp8_rowwise",
+           "silu_mul_quant_fp8", "gemm_bs_fp8", "gemm_bs_fp8_noalloc", "gemm_mxfp4_w4a8", "gemm_fp8_rowwise",
            "fp4_quant_rows", "gemm_mxfp4_w4a4", "gemm_mxfp4_w4a8_grouped", "bs_workspace_bytes",
            "bs_status_string", "BsError", "EPI_NONE", "EPI_BIAS", "EPI_BIAS_GELU_TANH",
            "weight_shape", "w_scale_shape", "library_path", "load_library",
@@ -28,9 +28,10 @@ __all__ = ["fp8_quant_rows", "fp8_quant_rows_static", "add_rms_norm_quant_fp8",
 
 EPI_NONE, EPI_BIAS, EPI_BIAS_GELU_TANH = 0, 1, 2
 BS_OK, BS_EINVAL, BS_EALIGN, BS_EARCH, BS_EWORKSPACE, BS_ELAUNCH = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 16 << 20      # BS_NOALLOC_SCRATCH_BYTES of include/bsgemm.h
 
 EXPORTED_SYMBOLS = ("fp8_quant_rows", "fp8_quant_rows_static", "add_rms_norm_quant_fp8",
-                    "silu_mul_quant_fp8", "gemm_bs_fp8", "gemm_mxfp4_w4a8", "gemm_fp8_rowwise",
+                    "silu_mul_quant_fp8", "gemm_bs_fp8", "gemm_bs_fp8_noalloc", "gemm_mxfp4_w4a8", "gemm_fp8_rowwise",
                     "fp4_quant_rows", "gemm_mxfp4_w4a4", "gemm_mxfp4_w4a8_grouped", "bs_workspace_bytes", "bs_status_string")
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsgemm.so")
@@ -70,6 +71,8 @@ def load_library():
         lib.gemm_bs_fp8.argtypes = gemm
         lib.gemm_bs_fp8.restype = i32
         lib.gemm_mxfp4_w4a8.argtypes = gemm
+        lib.gemm_bs_fp8_noalloc.argtypes = gemm[:13] + [vp]
+        lib.gemm_bs_fp8_noalloc.restype = i32
         lib.gemm_mxfp4_w4a8.restype = i32
         lib.gemm_fp8_rowwise.argtypes = gemm
         lib.gemm_fp8_rowwise.restype = i32
@@ -299,6 +302,44 @@ def gemm_bs_fp8(a, a_scale, w, w_scale, bias=None, epilogue=EPI_NONE, y=None, wo
     """y [M, N] bf16 = epilogue(a_scale[m] * sum_k a[m,k] w[n,k] 2^(S[n/32,k/32]-127) (+ bias)).
     a: e4m3 [M, K]; w: e4m3 [N, K]; w_scale: uint8 E8M0 [N/32, K/32]."""
     return _gemm("gemm_bs_fp8", 0, a, a_scale, w, w_scale, bias, epilogue, y, workspace, stream)
+
+
+def gemm_bs_fp8_noalloc(a, a_scale, w, w_scale, bias=None, epilogue=EPI_NONE, y=None,
+                        stream=None):
+    """gemm_bs_fp8 through the entry point that allocates nothing: the split-K
+    partial sums use the library's per-device scratch array
+    (NOALLOC_SCRATCH_BYTES) instead of a workspace. y [M, N] bf16 must be
+    given. Calls that overlap in time on one device race on that array."""
+    if y is None:
+        raise ValueError("gemm_bs_fp8_noalloc needs the output y: it allocates nothing")
+    a = _u8(a, "a")
+    w = _on(_u8(w, "w"), "w", a.device)
+    M, K = a.shape
+    N = w.shape[0]
+    lda = _matrix(a, "a", M, K)
+    ldw = _matrix(w, "w", N, K)
+    if a_scale.dtype != torch.float32 or a_scale.shape != (M,) or not a_scale.is_contiguous():
+        raise ValueError("a_scale must be a contiguous fp32 [M] tensor")
+    if w_scale.dtype != torch.uint8 or tuple(w_scale.shape) != w_scale_shape(0, N, K) \
+            or not w_scale.is_contiguous():
+        raise ValueError("w_scale must be a contiguous uint8 %s tensor" % (w_scale_shape(0, N, K),))
+    _on(a_scale, "a_scale", a.device)
+    _on(w_scale, "w_scale", a.device)
+    if epilogue != EPI_NONE:
+        if bias is None or bias.dtype != torch.bfloat16 or bias.shape != (N,) \
+                or not bias.is_contiguous():
+            raise ValueError("this epilogue needs a contiguous bf16 bias [N]")
+        _on(bias, "bias", a.device)
+    if y.dtype != torch.bfloat16:
+        raise TypeError("y must be bfloat16")
+    ldy = _matrix(_on(y, "y", a.device), "y", M, N)
+    st = load_library().gemm_bs_fp8_noalloc(
+        _ptr(a), lda, _ptr(a_scale), _ptr(w), ldw, _ptr(w_scale),
+        _ptr(bias if epilogue != EPI_NONE else None), int(epilogue), _ptr(y), ldy, M, N, K,
+        ctypes.c_void_p(_stream(stream)))
+    if st != BS_OK:
+        raise BsError(st, "gemm_bs_fp8_noalloc")
+    return y
 
 
 def gemm_fp8_rowwise(a, a_scale, w, w_scale, bias=None, epilogue=EPI_NONE, y=None,

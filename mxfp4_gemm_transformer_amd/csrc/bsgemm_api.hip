@@ -94,6 +94,29 @@ int gemm_common(bool fp4, const void *a_e4m3, int64_t ld_a, const float *a_scale
     return e == hipSuccess ? BS_OK : BS_ELAUNCH;
 }
 
+// Scratch of gemm_bs_fp8_noalloc: the split-K partial sums of a call that
+// would otherwise take them from a workspace argument. One copy per device,
+// held until the process ends. In host code `scratch` names a host-side
+// stand-in, never the device array: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) uint8_t scratch[BS_NOALLOC_SCRATCH_BYTES];
+
+std::atomic<void *> g_scratch_ptr[MAX_DEVICES];
+
+// The calling thread's current device's scratch address, looked up on the
+// first call on that device (with that device current).
+int scratch_address(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return BS_EARCH;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BS_ELAUNCH;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return BS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -160,6 +183,26 @@ int gemm_bs_fp8(const void *a_e4m3, int64_t ld_a, const float *a_scale, const vo
                 size_t workspace_bytes, void *stream) {
     return gemm_common(false, a_e4m3, ld_a, a_scale, w_e4m3, ld_w, w_scale, nullptr, bias_bf16,
                        epilogue, y_bf16, ld_y, M, N, K, workspace, workspace_bytes, stream);
+}
+
+int gemm_bs_fp8_noalloc(const void *a_e4m3, int64_t ld_a, const float *a_scale,
+                        const void *w_e4m3, int64_t ld_w, const uint8_t *w_scale,
+                        const void *bias_bf16, int epilogue, void *y_bf16, int64_t ld_y,
+                        int64_t M, int64_t N, int64_t K, void *stream) {
+    if (M < 1 || N < 1 || K < 1) return BS_EINVAL;
+    const size_t need = bs_workspace_bytes(0, M, N, K);
+    if (need > BS_NOALLOC_SCRATCH_BYTES) return BS_EWORKSPACE;
+    void *ws = nullptr;
+    if (need) {
+        // the device check first: the symbol lookup needs a usable device
+        int num_cus = 0;
+        int st = device_check(&num_cus);
+        if (st != BS_OK) return st;
+        if ((st = scratch_address(&ws)) != BS_OK) return st;
+    }
+    return gemm_common(false, a_e4m3, ld_a, a_scale, w_e4m3, ld_w, w_scale, nullptr, bias_bf16,
+                       epilogue, y_bf16, ld_y, M, N, K, ws, need ? BS_NOALLOC_SCRATCH_BYTES : 0,
+                       stream);
 }
 
 int gemm_mxfp4_w4a8(const void *a_e4m3, int64_t ld_a, const float *a_scale, const void *w_fp4x2,
