@@ -372,6 +372,15 @@ def gemm_record(name, M, steps, warmup, cpu_seconds, check):
     }
     if fp4w and compute_bound:
         roof["frac_vs_fp8_rate"] = round(achieved / FP8_PEAK_TFLOPS, 4)
+    if compute_bound:
+        # the scaled MFMA the kernel issues (32x32x64, weights as the A
+        # operand), measured now on random operands: the rate this GEMM could
+        # reach if it did nothing but MFMAs
+        pair = (4 if fp4w else 0, 4 if w4a4 else 0)
+        rate = measured_mfma_rate(G, pair)
+        roof["measured_mfma_tflops"] = {"operands": "%s weights x %s activations, 32x32x64" % (
+            "fp4" if pair[0] else "fp8", "fp4" if pair[1] else "fp8"), "value": rate}
+        roof["frac_vs_measured_mfma"] = round(achieved / rate, 4)
     if parity is not None:
         rec["parity"] = parity
     if cpu_seconds > 0:
@@ -680,7 +689,9 @@ def _bench_lib():
     lib.bsb_stream_read.restype = i32
     lib.bsb_empty.argtypes = [i32, vp]
     lib.bsb_empty.restype = i32
-    lib.bsb_mfma_rate.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.bsb_mfma_rate.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.bsb_stream_read_shared.argtypes = [vp, i64, vp, i64, vp, i32, i32, vp]
+    lib.bsb_stream_read_shared.restype = i32
     lib.bsb_mfma_rate.restype = i32
     return lib
 
@@ -734,6 +745,32 @@ def bench_ceiling(args):
         out["stream_read"].append(best)
         del bufs
         torch.cuda.empty_cache()
+    # the decode layer's weights (14,784,544 - 57,344 - 4 x 8 bytes of activations and
+    # scales, rounded) with every workgroup also reading the 57,344 activation bytes
+    # of 8 tokens, as the decode GEMM without a split K does
+    nb = 14727168
+    copies = max(2, math.ceil(ROTATION_BYTES / nb))
+    bufs = [torch.full((nb,), 0x5A, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    act = torch.full((8 * 7168,), 0x5A, dtype=torch.uint8, device=dev)
+    shared = []
+    for blocks_per_cu in (1, 2, 4, 8):
+        for unroll in (1, 2, 4, 8, 16):
+            blocks = blocks_per_cu * num_cus
+            if blocks * 256 * 16 * unroll > 4 * nb:
+                continue
+            fn = lambda i: ck(lib.bsb_stream_read_shared(
+                ctypes.c_void_p(bufs[i % copies].data_ptr()), nb, ctypes.c_void_p(act.data_ptr()),
+                act.numel(), ctypes.c_void_p(sink.data_ptr()), blocks, unroll,
+                ctypes.c_void_p(G.stream.cuda_stream)))
+            G.eager(fn, warmup)
+            g_flush = G.capture(fn, copies)
+            g = G.capture(fn, steps)
+            G.replay(g_flush)
+            shared.append([blocks, unroll, round(G.timed(g, flush=g_flush) / steps * 1e6, 3)])
+    out["stream_read_plus_shared_57344_per_workgroup"] = {
+        "bytes": nb, "best_us": min(r[2] for r in shared), "sweep_blocks_unroll_us": shared}
+    del bufs
+    torch.cuda.empty_cache()
     fn = lambda i: ck(lib.bsb_empty(num_cus, ctypes.c_void_p(G.stream.cuda_stream)))
     G.eager(fn, warmup)
     g = G.capture(fn, steps)
@@ -749,9 +786,10 @@ def bench_ceiling(args):
             "ceiling": out}
 
 
-def measure_mfma_rates(G, lib, dev, iters=2048, reps=5):
+def measure_mfma_rates(G, lib, dev, iters=2048, reps=5, random_bits=0):
     """Dense scaled-MFMA rate (TFLOP/s) per shape and operand-format pair:
-    4 waves per workgroup, 2 workgroups per CU, register operands."""
+    4 waves per workgroup, 2 workgroups per CU, register operands (a fixed
+    pattern of small values, or pseudo-random bits)."""
     import torch
     num_cus = torch.cuda.get_device_properties(dev).multi_processor_count
     sink = torch.zeros(256, dtype=torch.float32, device=dev)
@@ -762,7 +800,7 @@ def measure_mfma_rates(G, lib, dev, iters=2048, reps=5):
         for fa, fb, fname in ((0, 0, "fp8 x fp8"), (4, 0, "fp4 x fp8"), (0, 4, "fp8 x fp4"),
                               (4, 4, "fp4 x fp4")):
             def fn(i):
-                st = lib.bsb_mfma_rate(shape, fa, fb, iters, blocks, waves,
+                st = lib.bsb_mfma_rate(shape, fa, fb, iters, blocks, waves, random_bits,
                                        ctypes.c_void_p(sink.data_ptr()),
                                        ctypes.c_void_p(G.stream.cuda_stream))
                 if st != 0:
@@ -775,6 +813,29 @@ def measure_mfma_rates(G, lib, dev, iters=2048, reps=5):
     return res, {"blocks": blocks, "waves_per_block": waves, "mfma_per_wave": 4 * iters}
 
 
+def measured_mfma_rate(G, pair, iters=2048, reps=3):
+    """TFLOP/s of back-to-back 32x32x64 scaled MFMAs of one operand-format
+    pair (weights, activations) on random operands, 2 workgroups of 4 waves
+    per CU."""
+    import torch
+    lib = _bench_lib()
+    dev = torch.device("cuda:0")
+    num_cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    blocks, waves = 2 * num_cus, 4
+
+    def fn(i):
+        st = lib.bsb_mfma_rate(1, pair[0], pair[1], iters, blocks, waves, 1,
+                               ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(G.stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError("bsb_mfma_rate failed (hipError %d)" % st)
+    G.eager(fn, 1)
+    g = G.capture(fn, reps)
+    G.replay(g)
+    s = G.timed(g) / reps
+    return round(blocks * waves * 4 * iters * 2 * 32 * 32 * 64 / s / 1e12, 1)
+
+
 def bench_mfma_rate(args):
     """The scaled MFMA's dense rate per operand format on this GPU: the
     ceiling of each GEMM variant (e4m3 x e4m3; W4A8's fp4 weights with e4m3
@@ -785,6 +846,7 @@ def bench_mfma_rate(args):
     torch.cuda.set_device(dev)
     G = Graphs()
     rates, shape = measure_mfma_rates(G, lib, dev)
+    rates_rnd, _ = measure_mfma_rates(G, lib, dev, random_bits=1)
     best = rates["32x32x64 fp8 x fp8"]
     return {"metric": "scaled MFMA rate per operand format, 1 GPU", "value": best,
             "unit": "TFLOP/s", "n_gpus": 1, "steps": 5, "warmup": 2, "ms_per_step": None,
@@ -792,7 +854,7 @@ def bench_mfma_rate(args):
             "data": "synthetic",
             "config": {"workload": "mfma_rate: back-to-back V_MFMA_SCALE_F32 with register operands",
                        **shape},
-            "rates_tflops": rates,
+            "rates_tflops": rates, "rates_tflops_random_operands": rates_rnd,
             "published_peaks_tflops": {"fp8": FP8_PEAK_TFLOPS, "fp4": FP4_PEAK_TFLOPS}}
 
 

@@ -147,7 +147,14 @@ int silu_mul_quant_fp8(const void *gate_up_bf16, int64_t ld_gu, void *q_e4m3, in
                        float *scale, int64_t M, int64_t I, void *stream);
 
 /*
- * Block-scaled e4m3 GEMM (y = x W^T form):
+ * Block-scaled e4m3 GEMM (y = x W^T form). The weight format is the mono
+ * runner page's AttnWeights (an e4m3 [2048, 7168] projection weight with a
+ * [64, 224] uint8 E8M0 grid: one scale byte per 32x32 block); the
+ * computation is the exact dequantize-then-matmul that the sly-radiance
+ * README's emulation path states, taking the per-token (q_fp8, scale) pair
+ * of its fused producers; the bias and bias+GELU epilogues are the flash-rt
+ * groot_n17 frontend's fused FP8 GEMM epilogue (module docstring,
+ * _fused_epilogue_enabled):
  *     acc[m,n] = sum_kb 2^(w_scale[n/32][kb]-127) * sum_{k in block kb}
  *                e4m3(a[m,k]) * e4m3(w[n,k])               (fp32 accumulation)
  *     y[m,n]   = epilogue(a_scale[m] * acc[m,n] (+ bias[n]))   -> bf16, nearest-even
@@ -192,7 +199,11 @@ int gemm_bs_fp8_noalloc(const void *a_e4m3, int64_t ld_a, const float *a_scale,
                         int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
- * MXFP4-weight GEMM with e4m3 activations ("A8W4"):
+ * MXFP4-weight GEMM with e4m3 activations ("A8W4"): the sly-radiance
+ * README's W4A8 kernels (its decode and prefill kernel rows: fp4 weights,
+ * fp8 activations), on the mono runner page's MXFP4 layout
+ * (MonoLayerWeights.check: fp4x2 weights [.., N, K/2] with uint8 E8M0
+ * scales [N, K/32], one per row per 32 along K):
  *     w[n,k]   = e2m1(nibble k of row n) * 2^(w_scale[n][k/32]-127)
  *     y[m,n]   = epilogue(a_scale[m] * sum_k e4m3(a[m,k]) w[n,k] (+ bias[n]))
  *   w_fp4x2  [N, K/2] bytes, row stride ld_w bytes; element k of a row is in
