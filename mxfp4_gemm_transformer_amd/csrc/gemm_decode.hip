@@ -206,11 +206,10 @@ void launch_one(const uint8_t *a, int64_t lda, const float *as, const uint8_t *w
 // fits (at most 8 weight fragments, and at most 8 fragments x M-tiles).
 // Folded e4m3 weights take at most 2 (two passes of 2 measured 1.5 % faster
 // than one of 4 at M=8, N=2048, K=7168 on MI355X).
-template <bool FP4, bool FOLD, int MT>
+template <bool FP4, bool FOLD, int MT, int NW>
 void launch_spw(int per_wave, const uint8_t *a, int64_t lda, const float *as, const uint8_t *w,
                 int64_t ldw, const uint8_t *ws, const float *cs, const uint16_t *bias, int epi,
                 uint16_t *y, int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t st) {
-    constexpr int NW = 8;
     constexpr int CAP = (FOLD && !FP4) ? 2 : 8 / MT;
     if (per_wave <= 1 || CAP == 1)
         launch_one<FP4, FOLD, MT, NW, 1>(a, lda, as, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
@@ -786,11 +785,25 @@ hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const flo
         }
     }
     if (M <= 8 && !large_splitk(M, N, K)) {
+        // 16 waves a workgroup for one or two tokens on a layer of at most
+        // two workgroups per CU, 8 otherwise (measured on the 2048 x 7168
+        // layer: M = 1 5.25 against 5.47 us, M = 2 5.45 against 5.61; M = 4
+        // 5.82 against 5.74, M = 8 6.41 against 6.23; on the 248320 x 5120
+        // lm_head at M = 1, 324 against 219 us)
+        if (M <= 2 && N / 8 <= 2 * (int64_t)num_cus) {
+            constexpr int NW16 = 16;
+            const int per = (int)(((K + 255) / 256 + NW16 - 1) / NW16);
+            if (fp4)
+                launch_spw<true, true, 1, NW16>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
+            else
+                launch_spw<false, true, 1, NW16>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
+            return hipGetLastError();
+        }
         const int per = (int)(((K + 255) / 256 + NW - 1) / NW);
         if (fp4)
-            launch_spw<true, true, 1>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
+            launch_spw<true, true, 1, NW>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
         else
-            launch_spw<false, true, 1>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
+            launch_spw<false, true, 1, NW>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
         return hipGetLastError();
     }
     // 8 < M <= 64, or 2 <= M <= 8 on a large layer: split K over
