@@ -68,9 +68,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", default="default",
                    choices=["default"] + GEMM_WORKLOADS +
-                           ["moe", "add_rms", "silu_mul", "ceiling", "mfma_rate", "fused_step"],
+                           ["moe", "moe_prefill", "add_rms", "silu_mul", "ceiling", "mfma_rate",
+                            "fused_step"],
                    help="default: the decode and prefill projections in one line; a GEMM "
-                        "workload (quantize + GEMM per step); moe (grouped W4A8); a fused "
+                        "workload (quantize + GEMM per step); moe / moe_prefill (grouped W4A8, 8 or "
+                        "512 tokens routed top-8 over 32 experts); a fused "
                         "producer (add_rms: residual add + RMSNorm + quantize on [M, 5120]; "
                         "silu_mul: SiLU(gate) * up + quantize on [M, 2 x 17408]); ceiling "
                         "(streaming read of rotated buffers and an empty launch); mfma_rate "
@@ -455,7 +457,7 @@ def main():
     wl_name = args.workload
     if wl_name in synth.PRODUCERS:
         result = bench_producer(args)
-    elif wl_name == "moe":
+    elif wl_name in ("moe", "moe_prefill"):
         result = bench_moe(args)
     elif wl_name == "ceiling":
         result = bench_ceiling(args)
@@ -486,13 +488,13 @@ def main():
 def bench_moe(args):
     """One step = per-token quantization of the expert-sorted rows and one
     grouped W4A8 GEMM over every expert (32 experts [4096, 7168] MXFP4, top-8
-    routing of 8 decode tokens); expert-weight copies rotate as for the GEMM
-    workloads."""
+    routing of 8 decode tokens, or of 512 prefill tokens for moe_prefill);
+    expert-weight copies rotate as for the GEMM workloads."""
     import torch
     import mxfp4_gemm_transformer_amd as bs
     import synth
 
-    m = synth.MOE
+    m = synth.MOE_PREFILL if args.workload == "moe_prefill" else synth.MOE
     E, N, K, tokens, topk = m["E"], m["N"], m["K"], m["tokens"], m["topk"]
     steps = args.steps if args.steps is not None else 500
     warmup = args.warmup if args.warmup is not None else 20
@@ -514,9 +516,11 @@ def bench_moe(args):
     s = torch.empty((T,), dtype=torch.float32, device=dev)
     y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
 
+    max_rows = int(np.diff(off).max())
+
     def gemm(i):
         bs.gemm_mxfp4_w4a8_grouped(q, s, offsets, w_list[i % copies], ws_list[i % copies], y=y,
-                                   max_rows_per_expert=tokens)
+                                   max_rows_per_expert=max_rows)
 
     def step(i):
         bs.fp8_quant_rows(x, q, s)
@@ -533,15 +537,33 @@ def bench_moe(args):
     step_s = G.timed(g_step, flush=g_flush) / steps
     wall_s = time.perf_counter() - t0
     parity = None
+    big = T * N * K > (1 << 33)     # the prefill routing: outputs sampled per expert
     if not args.no_check:
         import oracle
         qh, sh = oracle.quant_rows(xt[row_token])
-        ref, absum = oracle.gemm_mxfp4_w4a8_grouped(qh, sh, off, w_host, ws_host)
         got = y.float().cpu().numpy().astype(np.float64)
-        ok = bool(np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4 * absum))
         qok = bool(np.array_equal(q.cpu().numpy(), qh))
+        if big:
+            rng_c = np.random.default_rng(11)
+            ok, pts = True, 0
+            for e in range(E):
+                r0, r1 = int(off[e]), int(off[e + 1])
+                if r0 == r1:
+                    continue
+                ms = np.concatenate([np.arange(r1 - r0), rng_c.integers(0, r1 - r0, 64)])
+                ns = np.concatenate([np.arange(r1 - r0) * 29 % N, rng_c.integers(0, N, 64)])
+                ref, absum = oracle.gemm_sampled("mxfp4", qh[r0:r1], sh[r0:r1], w_host[e], ws_host[e],
+                                                 None, 0, ms, ns)
+                g = got[r0 + ms, ns]
+                ok &= bool(np.all(np.abs(g - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4 * absum))
+                pts += ms.size
+            how = "every row, one column each, plus 64 random outputs per expert"
+        else:
+            ref, absum = oracle.gemm_mxfp4_w4a8_grouped(qh, sh, off, w_host, ws_host)
+            ok = bool(np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4 * absum))
+            pts, how = int(ref.size), "all outputs"
         parity = {"quant_bit_exact": qok, "gemm_within_tolerance": ok,
-                  "gemm_points": int(ref.size), "gemm_sample": "all outputs", "ok": ok and qok}
+                  "gemm_points": pts, "gemm_sample": how, "ok": ok and qok}
     gemm_s = G.timed(g_gemm, flush=g_flush) / steps
     active = int(np.count_nonzero(np.diff(off)))
     w_alg = active * (N * K // 2 + N * (K // 32))
@@ -552,15 +574,19 @@ def bench_moe(args):
         "value": round((gemm_bytes + quant_bytes) / step_s / 1e9, 2), "unit": "GB/s",
         "steps": steps, "warmup": warmup, "ms_per_step": round(step_s * 1e3, 5),
         "dtype": "fp8_e4m3 x fp4_e2m1",
-        "config": {"workload": "moe E=%d N=%d K=%d, %d tokens top-%d = %d rows over %d active "
-                               "experts (grouped MXFP4 W4A8)" % (E, N, K, tokens, topk, T, active),
+        "config": {"workload": "%s E=%d N=%d K=%d, %d tokens top-%d = %d rows over %d active "
+                               "experts (grouped MXFP4 W4A8)" % (args.workload, E, N, K, tokens, topk,
+                                                                  T, active),
                    "E": E, "N": N, "K": K, "rows": T, "active_experts": active,
                    "weight_copies_rotated": copies,
                    "step": "fp8_quant_rows + gemm_mxfp4_w4a8_grouped", "graph_replay": True},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "gemm_mxfp4_w4a8_grouped", "avg_launch_us": round(gemm_s * 1e6, 3),
-                     "algorithmic_bytes_per_launch": gemm_bytes},
+                     "algorithmic_bytes_per_launch": gemm_bytes,
+                     "algorithmic_flops_per_launch": 2 * T * N * K,
+                     "tflops": round(2 * T * N * K / gemm_s / 1e12, 1),
+                     "max_rows_per_expert": max_rows},
         "kernels_us": {"fp8_quant_rows+gemm": round(step_s * 1e6, 3),
                        "gemm_mxfp4_w4a8_grouped": round(gemm_s * 1e6, 3)},
         "step_bytes": gemm_bytes + quant_bytes, "wall_s_timed_region": round(wall_s, 6),
@@ -570,17 +596,28 @@ def bench_moe(args):
     if args.cpu_seconds > 0:
         import oracle
         oracle.build()
+        # the whole step, or for the prefill routing the first two rows of
+        # every expert (all N outputs each)
+        keep = np.concatenate([np.arange(off[e], min(off[e] + 2, off[e + 1])) for e in range(E)]) \
+            if big else np.arange(T)
+        counts = np.array([min(2, off[e + 1] - off[e]) if big else off[e + 1] - off[e]
+                           for e in range(E)])
+        off_s = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        xs = xt[row_token][keep]
         runs, t_total = 0, 0.0
         while t_total < args.cpu_seconds or runs == 0:
             t1 = time.perf_counter()
-            qh, sh = oracle.quant_rows(xt[row_token])
-            oracle.gemm_mxfp4_w4a8_grouped(qh, sh, off, w_host, ws_host)
+            qh, sh = oracle.quant_rows(xs)
+            oracle.gemm_mxfp4_w4a8_grouped(qh, sh, off_s, w_host, ws_host)
             t_total += time.perf_counter() - t1
             runs += 1
+        frac = len(keep) / T
+        step_b = (gemm_bytes + quant_bytes - w_alg) * frac + w_alg
         rec["cpu_baseline"] = {
-            "value": round((gemm_bytes + quant_bytes) * runs / t_total / 1e9, 4), "unit": "GB/s",
+            "value": round(step_b * runs / t_total / 1e9, 4), "unit": "GB/s",
             "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "the whole step (%d rows), %d passes in %.1f s" % (T, runs, t_total),
+            "sample": "%d of %d rows (all %d outputs each), %d passes in %.1f s" % (
+                len(keep), T, N, runs, t_total),
             "cpu_model": _cpu_model()}
     return line(rec)
 
@@ -692,6 +729,8 @@ def _bench_lib():
     lib.bsb_mfma_rate.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.bsb_stream_read_shared.argtypes = [vp, i64, vp, i64, vp, i32, i32, vp]
     lib.bsb_stream_read_shared.restype = i32
+    lib.bsb_l2_read.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+    lib.bsb_l2_read.restype = i32
     lib.bsb_mfma_rate.restype = i32
     return lib
 
@@ -771,6 +810,25 @@ def bench_ceiling(args):
         "bytes": nb, "best_us": min(r[2] for r in shared), "sweep_blocks_unroll_us": shared}
     del bufs
     torch.cuda.empty_cache()
+    # per-CU read rate from L2, into registers and with LDS-mode loads into
+    # LDS (the prefill kernels' staging), 1 or 2 workgroups of 256 per CU,
+    # each re-reading its own region (2 MiB per XCD in all, L2-resident)
+    l2 = {}
+    buf = torch.full((num_cus * 65536,), 0x5A, dtype=torch.uint8, device=dev)
+    for per_cu, chunk in ((1, 65536), (2, 32768)):
+        iters = 64 * 65536 // chunk
+        for dma in (0, 1):
+            fn = lambda i: ck(lib.bsb_l2_read(ctypes.c_void_p(buf.data_ptr()), chunk, iters,
+                                              per_cu * num_cus, dma, ctypes.c_void_p(sink.data_ptr()),
+                                              ctypes.c_void_p(G.stream.cuda_stream)))
+            G.eager(fn, 3)
+            g = G.capture(fn, 10)
+            G.replay(g)
+            us = G.timed(g) / 10 * 1e6
+            l2["%d workgroup(s) per CU, %s" % (per_cu, "LDS-mode loads" if dma else "registers")] = {
+                "us": round(us, 2), "GBps_per_CU": round(per_cu * chunk * iters / us / 1e3, 1)}
+    out["l2_read_per_cu"] = l2
+    del buf
     fn = lambda i: ck(lib.bsb_empty(num_cus, ctypes.c_void_p(G.stream.cuda_stream)))
     G.eager(fn, warmup)
     g = G.capture(fn, steps)

@@ -264,16 +264,18 @@ int gemm_mxfp4_w4a4(const void *a_fp4x2, int64_t ld_a, const uint8_t *a_scale,
  *   expert_offsets  DEVICE pointer to E + 1 int32, nondecreasing, from 0 to
  *                   at most T (read by the kernel; rows outside [0, T) are
  *                   never touched whatever they hold)
- *   max_rows_per_expert  an upper bound on any expert's rows (picks how many
- *                   tokens a pass takes; a wrong bound costs time, not
+ *   max_rows_per_expert  an upper bound on any expert's rows: it picks the
+ *                   kernel and its tiles (a wrong bound costs time, not
  *                   correctness)
  *   w_fp4x2  expert e's [N, K/2] at w + e * w_expert_stride bytes, row
  *            stride ld_w bytes; w_scale [E, N, K/32] E8M0 dense
  *   bias     [E, N] bf16 or NULL; y_bf16 [T, N], row stride ld_y
  *   E <= 65535. Rows of y outside every expert's range are not written.
- *   This is the decode-sized grouped kernel (rows per expert small: each
- *   workgroup streams its 8 weight rows of one expert once per pass of up
- *   to 32 rows).
+ *   Up to 32 rows per expert (decode), each workgroup streams its 8 weight
+ *   rows of one expert once per pass of up to 32 token rows. Past 32 (and
+ *   K % 64 == 0), every expert is computed with the large-M tiles of the
+ *   prefill GEMM (64x64 up to 64 rows, 128x128 up to 128, else 256x256),
+ *   experts side by side in one launch.
  */
 int gemm_mxfp4_w4a8_grouped(const void *a_e4m3, int64_t ld_a, const float *a_scale,
                             const int32_t *expert_offsets, int64_t E,

@@ -24,10 +24,19 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // xor that is stored only if it equals a value the data never produces
 // (the buffers hold repeated non-zero bytes), so no load is dead code and
 // nothing is written.
+// With `shared` (s16 chunks of 16 bytes): every workgroup also reads all of
+// it, as each workgroup of a decode GEMM without a split K reads every
+// token's activations once.
 template <int UNROLL>
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restrict__ p, int64_t n16,
-                                                          uint32_t *__restrict__ sink) {
+                                                          uint32_t *__restrict__ sink,
+                                                          const u32x4 *__restrict__ shared = nullptr,
+                                                          int64_t s16 = 0) {
     uint32_t acc = 0;
+    for (int64_t i = threadIdx.x; i < s16; i += 256) {
+        const u32x4 v = shared[i];
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
     const int64_t chunk = 256 * UNROLL;
     for (int64_t base = (int64_t)blockIdx.x * chunk; base < n16; base += (int64_t)gridDim.x * chunk) {
         u32x4 v[UNROLL];
@@ -44,17 +53,90 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restric
 
 __global__ void empty_kernel() {}
 
+// Per-CU read rate from L2: every workgroup reads its own `chunk`-byte
+// region (all regions together fit the XCDs' L2) `iters` times, 16 bytes a
+// lane, 8 loads in flight per wave, either into registers (DMA = false) or
+// with LDS-mode buffer loads straight into a 64 KiB LDS ring (DMA = true:
+// lane l's 16 bytes land at M0 + 16 l).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t m0, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rs)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <bool DMA>
+__global__ __launch_bounds__(256) void l2_read_kernel(const uint8_t *__restrict__ p, int chunk, int iters,
+                                                      uint32_t *__restrict__ sink) {
+    __shared__ __align__(16) uint8_t lds[65536];
+    const uint8_t *base = p + (int64_t)blockIdx.x * chunk;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(base), (short)0, chunk, 0x00020000);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t *)lds);
+    const int per = chunk / 4096;                  // 4 KiB per round of the 4 waves
+    uint32_t acc = 0;
+    for (int it = 0; it < iters; ++it) {
+        for (int j0 = 0; j0 < per; j0 += 8) {
+            if (DMA) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int j = j0 + u;
+                    const uint32_t off = (uint32_t)(j * 4096 + threadIdx.x * 16);
+                    const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+                        lds0 + (uint32_t)((j * 4096 + wave * 1024) & 65535));
+                    dma16(rs, m0, j < per ? off : 0x80000000u);
+                }
+                asm volatile("s_waitcnt vmcnt(8)" : : : "memory");
+            } else {
+                uint32_t v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int j = j0 + u;
+                    const auto q = __builtin_amdgcn_raw_buffer_load_b128(
+                        rs, j < per ? (uint32_t)(j * 4096 + threadIdx.x * 16) : 0x80000000u, 0, 0);
+                    v[u] = q[0] ^ q[1] ^ q[2] ^ q[3];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) acc ^= v[u];
+            }
+        }
+    }
+    if (DMA) {
+        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+        __syncthreads();
+        acc = reinterpret_cast<const uint32_t *>(lds)[threadIdx.x];
+    }
+    if (acc == 0xDEADBEEFu) sink[blockIdx.x & 255] = acc;
+}
+
 // `iters` rounds of 4 independent scaled MFMAs per wave (4 accumulators
 // hide the instruction's dependent-issue latency); operands stay in
 // registers. Formats per the instruction's cbsz / blgp encoding: 0 = fp8
 // e4m3, 4 = fp4 e2m1.
-template <int FA, int FB, bool BIG>
+// RND: operands of pseudo-random bits (fp8 codes with the top exponent bit
+// cleared, so none is NaN) instead of a fixed pattern of small values.
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+    x ^= x >> 16; x *= 0x7FEB352Du; x ^= x >> 15; x *= 0x846CA68Bu; x ^= x >> 16;
+    return x;
+}
+
+template <int FA, int FB, bool BIG, bool RND>
 __global__ __launch_bounds__(256) void mfma_rate_kernel(int iters, float *__restrict__ sink) {
     v8i a, b;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-        a[r] = (int)(0x38383838u + threadIdx.x + r);
-        b[r] = (int)(0x22222222u + threadIdx.x * 3 + r);
+        if (RND) {
+            const uint32_t t = (blockIdx.x * 256u + threadIdx.x) * 16u + (uint32_t)r;
+            a[r] = (int)(mix32(t) & (FA == 0 ? 0xBFBFBFBFu : 0xFFFFFFFFu));
+            b[r] = (int)(mix32(t + 8u) & (FB == 0 ? 0xBFBFBFBFu : 0xFFFFFFFFu));
+        } else {
+            a[r] = (int)(0x38383838u + threadIdx.x + r);
+            b[r] = (int)(0x22222222u + threadIdx.x * 3 + r);
+        }
     }
     if (BIG) {
         v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
@@ -108,6 +190,44 @@ int bsb_stream_read(const void *p, int64_t bytes, void *sink, int blocks, int un
     return (int)hipGetLastError();
 }
 
+// As bsb_stream_read, with every workgroup also reading all `shared_bytes`
+// (a multiple of 16) at the 16-byte-aligned device address `shared`.
+int bsb_stream_read_shared(const void *p, int64_t bytes, const void *shared, int64_t shared_bytes,
+                           void *sink, int blocks, int unroll, void *stream) {
+    if (!p || !shared || !sink || bytes <= 0 || bytes % 16 || shared_bytes <= 0 || shared_bytes % 16 ||
+        blocks < 1)
+        return (int)hipErrorInvalidValue;
+    const auto *q = static_cast<const u32x4 *>(p);
+    const auto *sh = static_cast<const u32x4 *>(shared);
+    auto *s = static_cast<uint32_t *>(sink);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t n16 = bytes / 16, s16 = shared_bytes / 16;
+    switch (unroll) {
+    case 1: hipLaunchKernelGGL(stream_read_kernel<1>, dim3(blocks), dim3(256), 0, st, q, n16, s, sh, s16); break;
+    case 2: hipLaunchKernelGGL(stream_read_kernel<2>, dim3(blocks), dim3(256), 0, st, q, n16, s, sh, s16); break;
+    case 4: hipLaunchKernelGGL(stream_read_kernel<4>, dim3(blocks), dim3(256), 0, st, q, n16, s, sh, s16); break;
+    case 8: hipLaunchKernelGGL(stream_read_kernel<8>, dim3(blocks), dim3(256), 0, st, q, n16, s, sh, s16); break;
+    case 16: hipLaunchKernelGGL(stream_read_kernel<16>, dim3(blocks), dim3(256), 0, st, q, n16, s, sh, s16); break;
+    default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
+// `blocks` workgroups of 256 threads each read their own `chunk` bytes
+// (a multiple of 32 KiB, at most 1 MiB) of the device buffer p (at least
+// blocks * chunk bytes) `iters` times: into registers (dma = 0) or into LDS
+// with LDS-mode loads (dma = 1). `sink`: 1 KiB, never written in practice.
+int bsb_l2_read(const void *p, int chunk, int iters, int blocks, int dma, void *sink, void *stream) {
+    if (!p || !sink || chunk <= 0 || chunk % 32768 || chunk > (1 << 20) || iters < 1 || blocks < 1)
+        return (int)hipErrorInvalidValue;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const auto *q = static_cast<const uint8_t *>(p);
+    auto *s = static_cast<uint32_t *>(sink);
+    if (dma) hipLaunchKernelGGL(l2_read_kernel<true>, dim3(blocks), dim3(256), 0, st, q, chunk, iters, s);
+    else hipLaunchKernelGGL(l2_read_kernel<false>, dim3(blocks), dim3(256), 0, st, q, chunk, iters, s);
+    return (int)hipGetLastError();
+}
+
 // One launch of a kernel with no body, `blocks` workgroups of 64 threads.
 int bsb_empty(int blocks, void *stream) {
     if (blocks < 1) return (int)hipErrorInvalidValue;
@@ -116,20 +236,23 @@ int bsb_empty(int blocks, void *stream) {
 }
 
 // `blocks` workgroups of `waves` (1..4) waves, each wave issuing 4 * iters
-// scaled MFMAs: shape 0 = 16x16x128, 1 = 32x32x64; formats (fa, fb) in
+// scaled MFMAs on fixed-pattern operands, or on pseudo-random bits when
+// random_bits != 0: shape 0 = 16x16x128, 1 = 32x32x64; formats (fa, fb) in
 // {(0,0) fp8 x fp8, (0,4) fp8 x fp4, (4,0) fp4 x fp8, (4,4) fp4 x fp4}.
 // FLOPs = blocks * waves * 4 * iters * (2 * 16 * 16 * 128, or 2 * 32 * 32 * 64).
 // `sink` is 1 KiB of device memory that is never written in practice.
-int bsb_mfma_rate(int shape, int fa, int fb, int iters, int blocks, int waves, void *sink,
-                  void *stream) {
+int bsb_mfma_rate(int shape, int fa, int fb, int iters, int blocks, int waves, int random_bits,
+                  void *sink, void *stream) {
     if (!sink || iters < 1 || blocks < 1 || waves < 1 || waves > 4) return (int)hipErrorInvalidValue;
     hipStream_t st = static_cast<hipStream_t>(stream);
     float *s = static_cast<float *>(sink);
     const dim3 grid(blocks), block(64 * waves);
 #define BSB_MFMA(FA, FB)                                                                          \
     if (fa == FA && fb == FB) {                                                                   \
-        if (shape) hipLaunchKernelGGL((mfma_rate_kernel<FA, FB, true>), grid, block, 0, st, iters, s); \
-        else hipLaunchKernelGGL((mfma_rate_kernel<FA, FB, false>), grid, block, 0, st, iters, s); \
+        if (shape && random_bits) hipLaunchKernelGGL((mfma_rate_kernel<FA, FB, true, true>), grid, block, 0, st, iters, s); \
+        else if (shape) hipLaunchKernelGGL((mfma_rate_kernel<FA, FB, true, false>), grid, block, 0, st, iters, s); \
+        else if (random_bits) hipLaunchKernelGGL((mfma_rate_kernel<FA, FB, false, true>), grid, block, 0, st, iters, s); \
+        else hipLaunchKernelGGL((mfma_rate_kernel<FA, FB, false, false>), grid, block, 0, st, iters, s); \
         return (int)hipGetLastError();                                                            \
     }
     BSB_MFMA(0, 0)

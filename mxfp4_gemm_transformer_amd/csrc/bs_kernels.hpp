@@ -68,6 +68,15 @@ hipError_t launch_gemm_grouped(bool fp4, const uint8_t *a, int64_t lda, const fl
                                const uint8_t *w, int64_t ldw, int64_t w_estride,
                                const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y,
                                int64_t ldy, int64_t T, int64_t N, int64_t K, hipStream_t stream);
+// Its prefill-sized form (the large-M tiles per expert), MXFP4 weights only;
+// launch_gemm_grouped takes it when max_rows > GROUPED_DECODE_MAX_ROWS and
+// K % 64 == 0.
+constexpr int64_t GROUPED_DECODE_MAX_ROWS = 32;
+hipError_t launch_gemm_grouped_prefill(const uint8_t *a, int64_t lda, const float *a_scale,
+                                       const int32_t *offsets, int64_t E, int64_t max_rows,
+                                       const uint8_t *w, int64_t ldw, int64_t w_estride,
+                                       const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y,
+                                       int64_t ldy, int64_t T, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_gemm_prefill_w4a4(const uint8_t *a, int64_t lda, const uint8_t *a_e8m0,
                                     const uint8_t *w, int64_t ldw, const uint8_t *ws,
                                     const uint16_t *bias, int epi, uint16_t *y, int64_t ldy,

@@ -955,6 +955,9 @@ hipError_t launch_gemm_grouped(bool fp4, const uint8_t *a, int64_t lda, const fl
                                const uint8_t *w, int64_t ldw, int64_t w_estride,
                                const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y,
                                int64_t ldy, int64_t T, int64_t N, int64_t K, hipStream_t st) {
+    if (fp4 && max_rows > GROUPED_DECODE_MAX_ROWS && K % 64 == 0)
+        return launch_gemm_grouped_prefill(a, lda, a_scale, offsets, E, max_rows, w, ldw, w_estride,
+                                           ws, bias, epi, y, ldy, T, N, K, st);
     const dim3 grid((unsigned)(N / 8), (unsigned)E);
 #define BSG_GROUPED(FP4_, G_)                                                                      \
     hipLaunchKernelGGL((gemm_grouped_decode_kernel<FP4_, G_>), grid, dim3(512), 0, st, a, lda,      \

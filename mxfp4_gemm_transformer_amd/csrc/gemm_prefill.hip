@@ -475,26 +475,61 @@ struct DCfg {
 
 // FP4A: fp4 activations [M, K/2] with E8M0 scales AS [M, K/32] (W4A4); then
 // a_scale is unused (1).
+//
+// GROUPED (MoE, prefill-sized expert batches): blockIdx.y is the expert e;
+// its token rows are [gp.off[e], gp.off[e + 1]) of A, a_scale and Y (offsets
+// read on the device, clamped to [0, gp.rows]), its weights start at
+// W + e * gp.w_estride with scales WS + e * (N or N / 32) * K / 32 and bias
+// + e * N. The grid's M (a bound on any expert's rows) sets the tiles per
+// expert; a workgroup takes m-tiles m0, m0 + that, ... up to the expert's
+// rows, so any distribution of rows is computed, whatever the bound.
+struct GroupArgs {
+    const int32_t *off;
+    int64_t w_estride;
+    int rows;
+};
+
 template <bool FP4, int BM, int BN, int NBUF, int WGM, int WGN, bool FP4A = false, int SPS = 1,
-          int SLAB_KB = 0>
+          int SLAB_KB = 0, bool GROUPED = false>
 __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
-    const uint8_t *__restrict__ A, int64_t lda, const float *__restrict__ a_scale,
-    const uint8_t *__restrict__ W, int64_t ldw, const uint8_t *__restrict__ WS,
-    const float *__restrict__ colscale, const uint16_t *__restrict__ bias, int epi,
-    uint16_t *__restrict__ Y, int64_t ldy, int M, int N, int K, int group_m,
-    const uint8_t *__restrict__ AS = nullptr) {
+    const uint8_t *__restrict__ A_in, int64_t lda, const float *__restrict__ a_scale_in,
+    const uint8_t *__restrict__ W_in, int64_t ldw, const uint8_t *__restrict__ WS_in,
+    const float *__restrict__ colscale, const uint16_t *__restrict__ bias_in, int epi,
+    uint16_t *__restrict__ Y_in, int64_t ldy, int M_grid, int N, int K, int group_m,
+    const uint8_t *__restrict__ AS, GroupArgs gp) {
     using C = DCfg<FP4, BM, BN, NBUF, WGM, WGN, FP4A, SPS, SLAB_KB>;
     __shared__ __align__(16) uint8_t lds[C::LDS];
 
     // ---- tile of this workgroup (XCD-aware grouped order)
-    const int Mt = (M + BM - 1) / BM, Nt = (N + BN - 1) / BN, T = Mt * Nt;
+    const int Mt = (M_grid + BM - 1) / BM, Nt = (N + BN - 1) / BN, T = Mt * Nt;
     int t = blockIdx.x;
     if (T % NXCD == 0) t = (t % NXCD) * (T / NXCD) + t / NXCD;
     const int per_group = group_m * Nt;
     const int first_m = (t / per_group) * group_m;
     const int gm = min(Mt - first_m, group_m);
-    const int m0 = (first_m + (t % per_group) % gm) * BM;
+    const int m_first = (first_m + (t % per_group) % gm) * BM;
     const int n0 = ((t % per_group) / gm) * BN;
+
+    const uint8_t *A = A_in;
+    const float *a_scale = a_scale_in;
+    const uint8_t *W = W_in;
+    const uint8_t *WS = WS_in;
+    const uint16_t *bias = bias_in;
+    uint16_t *Y = Y_in;
+    int M = M_grid;
+    if constexpr (GROUPED) {
+        const int e = blockIdx.y;
+        const int r0 = min(max(gp.off[e], 0), gp.rows);
+        const int r1 = max(r0, min(gp.off[e + 1], gp.rows));
+        A += (int64_t)r0 * lda;
+        a_scale += r0;
+        Y += (int64_t)r0 * ldy;
+        W += (int64_t)e * gp.w_estride;
+        if (WS) WS += (int64_t)e * (FP4 ? N : N / 32) * (K >> 5);
+        if (bias) bias += (int64_t)e * N;
+        M = r1 - r0;
+    }
+    for (int m0 = m_first; m0 < M; m0 += Mt * BM) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -825,6 +860,8 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         }
         __syncthreads();
     }
+    if constexpr (!GROUPED) break;   // one tile; the grid covers every m-tile
+    }
 }
 
 template <bool FP4, int BM, int BN, int NBUF, int WGM = 2, int WGN = 2, bool FP4A = false,
@@ -836,7 +873,25 @@ hipError_t launch_tile_dma(const uint8_t *a, int64_t lda, const float *as, const
     auto kern = gemm_prefill_dma_kernel<FP4, BM, BN, NBUF, WGM, WGN, FP4A, SPS, SLAB_KB>;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(WGM * WGN * 64), 0, st, a, lda, as, w,
-                       ldw, ws, cs, bias, epi, y, ldy, (int)M, (int)N, (int)K, 8, a_e8m0);
+                       ldw, ws, cs, bias, epi, y, ldy, (int)M, (int)N, (int)K, 8, a_e8m0,
+                       GroupArgs{nullptr, 0, 0});
+    return hipGetLastError();
+}
+
+// The grouped form over E experts: a grid of (m-tiles of max_rows) x
+// (n-tiles) per expert, experts on the grid's y.
+template <bool FP4, int BM, int BN, int NBUF, int WGM = 2, int WGN = 2, int SPS = 1, int SLAB_KB = 0>
+hipError_t launch_tile_dma_grouped(const uint8_t *a, int64_t lda, const float *as,
+                                   const int32_t *off, int64_t E, int64_t max_rows, int64_t T,
+                                   const uint8_t *w, int64_t ldw, int64_t w_estride,
+                                   const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y,
+                                   int64_t ldy, int64_t N, int64_t K, hipStream_t st) {
+    auto kern = gemm_prefill_dma_kernel<FP4, BM, BN, NBUF, WGM, WGN, false, SPS, SLAB_KB, true>;
+    const int64_t rows = max_rows < T ? max_rows : T;
+    const int64_t tiles = ((rows + BM - 1) / BM) * ((N + BN - 1) / BN);
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles, (unsigned)E), dim3(WGM * WGN * 64), 0, st, a, lda,
+                       as, w, ldw, ws, nullptr, bias, epi, y, ldy, (int)rows, (int)N, (int)K, 8,
+                       nullptr, GroupArgs{off, w_estride, (int)T});
     return hipGetLastError();
 }
 
@@ -977,6 +1032,27 @@ hipError_t launch_prefill_dma(bool fp4, const uint8_t *a, int64_t lda, const flo
 }
 
 }  // namespace
+
+// Grouped W4A8 for prefill-sized expert batches: MXFP4 weights, 64x64 tiles
+// for at most 64 rows per expert, 128x128 up to 128, else 256x256 (every
+// n-tile re-reads its expert's rows, so wider tiles halve that traffic);
+// with the tile's E8M0 rows in LDS when K % 128 == 0 and K / 32 <= 192,
+// else one-step stages.
+hipError_t launch_gemm_grouped_prefill(const uint8_t *a, int64_t lda, const float *a_scale,
+                                       const int32_t *offsets, int64_t E, int64_t max_rows,
+                                       const uint8_t *w, int64_t ldw, int64_t w_estride,
+                                       const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y,
+                                       int64_t ldy, int64_t T, int64_t N, int64_t K, hipStream_t st) {
+#define BSG_GARGS a, lda, a_scale, offsets, E, max_rows, T, w, ldw, w_estride, ws, bias, epi, y, ldy, N, K, st
+    if (K % 128 == 0 && K / 32 <= SLAB_KB_W4A8) {
+        if (max_rows <= 64) return launch_tile_dma_grouped<true, 64, 64, 2, 2, 2, 2, SLAB_KB_W4A8>(BSG_GARGS);
+        if (max_rows <= 128) return launch_tile_dma_grouped<true, 128, 128, 2, 2, 2, 2, SLAB_KB_W4A8>(BSG_GARGS);
+        return launch_tile_dma_grouped<true, 256, 256, 2, 4, 2, 2, SLAB_KB_W4A8>(BSG_GARGS);
+    }
+    if (max_rows <= 128) return launch_tile_dma_grouped<true, 128, 128, 4>(BSG_GARGS);
+    return launch_tile_dma_grouped<true, 256, 256, 4, 4, 2>(BSG_GARGS);
+#undef BSG_GARGS
+}
 
 hipError_t launch_gemm_prefill_w4a4(const uint8_t *a, int64_t lda, const uint8_t *a_e8m0,
                                     const uint8_t *w, int64_t ldw, const uint8_t *ws,

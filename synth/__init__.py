@@ -231,6 +231,9 @@ def make(name: str, M: int | None = None, seed: int = 0) -> dict:
 # size and routing are this workload's choice: 32 local experts, 2 inter =
 # 4096, top-8 routing of a decode batch of 8 tokens.
 MOE = {"E": 32, "N": 4096, "K": 7168, "tokens": 8, "topk": 8}
+# the same experts at prefill: 512 tokens routed top-8 (4096 rows, about 128
+# per expert)
+MOE_PREFILL = {"E": 32, "N": 4096, "K": 7168, "tokens": 512, "topk": 8}
 _T_ROUTE = 8
 
 
