@@ -153,6 +153,8 @@ def _load():
         lib.or_silu_mul_quant.restype = None
         lib.or_num_threads.argtypes = []
         lib.or_num_threads.restype = ctypes.c_int
+        lib.or_set_num_threads.argtypes = [ctypes.c_int]
+        lib.or_set_num_threads.restype = None
         _lib = lib
     return _lib
 
@@ -457,6 +459,11 @@ def quant_mxfp4_weights(values: np.ndarray):
 
 def num_threads() -> int:
     return int(_load().or_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on."""
+    _load().or_set_num_threads(int(n))
 
 
 def within_tolerance(y, ref, absum):

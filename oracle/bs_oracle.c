@@ -670,6 +670,18 @@ void or_quant_mxfp4_rows(const uint16_t *x, int64_t ldx, int64_t M, int64_t K,
 }
 
 /* Threads the OpenMP runtime will use (for reporting). */
+/* Threads of the parallel loops from now on (the benchmark's single-core
+ * baseline); n >= 1. */
+void or_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
+
 int or_num_threads(void)
 {
 #ifdef _OPENMP
