@@ -188,8 +188,9 @@ class Graphs:
             g.replay()
         self.torch.cuda.synchronize()
 
-    def timed(self, g, flush=None):
-        """Seconds for one replay of g; `flush` is replayed first, untimed."""
+    def timed(self, g, flush=None, replays=1):
+        """Seconds for `replays` back-to-back replays of g; `flush` is
+        replayed first, untimed."""
         torch = self.torch
         if flush is not None:
             self.replay(flush)
@@ -198,10 +199,17 @@ class Graphs:
         torch.cuda.synchronize()
         with torch.cuda.stream(self.stream):
             e0.record(self.stream)
-            g.replay()
+            for _ in range(replays):
+                g.replay()
             e1.record(self.stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e-3
+
+
+# Launches each kernel's own timing averages over (whole rotation cycles,
+# replayed back to back), so that a graph's launch latency is spread over
+# about this many launches whatever --steps is.
+KERNEL_TIMING_LAUNCHES = 200
 
 
 # --------------------------------------------------------- parity re-check
@@ -313,9 +321,8 @@ def gemm_record(name, M, steps, warmup, cpu_seconds, check):
     G.eager(step, warmup)                      # warm-up: eager steps
     g_flush = G.capture(gemm_only, copies)     # touches every weight copy once, in order
     g_step = G.capture(step, steps)
-    g_gemm = G.capture(gemm_only, steps)
     g_quant = G.capture(quant_only, steps)
-    for g in (g_flush, g_step, g_gemm, g_quant):
+    for g in (g_flush, g_step, g_quant):
         G.replay(g)                            # first replays, untimed
 
     t0 = time.perf_counter()
@@ -324,8 +331,14 @@ def gemm_record(name, M, steps, warmup, cpu_seconds, check):
     parity = None
     if check:
         parity = parity_check(wl, d, q.cpu().numpy(), s.cpu().numpy(), y.float().cpu().numpy())
-    gemm_s = G.timed(g_gemm, flush=g_flush) / steps
-    quant_s = G.timed(g_quant, flush=g_flush) / steps
+    # each kernel's average launch time: the GEMM over whole rotation cycles
+    # (the flush graph: one launch per weight copy, each copy last touched a
+    # cycle earlier), the quantizer over its own graph, both replayed back to
+    # back to about KERNEL_TIMING_LAUNCHES launches
+    r_gemm = max(1, math.ceil(KERNEL_TIMING_LAUNCHES / copies))
+    gemm_s = G.timed(g_flush, flush=g_flush, replays=r_gemm) / (r_gemm * copies)
+    r_quant = max(1, math.ceil(KERNEL_TIMING_LAUNCHES / steps))
+    quant_s = G.timed(g_quant, replays=r_quant) / (r_quant * steps)
 
     alg = algorithmic(wl, M)
     step_bytes = alg["quant_bytes"] + alg["gemm_bytes"]
@@ -367,7 +380,10 @@ def gemm_record(name, M, steps, warmup, cpu_seconds, check):
             ["none", "bias", "bias+tanh-GELU"][epi]),
             "M": M, "N": wl.N, "K": wl.K, "weight_copies_rotated": copies,
             "rotation": "every copy touched in order before each timed replay",
-            "step": "%s + %s" % (qname, kernel), "graph_replay": True},
+            "step": "%s + %s" % (qname, kernel), "graph_replay": True,
+            "kernel_timing": "GEMM: %d replays of a graph of one launch per weight copy (%d "
+                             "launches); quantizer: %d replays of its %d-launch graph" % (
+                                 r_gemm, r_gemm * copies, r_quant, steps)},
         "roofline": roof,
         "kernels_us": {qname: round(quant_s * 1e6, 3), kernel: round(gemm_s * 1e6, 3)},
         "step_bytes": step_bytes, "wall_s_timed_region": round(wall_s, 6),
@@ -467,8 +483,8 @@ def line(rec, n_gpus=1):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the layer's kernels run on one device and this "
-              "build has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU: the layer's kernels run on one device and the "
+              "library has no multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
@@ -552,8 +568,7 @@ def bench_moe(args):
     G.eager(step, warmup)
     g_flush = G.capture(gemm, copies)
     g_step = G.capture(step, steps)
-    g_gemm = G.capture(gemm, steps)
-    for g in (g_flush, g_step, g_gemm):
+    for g in (g_flush, g_step):
         G.replay(g)
     t0 = time.perf_counter()
     step_s = G.timed(g_step, flush=g_flush) / steps
@@ -586,7 +601,8 @@ def bench_moe(args):
             pts, how = int(ref.size), "all outputs"
         parity = {"quant_bit_exact": qok, "gemm_within_tolerance": ok,
                   "gemm_points": pts, "gemm_sample": how, "ok": ok and qok}
-    gemm_s = G.timed(g_gemm, flush=g_flush) / steps
+    r_gemm = max(1, math.ceil(KERNEL_TIMING_LAUNCHES / copies))
+    gemm_s = G.timed(g_flush, flush=g_flush, replays=r_gemm) / (r_gemm * copies)
     active = int(np.count_nonzero(np.diff(off)))
     w_alg = active * (N * K // 2 + N * (K // 32))
     gemm_bytes = w_alg + T * K + 4 * T + 2 * T * N

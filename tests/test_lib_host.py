@@ -235,7 +235,7 @@ def test_producer_argument_checks():
 def test_valid_call_without_a_gpu_is_refused_by_the_arch_gate():
     import subprocess
     import sys
-    # Run in a child with no visible devices so a GPU machine never launches on
+    # Run in a child with no visible devices so a machine with a GPU never launches on
     # the fake addresses: the gate must answer BS_EARCH before any launch.
     code = ("import ctypes,sys; sys.path.insert(0, %r); import mxfp4_gemm_transformer_amd as bs;"
             "lib=bs.load_library(); F=ctypes.c_void_p(0x10000);"
