@@ -381,9 +381,9 @@ def gemm_record(name, M, steps, warmup, cpu_seconds, check):
             "M": M, "N": wl.N, "K": wl.K, "weight_copies_rotated": copies,
             "rotation": "every copy touched in order before each timed replay",
             "step": "%s + %s" % (qname, kernel), "graph_replay": True,
-            "kernel_timing": "GEMM: %d replays of a graph of one launch per weight copy (%d "
-                             "launches); quantizer: %d replays of its %d-launch graph" % (
-                                 r_gemm, r_gemm * copies, r_quant, steps)},
+            "kernel_timing": "GEMM: a graph of one launch per weight copy, replayed %d time(s) "
+                             "(%d launches); quantizer: its %d-launch graph, replayed %d time(s)" % (
+                                 r_gemm, r_gemm * copies, steps, r_quant)},
         "roofline": roof,
         "kernels_us": {qname: round(quant_s * 1e6, 3), kernel: round(gemm_s * 1e6, 3)},
         "step_bytes": step_bytes, "wall_s_timed_region": round(wall_s, 6),
