@@ -96,8 +96,12 @@ def _explicit(rows, N, K, seed):
 
 
 @pytest.mark.parametrize("rows,N,K,max_rows", [
-    ([0, 1, 64, 65, 130, 300, 0, 33], 288, 1024, None),     # 128x128 tiles, scale rows in LDS
-    ([0, 1, 64, 65, 130, 300, 0, 33], 288, 1024, 100),      # bound below the largest expert
+    ([0, 1, 64, 65, 130, 300, 0, 33], 288, 1024, None),     # 256x256 tiles, scale rows in LDS
+    ([0, 1, 64, 65, 130, 300, 0, 33], 288, 1024, 100),      # 128x128, bound below the largest expert
+    ([150, 0, 129, 33, 160], 288, 1024, None),               # 160x256 tiles
+    ([300, 140, 0, 20], 288, 1024, 150),                     # 160x256, two m-tiles for one expert
+    ([150, 7], 64, 256, None),                               # 160x256, fewer stages than buffers
+    ([170, 5, 192, 0, 161], 544, 1024, None),                # 192x256 tiles
     ([40, 50, 0, 64], 160, 512, 64),                          # 64x64 tiles
     ([200, 0, 77, 129], 96, 1088, 200),                       # K % 128 = 64: one-step stages
 ])
