@@ -307,9 +307,10 @@ int gemm_fp8_rowwise(const void *a_e4m3, int64_t ld_a, const float *a_scale,
 /* Scratch bytes gemm_bs_fp8 (op 0), gemm_mxfp4_w4a8 (op 1), gemm_fp8_rowwise
  * (op 2) or gemm_mxfp4_w4a4 (op 3, every M <= 64) needs for this shape; 0
  * means none. Nonzero for
- * 8 < M <= 64, and for 2 <= M <= 8 when N * K >= 2^26: K is split across
- * workgroups and fp32 partial sums [S][M][N] go through the workspace
- * (S depends only on N and K). The workspace must then be 16-byte aligned;
+ * 8 < M <= 64, and for 2 <= M <= 8 when N * K >= 2^26, where K may be split
+ * across workgroups with fp32 partial sums [S][M][N] in the workspace (S
+ * depends only on N and K; from M = 9 to 14 on layers below 2^26 weights
+ * the decode kernel leaves it unused). The workspace must then be 16-byte aligned;
  * its contents on entry do not matter (every byte read is written first by
  * the same call), so one buffer serves every call of a shape. Calls that
  * share a workspace must not overlap in time. */

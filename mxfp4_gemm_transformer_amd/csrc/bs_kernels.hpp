@@ -35,7 +35,8 @@ constexpr int64_t DECODE_MAX_M = 64;
 // `ws` is the E8M0 grid, or NULL for e4m3 weights with one fp32 scale per
 // output channel in `cs` (NULL otherwise): Y = s[m] cs[n] sum_k a w.
 // `workspace` holds decode_workspace_bytes(M, N, K) bytes (fp32 partial sums
-// of the split-K path, 8 < M <= 64), 16-byte aligned; unused otherwise.
+// of the split-K path, sized for 8 < M <= 64), 16-byte aligned; unused
+// otherwise.
 hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
                               const uint8_t *w, int64_t ldw, const uint8_t *ws, const float *cs,
                               const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,

@@ -9,7 +9,7 @@
 // once. The waves' partial tiles meet in LDS, in a fixed order, and the
 // bias / GELU epilogue writes bf16. Two more shapes of the same idea follow:
 // for wide layers, one workgroup per CU with (row group, K step) units dealt
-// evenly to its waves; for 8 < M <= 64 on narrow layers, K split across
+// evenly to its waves; for 14 < M <= 64 on narrow layers, K split across
 // workgroups with fp32 partial sums in the caller's workspace, added in a
 // fixed order by a second kernel. No inter-workgroup synchronisation.
 //
@@ -18,7 +18,8 @@
 // block scales applied by the instruction per 32-element K block, and the
 // activation scale (fp32, per token) applied in the epilogue.
 //
-// Folded layout for M <= 8: the 16 A rows hold 8 tokens twice and the 16 B
+// Folded layout for M <= 8 (and two such token groups for M <= 14 on
+// narrow layers): the 16 A rows hold 8 tokens twice and the 16 B
 // columns hold 8 weight rows twice, each copy on a different 128-wide half
 // of a 256-wide K window. The two diagonal 8x8 blocks of the 16x16 result
 // are partial sums over the two halves and add up to the 8x8 output; the
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_decode_kernel(
     const float *__restrict__ colscale, const uint16_t *__restrict__ bias, int epi,
     uint16_t *__restrict__ Y, int64_t ldy, int M, int K) {
     constexpr int COLS = FOLD ? 8 : 16;
-    constexpr int ROWS = FOLD ? 8 : 16 * MT;
+    constexpr int ROWS = FOLD ? 8 * MT : 16 * MT;
     constexpr int KSTEP = FOLD ? 256 : 128;
     __shared__ float red[NW][ROWS][COLS + 1];
 
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_decode_kernel(
             wsc[u] = sc;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const int m = FOLD ? (i & 7) : (mt * 16 + i);
+                const int m = FOLD ? (mt * 8 + (i & 7)) : (mt * 16 + i);
                 uint4 alo = make_uint4(0u, 0u, 0u, 0u), ahi = alo;
                 if (on && m < M) {
                     const uint8_t *arow = A + (int64_t)m * lda;
@@ -165,10 +166,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_decode_kernel(
     // D: lane l = i + 16 g, VGPR v -> token row 4 g + v, weight column i.
     if (FOLD) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[0][v] += __shfl_down(acc[0][v], 40, 64);
-        if (g < 2 && i < 8) {
+        for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) red[wave][4 * g + v][i] = acc[0][v];
+            for (int v = 0; v < 4; ++v) acc[mt][v] += __shfl_down(acc[mt][v], 40, 64);
+            if (g < 2 && i < 8) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) red[wave][mt * 8 + 4 * g + v][i] = acc[mt][v];
+            }
         }
     } else {
 #pragma unroll
@@ -532,7 +536,7 @@ hipError_t launch_units_upw(int64_t upw, const uint8_t *a, int64_t lda, const fl
 inline bool units_epilogue_fits(int mt, int gpw) { return 8 * mt + 8 * gpw <= 1024; }
 
 // ---------------------------------------------------------------------------
-// Split-K decode for 8 < M <= 64 on narrow layers. With every workgroup on
+// Split-K decode for 14 < M <= 64 on narrow layers. With every workgroup on
 // all of K, each one would read all M x K activations (M/8 times the bytes
 // of its 8-row weight slice at M = 64); here a workgroup takes 64 weight
 // rows and a 1/S slice of K, with the activations' slice staged once in LDS,
@@ -806,7 +810,20 @@ hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const flo
             launch_spw<false, true, 1, NW>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
         return hipGetLastError();
     }
-    // 8 < M <= 64, or 2 <= M <= 8 on a large layer: split K over
+    if (M <= 14 && !large_splitk(8, N, K)) {
+        // two folded 8-token groups on each weight fragment: every workgroup
+        // reads M x K activation bytes (up to twice its weight slice, from
+        // L2), against a second launch and fp32 partial sums for split-K
+        // (measured on the 2048 x 7168 layer: M = 12 7.79 against 8.27 us,
+        // M = 16 8.56 against 8.40; the re-read grows with M)
+        const int per = (int)(((K + 255) / 256 + NW - 1) / NW);
+        if (fp4)
+            launch_spw<true, true, 2, NW>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
+        else
+            launch_spw<false, true, 2, NW>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
+        return hipGetLastError();
+    }
+    // 14 < M <= 64, or 2 <= M <= 14 on a large layer: split K over
     // workgroups, partial sums in the workspace
     float *part = static_cast<float *>(workspace);
     switch ((M + 15) / 16) {
