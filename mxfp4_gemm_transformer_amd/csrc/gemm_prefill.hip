@@ -430,7 +430,7 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
 // rows, a separate cache line each, every step: more L2 requests than the
 // tiles themselves.
 template <bool FP4, int BM, int BN, int NBUF, int WGM, int WGN, bool FP4A = false, int SPS = 1,
-          int SLAB_KB = 0>
+          int SLAB_KB = 0, int WBUF = NBUF>
 struct DCfg {
     static constexpr int NW = WGM * WGN;              // waves, WGM x WGN
     static constexpr int NT = NW * 64;
@@ -461,8 +461,17 @@ struct DCfg {
     static constexpr int SLAB_ROUND = 4 * NT;
     static constexpr int WSLAB = SLAB ? (SC_ROWS * SLAB_KB + SLAB_ROUND - 1) / SLAB_ROUND * SLAB_ROUND : 0;
     static constexpr int ASLAB = SLAB && FP4A ? (BM * SLAB_KB + SLAB_ROUND - 1) / SLAB_ROUND * SLAB_ROUND : 0;
-    static constexpr int WSLAB_OFF = NBUF * STAGE, ASLAB_OFF = WSLAB_OFF + WSLAB;
-    static constexpr int MAIN = NBUF * STAGE + WSLAB + ASLAB;
+    // WBUF > NBUF (two-step stages with scale slabs only): the W tiles have
+    // a ring of their own after the NBUF A tiles, one stage deeper, so each
+    // W stage is fetched a stage earlier than its A stage
+    static constexpr bool WRING = WBUF != NBUF;
+    static constexpr int RING = WRING ? NBUF * A_STAGE + WBUF * W_STAGE : NBUF * STAGE;
+    __host__ __device__ static constexpr int a_base(int b) { return WRING ? b * A_STAGE : b * STAGE; }
+    __host__ __device__ static constexpr int w_base(int b) {
+        return WRING ? NBUF * A_STAGE + b * W_STAGE : b * STAGE + A_STAGE;
+    }
+    static constexpr int WSLAB_OFF = RING, ASLAB_OFF = WSLAB_OFF + WSLAB;
+    static constexpr int MAIN = RING + WSLAB + ASLAB;
     static constexpr int LDS = MAIN > EP_ALL ? MAIN : EP_ALL;
     static_assert(A_STAGE % (16 * NT) == 0 && W_STAGE % (16 * NT) == 0, "stage split");
     static_assert(SC_ROWS <= NT, "one scale row per thread");
@@ -470,6 +479,7 @@ struct DCfg {
     static_assert(SPS == 1 ? NBUF >= 4 : (SPS == 2 && NBUF == 2), "pipeline shape");
     static_assert(SPS != 1 || LPS * (NBUF - 3) <= 63, "vmcnt range");
     static_assert(!SLAB || FP4, "scale slabs hold per-row (MXFP4) scales");
+    static_assert(!WRING || (SPS == 2 && NBUF == 2 && WBUF == 3 && SLAB), "W ring shape");
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
@@ -490,14 +500,14 @@ struct GroupArgs {
 };
 
 template <bool FP4, int BM, int BN, int NBUF, int WGM, int WGN, bool FP4A = false, int SPS = 1,
-          int SLAB_KB = 0, bool GROUPED = false>
+          int SLAB_KB = 0, bool GROUPED = false, int WBUF = NBUF>
 __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     const uint8_t *__restrict__ A_in, int64_t lda, const float *__restrict__ a_scale_in,
     const uint8_t *__restrict__ W_in, int64_t ldw, const uint8_t *__restrict__ WS_in,
     const float *__restrict__ colscale, const uint16_t *__restrict__ bias_in, int epi,
     uint16_t *__restrict__ Y_in, int64_t ldy, int M_grid, int N, int K, int group_m,
     const uint8_t *__restrict__ AS, GroupArgs gp) {
-    using C = DCfg<FP4, BM, BN, NBUF, WGM, WGN, FP4A, SPS, SLAB_KB>;
+    using C = DCfg<FP4, BM, BN, NBUF, WGM, WGN, FP4A, SPS, SLAB_KB, WBUF>;
     __shared__ __align__(16) uint8_t lds[C::LDS];
 
     // ---- tile of this workgroup (XCD-aware grouped order)
@@ -581,20 +591,26 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
 
     // Load i (0 .. LPS-1) of stage p into buffer p % NBUF: the A chunks, the
     // W chunks, then each step's scale pairs (weights, then fp4 activations).
-    // Past the last stage every lane reads outside the buffers' ranges,
-    // which writes zeros.
+    // With a W ring of its own the W chunks are those of stage p + 1, into
+    // W buffer (p + 1) % WBUF. Past the last stage every lane reads outside
+    // the buffers' ranges, which writes zeros.
+    auto issue_w = [&](int p, int j) {
+        const bool live = p < nstages;
+        const uint32_t kbase = (uint32_t)__builtin_amdgcn_readfirstlane(live ? p * C::KS : 0);
+        const uint32_t base = lds0 + (uint32_t)C::w_base(p % WBUF) + (uint32_t)wave * 1024u;
+        dma_b128(rsW, base + j * C::NT * 16, live ? w_off : OOB,
+                 (uint32_t)(j * W_ROWS_PER_J * ldw) + (FP4 ? kbase / 2 : kbase));
+    };
     auto issue_one = [&](int p, int i) {
         const bool live = p < nstages;
         const uint32_t kbase = (uint32_t)__builtin_amdgcn_readfirstlane(live ? p * C::KS : 0);
         const uint32_t sbase = lds0 + (uint32_t)((p % NBUF) * C::STAGE);
-        const uint32_t base = sbase + (uint32_t)wave * 1024u;
+        const uint32_t base = lds0 + (uint32_t)C::a_base(p % NBUF) + (uint32_t)wave * 1024u;
         if (i < C::A_LD) {
             dma_b128(rsA, base + i * C::NT * 16, live ? a_off : OOB,
                      (uint32_t)(i * A_ROWS_PER_J * lda) + (FP4A ? kbase / 2 : kbase));
         } else if (i < C::A_LD + C::W_LD) {
-            const int j = i - C::A_LD;
-            dma_b128(rsW, base + C::A_STAGE + j * C::NT * 16, live ? w_off : OOB,
-                     (uint32_t)(j * W_ROWS_PER_J * ldw) + (FP4 ? kbase / 2 : kbase));
+            issue_w(C::WRING ? p + 1 : p, i - C::A_LD);
         } else if (C::SLAB) {
             // unreachable: with scale slabs a stage has only tile loads
         } else if (i < C::A_LD + C::W_LD + SPS) {
@@ -631,7 +647,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     // MFMA selects it); step q = 1 reuses that word (copied by the caller).
     auto read_a = [&](Frags &f, int s, int a, int qk) {
         const int q = SPS == 1 ? 0 : qk;
-        const uint8_t *sa = lds + ((s / SPS) % NBUF) * C::STAGE;
+        const uint8_t *sa = lds + C::a_base((s / SPS) % NBUF);
         const int row = wm * (BM / WGM) + a * 32 + li;
         const int fz = swz<C::A_CH>(row);
         const uint8_t *p = sa + row * C::AROW;
@@ -651,7 +667,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     };
     auto read_b = [&](Frags &f, int s, int b, int qk) {
         const int q = SPS == 1 ? 0 : qk;
-        const uint8_t *sw = lds + ((s / SPS) % NBUF) * C::STAGE + C::A_STAGE;
+        const uint8_t *sw = lds + C::w_base((s / SPS) % WBUF);
         const uint8_t *ss = lds + ((s / SPS) % NBUF) * C::STAGE + C::SC_OFF + q * 4 * C::NT;
         const int row = wn * (BN / WGN) + b * 32 + li;
         const int fz = swz<C::W_CH>(row);
@@ -732,11 +748,15 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
             }
         }
     }
+    if constexpr (C::WRING) {   // W stage 0 first: then A p and W p + 1 per stage
+#pragma unroll
+        for (int j = 0; j < C::W_LD; ++j) issue_w(0, j);
+    }
 #pragma unroll
     for (int p = 0; p < PRO; ++p)
 #pragma unroll
         for (int i = 0; i < C::LPS; ++i) issue_one(p, i);
-    wait_loads_and_barrier<SPS == 1 ? C::LPS * (NBUF - 3) : C::LPS>();
+    wait_loads_and_barrier<SPS == 1 ? C::LPS * (NBUF - 3) : C::LPS + (C::WRING ? C::W_LD : 0)>();
     Frags f0, f1;
 #pragma unroll
     for (int a = 0; a < C::TM; ++a) read_a(f0, 0, a, 0);
@@ -763,7 +783,10 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     // are done and stage p + 1 has landed, and meet: stage p is then free
     // in every wave. Odd step 2p + 1: MFMAs, the reads of step 2p + 2
     // (stage p + 1) and the loads of stage p + 2 into stage p's buffer,
-    // which have until the end of step 2p + 2 to land.
+    // which have until the end of step 2p + 2 to land (with a W ring of its
+    // own, W stage p + 3 into W buffer p % 3, with until the end of step
+    // 2p + 4: W tiles that stream from HBM once wait a full memory latency,
+    // while A tiles come from L2).
     auto step_even = [&](const Frags &cur, Frags &nxt, int s) {
         mfmas(cur, Q0{});
         reads_and_loads(nxt, s + 1, 0, 0, 1);
@@ -776,7 +799,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
         interleave();
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
-        wait_loads_and_barrier<0>();
+        wait_loads_and_barrier<C::WRING ? C::W_LD : 0>();
         __builtin_amdgcn_sched_barrier(0);
     };
     auto step_odd = [&](const Frags &cur, Frags &nxt, int s) {
@@ -880,13 +903,14 @@ hipError_t launch_tile_dma(const uint8_t *a, int64_t lda, const float *as, const
 
 // The grouped form over E experts: a grid of (m-tiles of max_rows) x
 // (n-tiles) per expert, experts on the grid's y.
-template <bool FP4, int BM, int BN, int NBUF, int WGM = 2, int WGN = 2, int SPS = 1, int SLAB_KB = 0>
+template <bool FP4, int BM, int BN, int NBUF, int WGM = 2, int WGN = 2, int SPS = 1, int SLAB_KB = 0,
+          int WBUF = NBUF>
 hipError_t launch_tile_dma_grouped(const uint8_t *a, int64_t lda, const float *as,
                                    const int32_t *off, int64_t E, int64_t max_rows, int64_t T,
                                    const uint8_t *w, int64_t ldw, int64_t w_estride,
                                    const uint8_t *ws, const uint16_t *bias, int epi, uint16_t *y,
                                    int64_t ldy, int64_t N, int64_t K, hipStream_t st) {
-    auto kern = gemm_prefill_dma_kernel<FP4, BM, BN, NBUF, WGM, WGN, false, SPS, SLAB_KB, true>;
+    auto kern = gemm_prefill_dma_kernel<FP4, BM, BN, NBUF, WGM, WGN, false, SPS, SLAB_KB, true, WBUF>;
     const int64_t rows = max_rows < T ? max_rows : T;
     const int64_t tiles = ((rows + BM - 1) / BM) * ((N + BN - 1) / BN);
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles, (unsigned)E), dim3(WGM * WGN * 64), 0, st, a, lda,
@@ -1044,7 +1068,9 @@ hipError_t launch_prefill_dma(bool fp4, const uint8_t *a, int64_t lda, const flo
 // K / 32 <= 224 (K <= 7168), else one-step stages. Measured on 512 tokens
 // top-8 over 32 experts of 4096 x 7168 (at most 142 rows): 245 us with
 // 256x256 tiles and per-step scale loads, 210 us with the scale slab, 186 us
-// with 192-row and 181 us with 160-row tiles.
+// with 192-row and 181 us with 160-row tiles, 166 us with the 160- and
+// 192-row tiles' W stages in a ring of three (each expert's weights are read
+// once, from HBM, so their loads get a stage more to land).
 hipError_t launch_gemm_grouped_prefill(const uint8_t *a, int64_t lda, const float *a_scale,
                                        const int32_t *offsets, int64_t E, int64_t max_rows,
                                        const uint8_t *w, int64_t ldw, int64_t w_estride,
@@ -1054,8 +1080,8 @@ hipError_t launch_gemm_grouped_prefill(const uint8_t *a, int64_t lda, const floa
     if (K % 128 == 0 && K / 32 <= SLAB_KB_W4A8) {
         if (max_rows <= 64) return launch_tile_dma_grouped<true, 64, 64, 2, 2, 2, 2, SLAB_KB_W4A8>(BSG_GARGS);
         if (max_rows <= 128) return launch_tile_dma_grouped<true, 128, 128, 2, 2, 2, 2, SLAB_KB_W4A8>(BSG_GARGS);
-        if (max_rows <= 160) return launch_tile_dma_grouped<true, 160, 256, 2, 1, 4, 2, SLAB_KB_W4A8>(BSG_GARGS);
-        if (max_rows <= 192) return launch_tile_dma_grouped<true, 192, 256, 2, 2, 2, 2, SLAB_KB_W4A8>(BSG_GARGS);
+        if (max_rows <= 160) return launch_tile_dma_grouped<true, 160, 256, 2, 1, 4, 2, SLAB_KB_W4A8, 3>(BSG_GARGS);
+        if (max_rows <= 192) return launch_tile_dma_grouped<true, 192, 256, 2, 2, 2, 2, SLAB_KB_W4A8, 3>(BSG_GARGS);
         return launch_tile_dma_grouped<true, 256, 256, 2, 4, 2, 2, SLAB_KB_W4A8>(BSG_GARGS);
     }
     if (max_rows <= 128) return launch_tile_dma_grouped<true, 128, 128, 4>(BSG_GARGS);
