@@ -399,6 +399,7 @@ def gemm_record(name, M, steps, warmup, cpu_seconds, check):
         roof["measured_mfma_tflops"] = {"operands": "%s weights x %s activations, 32x32x64" % (
             "fp4" if pair[0] else "fp8", "fp4" if pair[1] else "fp8"), "value": rate}
         roof["frac_vs_measured_mfma"] = round(achieved / rate, 4)
+        roof["peak_derived"] = derived_peak("fp4" if w4a4 else "fp8")
     if parity is not None:
         rec["parity"] = parity
     if cpu_seconds > 0:
@@ -415,20 +416,20 @@ def cpu_baseline(d, wl, M, alg, compute_bound, budget_s):
     # rows so that one pass is about a second of work at ~1 GMAC/s/thread
     rows = max(1, min(M, int(2e9 / (wl.N * wl.K))))
     sample = d["a_bf16"][:rows]
-    runs, t_total = 0, 0.0
-    while t_total < budget_s or runs == 0:
-        t0 = time.perf_counter()
+    def one_pass():
         if wl.fmt == "mxfp4_w4a4":
             qa, sa = oracle.quant_mxfp4_rows(sample)
             oracle.gemm_mxfp4_w4a4(qa, sa, d["w"], d["w_scale"], d["bias"], d["epilogue"])
-        else:
-            qa, sa = oracle.quant_rows(sample)
-            if wl.fmt == "fp8":
-                oracle.gemm_bs_fp8(qa, sa, d["w"], d["w_scale"], d["bias"], d["epilogue"])
-            elif wl.fmt == "fp8_rowwise":
-                oracle.gemm_fp8_rowwise(qa, sa, d["w"], d["w_scale"], d["bias"], d["epilogue"])
-            else:
-                oracle.gemm_mxfp4_w4a8(qa, sa, d["w"], d["w_scale"], d["bias"], d["epilogue"])
+            return
+        qa, sa = oracle.quant_rows(sample)
+        fn = {"fp8": oracle.gemm_bs_fp8, "fp8_rowwise": oracle.gemm_fp8_rowwise,
+              "mxfp4": oracle.gemm_mxfp4_w4a8}[wl.fmt]
+        fn(qa, sa, d["w"], d["w_scale"], d["bias"], d["epilogue"])
+
+    runs, t_total = 0, 0.0
+    while t_total < budget_s or runs == 0:
+        t0 = time.perf_counter()
+        one_pass()
         t_total += time.perf_counter() - t0
         runs += 1
         if t_total > 3 * budget_s:
@@ -445,7 +446,8 @@ def cpu_baseline(d, wl, M, alg, compute_bound, budget_s):
     rec = {"value": round(value, 4), "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
            "sample": "%d of %d token rows (all %d outputs each), %d passes of quantize + GEMM + "
                      "epilogue in %.1f s" % (rows, M, wl.N, runs, t_total),
-           "cpu_model": _cpu_model()}
+           "cpu_model": _cpu_model(),
+           "gflops": round(alg["gemm_flops"] * frac * runs / t_total / 1e9, 3)}
     if not compute_bound and rows * wl.N * wl.K <= (1 << 27):
         # small workloads (the tiny GEMM, the decode projection): the same
         # sample on one core too, for about a third of the budget
@@ -455,15 +457,14 @@ def cpu_baseline(d, wl, M, alg, compute_bound, budget_s):
             r1, t1s = 0, 0.0
             while t1s < budget_s / 3 or r1 == 0:
                 t0 = time.perf_counter()
-                qa, sa = oracle.quant_rows(sample)
-                fn = oracle.gemm_bs_fp8 if wl.fmt == "fp8" else oracle.gemm_mxfp4_w4a8
-                fn(qa, sa, d["w"], d["w_scale"], d["bias"], d["epilogue"])
+                one_pass()
                 t1s += time.perf_counter() - t0
                 r1 += 1
         finally:
             oracle.set_num_threads(cores)
         v1, _ = rate(r1, t1s)
         rec["single_core"] = {"value": round(v1, 4), "unit": unit, "cores": 1,
+                              "gflops": round(alg["gemm_flops"] * frac * r1 / t1s / 1e9, 3),
                               "sample": "the same, %d passes in %.1f s" % (r1, t1s)}
     return rec
 
@@ -770,7 +771,31 @@ def _bench_lib():
     lib.bsb_l2_read.argtypes = [vp, i32, i32, i32, i32, vp, vp]
     lib.bsb_l2_read.restype = i32
     lib.bsb_mfma_rate.restype = i32
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.bsb_device_info.argtypes = [ip, ip, ip, ip]
+    lib.bsb_device_info.restype = i32
     return lib
+
+
+# Dense MFMA work per CU per engine clock on gfx950: a 32x32x64 MFMA with
+# 8-bit operands is 131072 flops in 64 cycles on each of a CU's 4 SIMDs;
+# 4-bit operands on both sides double it.
+MFMA_FLOP_PER_CLK_CU = {"fp8": 8192, "fp4": 16384}
+
+
+def derived_peak(kind):
+    """The dense MFMA peak of an operand kind from the device's own compute
+    unit count and peak engine clock, beside AMD's published figure."""
+    lib = _bench_lib()
+    v = [ctypes.c_int(0) for _ in range(4)]
+    if lib.bsb_device_info(*[ctypes.byref(x) for x in v]) != 0:
+        return None
+    cus, sclk_khz, mclk_khz, bus_bits = (x.value for x in v)
+    tf = cus * MFMA_FLOP_PER_CLK_CU[kind] * sclk_khz * 1e3 / 1e12
+    return {"value": round(tf, 1), "unit": "TFLOP/s",
+            "from": "%d CUs x %d flop/clk x %.3f GHz (device-reported peak engine clock)" % (
+                cus, MFMA_FLOP_PER_CLK_CU[kind], sclk_khz / 1e6),
+            "memory": "%d-bit bus, %.3f GHz memory clock (device-reported)" % (bus_bits, mclk_khz / 1e6)}
 
 
 def bench_ceiling(args):

@@ -263,4 +263,18 @@ int bsb_mfma_rate(int shape, int fa, int fb, int iters, int blocks, int waves, i
     return (int)hipErrorInvalidValue;
 }
 
+// The current device's compute-unit count and peak engine and memory clocks
+// (kHz) and memory bus width (bits), as the runtime reports them: the inputs
+// of a peak derived on the box itself.
+int bsb_device_info(int *cus, int *sclk_khz, int *mclk_khz, int *bus_bits) {
+    if (!cus || !sclk_khz || !mclk_khz || !bus_bits) return (int)hipErrorInvalidValue;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(sclk_khz, hipDeviceAttributeClockRate, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(mclk_khz, hipDeviceAttributeMemoryClockRate, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(bus_bits, hipDeviceAttributeMemoryBusWidth, dev);
+    return (int)e;
+}
+
 }  // extern "C"
