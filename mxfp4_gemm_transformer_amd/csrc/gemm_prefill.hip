@@ -970,10 +970,15 @@ int best_shape(int64_t M, int64_t N, int64_t K, int num_cus, int nshapes, double
 constexpr int SLAB_KB_W4A8 = 224;   // K <= 7168 (256x256 tiles: 152 KB of LDS)
 constexpr int SLAB_KB_W4A4 = 160;   // K <= 5120 (weight and activation slabs)
 
+// num_cus: for the e4m3 128x128 tiles, which take two-step stages when at
+// least two share every CU (2048x4096x1024: 18.6 -> 16.8 us) and one-step
+// stages, whose ring runs a step further ahead, when a CU has one
+// (4096x896 at K = 1024, 2048 and 4096: 11.9, 17.8 and 30.4 us against
+// 12.4, 18.9 and 32.2 with two-step stages).
 hipError_t launch_shape(int shape, bool fp4, const uint8_t *a, int64_t lda, const float *a_scale,
                         const uint8_t *w, int64_t ldw, const uint8_t *ws, const float *cs,
                         const uint16_t *bias, int epi, uint16_t *y, int64_t ldy, int64_t M,
-                        int64_t N, int64_t K, hipStream_t st, const uint8_t *a_e8m0) {
+                        int64_t N, int64_t K, hipStream_t st, const uint8_t *a_e8m0, int num_cus) {
 #define BSG_ARGS a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st
     if (a_e8m0) {   // W4A4: fp4 activations with their E8M0 scales, MXFP4 weights
         if (K % 128 == 0 && K / 32 <= SLAB_KB_W4A4) {
@@ -1008,8 +1013,10 @@ hipError_t launch_shape(int shape, bool fp4, const uint8_t *a, int64_t lda, cons
         return fp4 ? launch_tile_dma<true, 256, 128, 4>(BSG_ARGS)
                    : launch_tile_dma<false, 256, 128, 4>(BSG_ARGS);
     case 2:
-        return fp4 ? launch_tile_dma<true, 128, 128, 4>(BSG_ARGS)
-                   : launch_tile_dma<false, 128, 128, 4>(BSG_ARGS);
+        if (fp4) return launch_tile_dma<true, 128, 128, 4>(BSG_ARGS);
+        if (((M + 127) / 128) * ((N + 127) / 128) >= 2 * (int64_t)num_cus)
+            return launch_tile_dma<false, 128, 128, 2, 2, 2, false, 2>(BSG_ARGS);
+        return launch_tile_dma<false, 128, 128, 4>(BSG_ARGS);
     default:   // 64x64: e4m3 weights only here (the planner offers it to MXFP4 only with slabs)
         return fp4 ? launch_tile_dma<true, 128, 128, 4>(BSG_ARGS)
                    : launch_tile_dma<false, 64, 64, 4>(BSG_ARGS);
@@ -1040,7 +1047,7 @@ hipError_t launch_prefill_dma(bool fp4, const uint8_t *a, int64_t lda, const flo
         const int two = best_shape(M, N - n1, K, num_cus, nshapes, &c2);
         if (c1 + c2 + LAUNCH_COST < one_cost) {
             hipError_t e = launch_shape(0, fp4, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy,
-                                        M, n1, K, st, a_e8m0);
+                                        M, n1, K, st, a_e8m0, num_cus);
             if (e != hipSuccess) return e;
             const int64_t kb = K / 32;
             const uint8_t *w2 = w + n1 * ldw;
@@ -1048,11 +1055,11 @@ hipError_t launch_prefill_dma(bool fp4, const uint8_t *a, int64_t lda, const flo
             const float *cs2 = cs ? cs + n1 : nullptr;
             const uint16_t *bias2 = bias ? bias + n1 : nullptr;
             return launch_shape(two, fp4, a, lda, a_scale, w2, ldw, ws2, cs2, bias2, epi, y + n1,
-                                ldy, M, N - n1, K, st, a_e8m0);
+                                ldy, M, N - n1, K, st, a_e8m0, num_cus);
         }
     }
     return launch_shape(one, fp4, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st,
-                        a_e8m0);
+                        a_e8m0, num_cus);
 }
 
 }  // namespace

@@ -107,13 +107,14 @@ def test_prefill_dma_shapes(fmt, M, N, K):
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
 @pytest.mark.parametrize("M,N,K", [(4000, 2016, 2048), (3900, 4064, 1024), (3900, 4064, 1088),
-                                   (4000, 4192, 1024)])
+                                   (4000, 4192, 1024), (2000, 4000, 1088)])
 def test_prefill_dma_large_tiles(fmt, M, N, K):
     # the launch plans past one round of small tiles, ragged in M and N: one
-    # launch of 256x128 tiles, one of 256x256 (K % 128 == 0 and == 64), and
-    # two launches over column ranges (256x256 tiles in one whole round, then
-    # 64x64 tiles over the 96-column rest); y is a view into a larger
-    # NaN-filled buffer
+    # launch of 256x128 tiles, one of 256x256 (K % 128 == 0 and == 64), two
+    # launches over column ranges (256x256 tiles in one whole round, then
+    # 64x64 tiles over the 96-column rest), and 128x128 tiles two to a CU
+    # (e4m3: two-step stages, here with a last half stage); y is a view into
+    # a larger NaN-filled buffer
     for epi in (synth.EPI_NONE, synth.EPI_BIAS_GELU_TANH):
         a, s, w, ws, b = _random_problem(fmt, M, N, K, seed=M + N + epi)
         y_full = torch.full((M + 3, N + 64), float("nan"), dtype=torch.bfloat16, device=DEV)
