@@ -274,8 +274,9 @@ int gemm_mxfp4_w4a4(const void *a_fp4x2, int64_t ld_a, const uint8_t *a_scale,
  *   Up to 32 rows per expert (decode), each workgroup streams its 8 weight
  *   rows of one expert once per pass of up to 32 token rows. Past 32 (and
  *   K % 64 == 0), every expert is computed with the large-M tiles of the
- *   prefill GEMM (64x64 up to 64 rows, 128x128 up to 128, else 256x256),
- *   experts side by side in one launch.
+ *   prefill GEMM (64x64 up to 64 rows, 128x128 up to 128, 160x256 up to
+ *   160, 192x256 up to 192, else 256x256), experts side by side in one
+ *   launch.
  */
 int gemm_mxfp4_w4a8_grouped(const void *a_e4m3, int64_t ld_a, const float *a_scale,
                             const int32_t *expert_offsets, int64_t E,
