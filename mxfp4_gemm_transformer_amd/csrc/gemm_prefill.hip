@@ -453,9 +453,8 @@ struct DCfg {
     // epilogue staging: each wave's 32 x (32 TN) fp32 slab, rows padded by 16 bytes
     static constexpr int EP_ROW = TN * 32 * 4 + 16;
     static constexpr int EP_WAVE = 32 * EP_ROW;
-    static constexpr int EP_BIAS = NW * EP_WAVE;      // then each wave's TN*32 bias values
-    static constexpr int EP_CS = EP_BIAS + NW * TN * 32 * 4;   // and per-channel scales
-    static constexpr int EP_ALL = EP_CS + NW * TN * 32 * 4;
+    static constexpr int EP_ALL = NW * EP_WAVE;
+    static_assert(64 % (TN * 8) == 0, "a lane reads the same 4 columns in every slab row it reads");
     // scale slabs after the stages: weight rows, then (fp4 activations) A
     // rows, each rounded up to whole rounds of 4-byte loads
     static constexpr int SLAB_ROUND = 4 * NT;
@@ -472,7 +471,15 @@ struct DCfg {
     }
     static constexpr int WSLAB_OFF = RING, ASLAB_OFF = WSLAB_OFF + WSLAB;
     static constexpr int MAIN = RING + WSLAB + ASLAB;
-    static constexpr int LDS = MAIN > EP_ALL ? MAIN : EP_ALL;
+    // the epilogue's operands, fetched by LDS-mode loads when the tile starts
+    // into a region of their own past the ring and the epilogue's staging: a
+    // 4-byte slot per row (per-token scale) and two per column (bias, whose
+    // bf16 bits land in the slot's low half, and channel scale); each part
+    // holds whole waves' worth of slots (64), every slot a wave writes
+    static constexpr int EPO_AS = MAIN > EP_ALL ? MAIN : EP_ALL;
+    static constexpr int EPO_B = EPO_AS + 4 * ((BM + 63) / 64 * 64);
+    static constexpr int EPO_CS = EPO_B + 4 * ((BN + 63) / 64 * 64);
+    static constexpr int LDS = EPO_CS + 4 * ((BN + 63) / 64 * 64);
     static_assert(A_STAGE % (16 * NT) == 0 && W_STAGE % (16 * NT) == 0, "stage split");
     static_assert(SC_ROWS <= NT, "one scale row per thread");
     static_assert(!FP4A || BM <= NT, "one activation scale row per thread");
@@ -726,6 +733,27 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     // prologue: SPS = 1, stages 0 .. NBUF-2 in flight, wait for stages 0 and
     // 1; SPS = 2, both stages in flight, wait for stage 0
     constexpr int PRO = SPS == 1 ? NBUF - 1 : 2;
+    {
+        // the epilogue's per-token scales, bias and channel scales first (the
+        // oldest loads, so every wait below covers them): a lane's 4-byte slot
+        // at M0 + 4 lane, waves past the tile's rows or columns issue none
+        if (!FP4A && wave * 64 < BM) {
+            const int64_t ab = (int64_t)(M - m0) * 4;
+            const __amdgpu_buffer_rsrc_t rsT = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(a_scale + m0), (short)0, (int)(ab > 0x7FFFFFF0 ? 0x7FFFFFF0 : ab), 0x00020000);
+            dma_u32(rsT, lds0 + C::EPO_AS + (uint32_t)wave * 256u, tid < BM ? (uint32_t)(4 * tid) : OOB);
+        }
+        if (epi != EPI_NONE && wave * 64 < BN) {
+            const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(bias + n0), (short)0, (int)((int64_t)(N - n0) * 2), 0x00020000);
+            dma_u16(rsB, lds0 + C::EPO_B + (uint32_t)wave * 256u, tid < BN ? (uint32_t)(2 * tid) : OOB);
+        }
+        if (colscale && wave * 64 < BN) {
+            const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(colscale + n0), (short)0, (int)((int64_t)(N - n0) * 4), 0x00020000);
+            dma_u32(rsC, lds0 + C::EPO_CS + (uint32_t)wave * 256u, tid < BN ? (uint32_t)(4 * tid) : OOB);
+        }
+    }
     if constexpr (C::SLAB) {
         // the tile's scale rows, [rows, KB] bytes, in 4-byte pieces: piece d
         // of the flattened slab comes from row d / (KB / 4); pieces past the
@@ -828,28 +856,33 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
     // it in LDS as fp32, and reads it back as 4-column chunks in row-major
     // order, adding the bias, applying GELU and rounding to bf16, so that
     // consecutive lanes write consecutive 8-byte pieces of an output row.
+    // A wave's slab is its own, so the waves go through their slabs without
+    // meeting: a wave's LDS writes complete before its reads (and its reads
+    // before its next writes) by lgkmcnt(0). A lane reads the same 4
+    // columns in every slab row it reads, so their bias and channel scales
+    // are read once.
     wait_loads_and_barrier<0>();
     uint8_t *slab = lds + wave * C::EP_WAVE;
-    float *bias_w = reinterpret_cast<float *>(lds + C::EP_BIAS) + wave * C::TN * 32;
-    float *cs_w = reinterpret_cast<float *>(lds + C::EP_CS) + wave * C::TN * 32;
     constexpr int WCOLS = C::TN * 32;               // the wave's columns
     constexpr int CPR = WCOLS / 4;                  // 4-column chunks per slab row
     const int ncol0 = n0 + wn * (BN / WGN);         // the wave's first column
-#pragma unroll
-    for (int c = lane; c < WCOLS; c += 64) {        // bias and channel scale of the wave's columns
-        const int n = ncol0 + c;
-        float bv = 0.f, cv = 1.f;
-        if ((epi != EPI_NONE) & (n < N)) bv = bf16_to_f32(bias[n]);
-        if (colscale && (n < N)) cv = colscale[n];
-        bias_w[c] = bv;
-        cs_w[c] = cv;
+    const int cc = 4 * (lane % CPR);                // this lane's 4 columns (of the wave's)
+    float4 bv = make_float4(0.f, 0.f, 0.f, 0.f), cv = make_float4(1.f, 1.f, 1.f, 1.f);
+    {   // (zeros past N: those columns are not stored)
+        const int cl = wn * (BN / WGN) + cc;
+        if (epi != EPI_NONE) {
+            const uint4 b4 = *reinterpret_cast<const uint4 *>(lds + C::EPO_B + 4 * cl);
+            bv = make_float4(bf16_to_f32(b4.x & 0xFFFFu), bf16_to_f32(b4.y & 0xFFFFu),
+                             bf16_to_f32(b4.z & 0xFFFFu), bf16_to_f32(b4.w & 0xFFFFu));
+        }
+        if (colscale) cv = *reinterpret_cast<const float4 *>(lds + C::EPO_CS + 4 * cl);
     }
     float asv[C::TM];
 #pragma unroll
-    for (int a = 0; a < C::TM; ++a) {
-        const int m = m0 + wm * (BM / WGM) + a * 32 + li;
-        asv[a] = FP4A ? 1.0f : a_scale[m < M ? m : 0];   // rows past M are not stored
-    }
+    for (int a = 0; a < C::TM; ++a)   // (zeros past M: those rows are not stored)
+        asv[a] = FP4A ? 1.0f
+                      : *reinterpret_cast<const float *>(lds + C::EPO_AS +
+                                                         4 * (wm * (BM / WGM) + a * 32 + li));
 #pragma unroll
     for (int a = 0; a < C::TM; ++a) {
 #pragma unroll
@@ -864,15 +897,13 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
                 v.w = asv[a] * acc[a][b][4 * q + 3];
                 *reinterpret_cast<float4 *>(slab + li * C::EP_ROW + 4 * col) = v;
             }
-        __syncthreads();
+        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+        __builtin_amdgcn_wave_barrier();
         const int mrow = m0 + wm * (BM / WGM) + a * 32;
 #pragma unroll
         for (int it = 0; it < 32 * CPR / 64; ++it) {
-            const int ch = it * 64 + lane;
-            const int rr = ch / CPR, cc = 4 * (ch % CPR);
+            const int rr = (it * 64 + lane) / CPR;
             const float4 v = *reinterpret_cast<const float4 *>(slab + rr * C::EP_ROW + 4 * cc);
-            const float4 bv = *reinterpret_cast<const float4 *>(bias_w + cc);
-            const float4 cv = *reinterpret_cast<const float4 *>(cs_w + cc);
             const uint32_t h01 = pack_bf16x2(epilogue_rest(v.x * cv.x, bv.x, epi),
                                              epilogue_rest(v.y * cv.y, bv.y, epi));
             const uint32_t h23 = pack_bf16x2(epilogue_rest(v.z * cv.z, bv.z, epi),
@@ -881,9 +912,11 @@ __global__ __launch_bounds__(WGM * WGN * 64, 1) void gemm_prefill_dma_kernel(
             if (m < M && n < N)
                 store_y8(Y + (int64_t)m * ldy + n, h01, h23);
         }
-        __syncthreads();
+        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+        __builtin_amdgcn_wave_barrier();
     }
     if constexpr (!GROUPED) break;   // one tile; the grid covers every m-tile
+    __syncthreads();                 // the next m-tile's loads reuse every wave's LDS
     }
 }
 
