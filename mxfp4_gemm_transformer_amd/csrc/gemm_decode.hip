@@ -20,8 +20,9 @@
 //
 // Folded layout for M <= 8 (and two such token groups for M <= 14 on
 // narrow layers): the 16 A rows hold 8 tokens twice and the 16 B
-// columns hold 8 weight rows twice, each copy on a different 128-wide half
-// of a 256-wide K window. The two diagonal 8x8 blocks of the 16x16 result
+// columns hold 8 weight rows twice, each copy on a different half of a
+// 256-wide K window (the halves interleave at 64 bytes so that loads cover
+// whole cache lines; see fold_k). The two diagonal 8x8 blocks of the 16x16 result
 // are partial sums over the two halves and add up to the 8x8 output; the
 // off-diagonal blocks are discarded. This halves the weight rows per
 // workgroup, doubling the number of workgroups that stream W.
@@ -65,6 +66,25 @@ template <bool NT>
 __device__ __forceinline__ uint4 bloadw16(__amdgpu_buffer_rsrc_t rs, uint32_t voff) {
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, NT ? 2 : 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Where lane group g of K-half `half` finds its operand pieces in the folded
+// layout's 256-wide window starting at kw. The instruction's 8-bit operand
+// takes, per lane group g, a 16-byte "lo" piece (its K elements 16 g ...)
+// and a "hi" piece (64 + 16 g ...); its K blocks of 32 are the lo pieces of
+// groups 0-1 and 2-3, then the hi pieces of the same; an fp4 operand holds
+// block g in group g. Any placement that gives each block one whole
+// 32-element block of the window keeps the products and the E8M0 scales
+// right. This one interleaves the halves at 64 bytes (lo at 64 half + 16 g,
+// hi 128 bytes later), so each 16-byte-per-lane load covers whole 128-byte
+// lines of 8 rows instead of one 64-byte half of each; block b of half h
+// is block 2 h + (b & 1) + 4 (b >> 1) of the window.
+struct FoldK {
+    int kblk, klo, khi;   // scale / fp4 block start, fp8 lo and hi pieces (elements)
+};
+__device__ __forceinline__ FoldK fold_k(int kw, int half, int g) {
+    const int klo = kw + 64 * half + 16 * g;
+    return {kw + 32 * (2 * half + (g & 1) + 4 * (g >> 1)), klo, klo + 128};
 }
 
 template <bool FP4, bool FOLD, int MT, int NW, int SPW>
@@ -127,9 +147,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_decode_kernel(
         for (int u = 0; u < SPW; ++u) {
             const int s = s0 + u * NW;
             const bool on = s < nsteps;
-            const int k0 = s * KSTEP + half * 128;  // this lane's 128-wide window
-            const int kblk = k0 + 32 * g;           // the block whose scale this lane supplies
-            const int klo = k0 + 16 * g, khi = k0 + 64 + 16 * g;  // fp8 operand halves
+            const int k0 = s * KSTEP + half * 128;  // this lane's 128-wide window (unfolded)
+            const FoldK fk = fold_k(s * KSTEP, half, g);
+            // the block whose scale this lane supplies, and the fp8 operand pieces
+            const int kblk = FOLD ? fk.kblk : k0 + 32 * g;
+            const int klo = FOLD ? fk.klo : k0 + 16 * g, khi = FOLD ? fk.khi : k0 + 64 + 16 * g;
             uint4 lo = make_uint4(0u, 0u, 0u, 0u), hi = lo;
             int sc = E8M0_ONE;
             if (FP4) {
@@ -236,7 +258,9 @@ void launch_spw(int per_wave, const uint8_t *a, int64_t lda, const float *as, co
 // activations (a padded row per token) and the workgroup's E8M0 scales are
 // read once per workgroup into LDS, ahead of the weights, so waiting for
 // them does not wait for the weight stream. Tokens are folded as in the
-// kernel above, MT groups of 8 sharing each weight fragment. Group sums go
+// kernel above, MT groups of 8 sharing each weight fragment, but on two
+// plain 128-wide halves of each window (the activations come from LDS,
+// where the interleaved halves would put two lanes on one bank). Group sums go
 // through LDS: a group a wave covers whole as that wave's sum, a group cut
 // between waves (a wave's first and last group) as partial sums added in
 // wave order; the epilogue runs after every weight has been consumed.
@@ -874,8 +898,8 @@ __global__ __launch_bounds__(512) void gemm_grouped_decode_kernel(
 #pragma unroll
         for (int q = 0; q < G; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
         for (int s = wave; s < nsteps; s += NW) {
-            const int k0 = s * KSTEP + half * 128;
-            const int kblk = k0 + 32 * g, klo = k0 + 16 * g, khi = k0 + 64 + 16 * g;
+            const FoldK fk = fold_k(s * KSTEP, half, g);
+            const int kblk = fk.kblk, klo = fk.klo, khi = fk.khi;
             uint4 lo = make_uint4(0u, 0u, 0u, 0u), hi = lo;
             int sc = E8M0_ONE;
             if (FP4) {
