@@ -310,7 +310,7 @@ int gemm_fp8_rowwise(const void *a_e4m3, int64_t ld_a, const float *a_scale,
  * means none. Nonzero for
  * 8 < M <= 64, and for 2 <= M <= 8 when N * K >= 2^26, where K may be split
  * across workgroups with fp32 partial sums [S][M][N] in the workspace (S
- * depends only on N and K; from M = 9 to 14 on layers below 2^26 weights
+ * depends only on N and K; from M = 9 to 16 on layers below 2^26 weights
  * the decode kernel leaves it unused). The workspace must then be 16-byte aligned;
  * its contents on entry do not matter (every byte read is written first by
  * the same call), so one buffer serves every call of a shape. Calls that

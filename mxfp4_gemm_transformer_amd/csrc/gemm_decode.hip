@@ -9,7 +9,7 @@
 // once. The waves' partial tiles meet in LDS, in a fixed order, and the
 // bias / GELU epilogue writes bf16. Two more shapes of the same idea follow:
 // for wide layers, one workgroup per CU with (row group, K step) units dealt
-// evenly to its waves; for 14 < M <= 64 on narrow layers, K split across
+// evenly to its waves; for 16 < M <= 64 on narrow layers, K split across
 // workgroups with fp32 partial sums in the caller's workspace, added in a
 // fixed order by a second kernel. No inter-workgroup synchronisation.
 //
@@ -18,7 +18,7 @@
 // block scales applied by the instruction per 32-element K block, and the
 // activation scale (fp32, per token) applied in the epilogue.
 //
-// Folded layout for M <= 8 (and two such token groups for M <= 14 on
+// Folded layout for M <= 8 (and two such token groups for M <= 16 on
 // narrow layers): the 16 A rows hold 8 tokens twice and the 16 B
 // columns hold 8 weight rows twice, each copy on a different half of a
 // 256-wide K window (the halves interleave at 64 bytes so that loads cover
@@ -560,7 +560,7 @@ hipError_t launch_units_upw(int64_t upw, const uint8_t *a, int64_t lda, const fl
 inline bool units_epilogue_fits(int mt, int gpw) { return 8 * mt + 8 * gpw <= 1024; }
 
 // ---------------------------------------------------------------------------
-// Split-K decode for 14 < M <= 64 on narrow layers. With every workgroup on
+// Split-K decode for 16 < M <= 64 on narrow layers. With every workgroup on
 // all of K, each one would read all M x K activations (M/8 times the bytes
 // of its 8-row weight slice at M = 64); here a workgroup takes 64 weight
 // rows and a 1/S slice of K, with the activations' slice staged once in LDS,
@@ -834,12 +834,13 @@ hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const flo
             launch_spw<false, true, 1, NW>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
         return hipGetLastError();
     }
-    if (M <= 14 && !large_splitk(8, N, K)) {
+    if (M <= 16 && !large_splitk(8, N, K)) {
         // two folded 8-token groups on each weight fragment: every workgroup
         // reads M x K activation bytes (up to twice its weight slice, from
         // L2), against a second launch and fp32 partial sums for split-K
-        // (measured on the 2048 x 7168 layer: M = 12 7.79 against 8.27 us,
-        // M = 16 8.56 against 8.40; the re-read grows with M)
+        // (measured on the 2048 x 7168 layer: M = 12 7.39 against 8.27 us,
+        // M = 15 8.09-8.14 against 8.29-8.32, M = 16 8.33-8.38 either way;
+        // the re-read grows with M)
         const int per = (int)(((K + 255) / 256 + NW - 1) / NW);
         if (fp4)
             launch_spw<true, true, 2, NW>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
@@ -847,7 +848,7 @@ hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const flo
             launch_spw<false, true, 2, NW>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
         return hipGetLastError();
     }
-    // 14 < M <= 64, or 2 <= M <= 14 on a large layer: split K over
+    // 16 < M <= 64, or 2 <= M <= 16 on a large layer: split K over
     // workgroups, partial sums in the workspace
     float *part = static_cast<float *>(workspace);
     switch ((M + 15) / 16) {

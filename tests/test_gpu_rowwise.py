@@ -44,8 +44,8 @@ def _run(a, s, w, ws, b, epi, ld_pad=0):
 
 @pytest.mark.parametrize("M,N,K", [
     (1, 96, 1056), (8, 2048, 512), (5, 32768 + 32, 640), (16, 32768 + 32, 1024),   # decode
-    (12, 2080, 1184),                                                               # two folds
-    (24, 2048, 1152), (64, 512, 4096), (15, 2080, 1184),                            # split-K
+    (12, 2080, 1184), (16, 2080, 1184),                                             # two folds
+    (24, 2048, 1152), (64, 512, 4096), (17, 2080, 1184),                            # split-K
     (200, 320, 512), (300, 4192, 256), (513, 1024, 2048),                           # prefill DMA
     (130, 416, 96), (257, 160, 1056)])                                              # K % 64 = 32
 @pytest.mark.parametrize("epi", [synth.EPI_NONE, synth.EPI_BIAS_GELU_TANH])
