@@ -840,7 +840,20 @@ hipError_t launch_gemm_decode(bool fp4, const uint8_t *a, int64_t lda, const flo
         // L2), against a second launch and fp32 partial sums for split-K
         // (measured on the 2048 x 7168 layer: M = 12 7.39 against 8.27 us,
         // M = 15 8.09-8.14 against 8.29-8.32, M = 16 8.33-8.38 either way;
-        // the re-read grows with M)
+        // the re-read grows with M). On a layer of at most two workgroups
+        // per CU, 16 waves a workgroup, so that a wave's two steps are one
+        // pass (M = 16: 8.04-8.11 against 8.35-8.36 us with 8 waves in two
+        // passes; at M = 8 the single group keeps 8 waves, 6.27 against 6.35
+        // with 16)
+        if (N / 8 <= 2 * (int64_t)num_cus) {
+            constexpr int NW16 = 16;
+            const int per = (int)(((K + 255) / 256 + NW16 - 1) / NW16);
+            if (fp4)
+                launch_spw<true, true, 2, NW16>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
+            else
+                launch_spw<false, true, 2, NW16>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);
+            return hipGetLastError();
+        }
         const int per = (int)(((K + 255) / 256 + NW - 1) / NW);
         if (fp4)
             launch_spw<true, true, 2, NW>(per, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K, st);

@@ -65,6 +65,15 @@ def test_decode_wide_rows_windowed(M, N, K, epi):
     _full_check("fp8", M, N, K, epi, seed=M + K)
 
 
+# more than two 8-row groups per CU on a layer the wide-layer kernel leaves
+# (K % 128 = 32): the folded kernel keeps 8 waves a workgroup, one token
+# group (M = 5) or two (M = 12, 16); narrower layers take 16 waves
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("M", [5, 12, 16])
+def test_decode_folded_many_groups(fmt, M):
+    _full_check(fmt, M, 8192, 1056, synth.EPI_BIAS, seed=M + 1056)
+
+
 # split-K (16 < M <= 64, narrow layers): K cut into S slices of whole 128-k
 # steps; (2048, 1152) leaves the last three slices empty, (2080, 1184) adds
 # a half-full last column block and a 32-wide K tail
