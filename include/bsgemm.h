@@ -35,8 +35,12 @@
  *     (a hipStream_t passed as void*, NULL = the null stream) and the call
  *     returns before it runs. Calls may be captured into a HIP graph.
  *   - Matrices are row-major with a leading dimension (row stride) given in
- *     elements (bytes for 8-bit and packed data). Base pointers and leading
- *     dimensions in bytes must be multiples of 16.
+ *     elements (bytes for 8-bit and packed data). Alignment: matrices of
+ *     codes, bf16 matrices, the bf16 norm weight and the outputs start on
+ *     16-byte boundaries, and leading dimensions are multiples of 16 bytes;
+ *     fp32 per-token scales (and the static scale) are 4-byte aligned, fp32
+ *     per-channel scales 16-byte aligned, the bias 2-byte aligned; E8M0
+ *     scale grids may start at any byte address.
  *   - Arguments are checked on the host before anything is launched; on
  *     error nothing is launched and outputs are untouched. The first call
  *     on a device also checks that it is a gfx950 (BS_EARCH otherwise).
@@ -56,7 +60,7 @@ extern "C" {
 enum bs_status {
     BS_OK = 0,
     BS_EINVAL = -1,      /* a size, leading dimension, epilogue or null pointer is invalid */
-    BS_EALIGN = -2,      /* a pointer or leading dimension is not 16-byte aligned */
+    BS_EALIGN = -2,      /* a pointer or leading dimension is not aligned as required */
     BS_EARCH = -3,       /* no HIP device, or the current device is not gfx950 */
     BS_EWORKSPACE = -4,  /* workspace smaller than bs_workspace_bytes() */
     BS_ELAUNCH = -5      /* the kernel launch failed (hipGetLastError) */

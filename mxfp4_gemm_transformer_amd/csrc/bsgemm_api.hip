@@ -330,7 +330,7 @@ const char *bs_status_string(int status) {
     switch (status) {
     case BS_OK: return "ok";
     case BS_EINVAL: return "invalid argument (size, leading dimension, epilogue or null pointer)";
-    case BS_EALIGN: return "pointer or leading dimension not 16-byte aligned";
+    case BS_EALIGN: return "pointer or leading dimension not aligned as required";
     case BS_EARCH: return "no HIP device, or the current device is not gfx950";
     case BS_EWORKSPACE: return "workspace smaller than bs_workspace_bytes()";
     case BS_ELAUNCH: return "kernel launch failed";
