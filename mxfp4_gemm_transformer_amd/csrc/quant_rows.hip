@@ -386,8 +386,12 @@ hipError_t launch_quant_rows(const uint16_t *x, int64_t ld_x, uint8_t *q, int64_
     // threads a row with up to 4 chunks each past 4096 values, else 128
     // (4096 x 8192 in 26.3 us against 27.2 with 512 threads of 2 chunks,
     // 4096 x 5120 in 18.3 against 19.9); from 512 rows, one or two chunks
-    // per thread, up to 512 threads a row (512 x 8192 in 6.2 us).
-    int tpr = M <= 64 ? 1024 : 256;
+    // per thread, up to 512 threads a row (512 x 8192 in 6.2 us). A single
+    // row takes 512 threads of two chunks: 1 x 7168 in 3.0-3.3 us against
+    // 3.2-3.3 with 1024, and a quantize + GEMM step of 8.4 against 9.1 us;
+    // from two rows on, 1024 (8 x 7168: 3.5-3.6 us against 3.5-3.8 with 512
+    // and 4.2-4.3 with 256; 16 and 64 rows alike).
+    int tpr = M == 1 ? 512 : M <= 64 ? 1024 : 256;
     if (M >= 2048) {
         tpr = nch > 512 ? 256 : 128;
     } else if (M >= 512) {

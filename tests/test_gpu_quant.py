@@ -53,6 +53,9 @@ def test_quant_prefill_full_size():
 
 @pytest.mark.parametrize("M,K", [(3, 32), (17, 96), (5, 544), (300, 4128), (33, 8192 + 32),
                                  (2, 65536 + 64), (1, 131072),
+                                 # one row: 512 threads of one to four chunks, or
+                                 # 256 threads past that
+                                 (1, 2080), (1, 8192 + 32), (1, 16384 + 32),
                                  # many rows: 64 / 256 / 512 threads a row, 1-3 chunks a
                                  # thread, and rows too long for 512 threads
                                  (513, 96), (700, 2080), (600, 4128), (1030, 8224),
