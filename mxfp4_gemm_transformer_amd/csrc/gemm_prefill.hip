@@ -945,8 +945,15 @@ hipError_t launch_tile_dma(const uint8_t *a, int64_t lda, const float *as, const
                            hipStream_t st, const uint8_t *a_e8m0 = nullptr) {
     auto kern = gemm_prefill_dma_kernel<FP4, BM, BN, NBUF, WGM, WGN, FP4A, SPS, SLAB_KB>;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    // tile-rows per group of the tile order: 4 for 256-row tiles, 8 below
+    // (one box, two alternating passes, 4 against 8: the MXFP4 gate_up at
+    // M = 4096 552.6 against 575.1 us, W4A4 468.6 against 486.2, at M = 512
+    // 95.4 against 96.9, 4096x7168x8192 212.5-213.7 against 214.9-216.2;
+    // 2048x4096x1024 on 128x128 tiles 18.1 against 17.2 with bias, so
+    // those keep 8; 2 and 16 slower on both)
+    const int group_m = BM >= 256 ? 4 : 8;
     hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(WGM * WGN * 64), 0, st, a, lda, as, w,
-                       ldw, ws, cs, bias, epi, y, ldy, (int)M, (int)N, (int)K, 8, a_e8m0,
+                       ldw, ws, cs, bias, epi, y, ldy, (int)M, (int)N, (int)K, group_m, a_e8m0,
                        GroupArgs{nullptr, 0, 0});
     return hipGetLastError();
 }
