@@ -237,14 +237,22 @@ def test_valid_call_without_a_gpu_is_refused_by_the_arch_gate():
     import sys
     # Run in a child with no visible devices so a machine with a GPU never launches on
     # the fake addresses: the gate must answer BS_EARCH before any launch.
+    # E8M0 scale grids may start at any byte address: grids at odd addresses
+    # pass every host check too (G1, G3), for the block-scaled, MXFP4 and
+    # W4A4 GEMMs
     code = ("import ctypes,sys; sys.path.insert(0, %r); import mxfp4_gemm_transformer_amd as bs;"
             "lib=bs.load_library(); F=ctypes.c_void_p(0x10000);"
+            "G1=ctypes.c_void_p(0x10001); G3=ctypes.c_void_p(0x10003);"
+            "wk=bs.bs_workspace_bytes(3,8,64,64);"
             "print(lib.fp8_quant_rows(F,64,F,64,F,4,64,None),"
-            " lib.gemm_bs_fp8(F,64,F,F,64,F,None,0,F,64,8,64,64,None,0,None))") % ROOT
+            " lib.gemm_bs_fp8(F,64,F,F,64,F,None,0,F,64,8,64,64,None,0,None),"
+            " lib.gemm_bs_fp8(F,64,F,F,64,G1,None,0,F,64,8,64,64,None,0,None),"
+            " lib.gemm_mxfp4_w4a8(F,128,F,F,64,G3,None,0,F,64,200,64,128,None,0,None),"
+            " lib.gemm_mxfp4_w4a4(F,64,G1,F,64,G3,None,0,F,64,8,64,64,F,wk,None))") % ROOT
     env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1",
                CUDA_VISIBLE_DEVICES="-1")
     out = subprocess.check_output([sys.executable, "-c", code], env=env, text=True, timeout=120)
-    assert out.split() == [str(bs.BS_EARCH)] * 2
+    assert out.split() == [str(bs.BS_EARCH)] * 5
 
 
 def test_binding_refuses_tensors_off_the_device():
