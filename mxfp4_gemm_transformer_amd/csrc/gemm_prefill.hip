@@ -1168,19 +1168,15 @@ hipError_t launch_gemm_prefill(bool fp4, const uint8_t *a, int64_t lda, const fl
     if (K % 64 == 0)   // whole steps: LDS-mode staging
         return launch_prefill_dma(fp4, a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, ldy, M, N, K,
                                   num_cus, st);
-    // K % 64 == 32: register-staged kernel; the largest tile that still
-    // gives every CU a tile
-    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-    const int64_t t128 = ((M + 255) / 256) * ((N + 127) / 128);
-#define BSG_PREFILL(BM_, BN_)                                                                      \
-    return fp4 ? launch_tile<true, BM_, BN_, 2, 2>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y,  \
-                                                   ldy, M, N, K, st)                               \
-               : launch_tile<false, BM_, BN_, 2, 2>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y, \
-                                                    ldy, M, N, K, st)
-    if (t256 >= num_cus) BSG_PREFILL(256, 256);
-    if (t128 >= num_cus) BSG_PREFILL(256, 128);
-    BSG_PREFILL(128, 128);
-#undef BSG_PREFILL
+    // K % 64 == 32: the register-staged kernel on 128x128 tiles at every
+    // size (its 256x256 form needs more registers than a lane has and
+    // spills; shapes with K % 64 == 32 are a fallback, several times slower
+    // than the LDS-mode path either way)
+    (void)num_cus;
+    return fp4 ? launch_tile<true, 128, 128, 2, 2>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y,
+                                                   ldy, M, N, K, st)
+               : launch_tile<false, 128, 128, 2, 2>(a, lda, a_scale, w, ldw, ws, cs, bias, epi, y,
+                                                    ldy, M, N, K, st);
 }
 
 }  // namespace bsg
